@@ -1,0 +1,215 @@
+"""CPU oracle for the MTP draft / verify LM-head path (test infrastructure).
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg use this
+package. It is a ctypes wrapper over ``mtp_oracle.c`` (plain C, fp64
+accumulation, fp32 argmax decision); it shares no code with the HIP library
+and never imports it.
+
+Functions follow the method's steps (see ``mtp_oracle.c`` for the passages of
+the pages each one follows):
+  pack(head, ids)             candidate sub-table rows head[ids[i]]
+  logits(x, w)                [M][N] fp64 logits
+  argmax(x, w, ids=None)      per-row first maximum of the fp32-rounded logits
+  draft(h, table, ids)        argmax over the candidate table, mapped to ids
+  verify(hv, head, B, k)      argmax over the full head, shaped [B][k+1]
+  accept(draft, target)       greedy acceptance plus bonus token
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Dict, Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "mtp_oracle.c")
+_LIB = os.path.join(_HERE, "libmtp_oracle.so")
+
+ORC_OK = 0
+
+
+def build(force: bool = True, src: str = _SRC, out: str = _LIB) -> str:
+    """Compile the oracle with gcc (no fast-math, no FP contraction)."""
+    if force or not os.path.exists(out):
+        tmp = out + ".tmp"
+        subprocess.run(
+            ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-std=c11",
+             "-Wall", "-Wextra", "-shared", "-fPIC", src, "-o", tmp, "-lm"],
+            check=True)
+        os.replace(tmp, out)
+    return out
+
+
+class _Lib:
+    """The compiled oracle at one path (tests may load other builds)."""
+
+    def __init__(self, path: str):
+        lib = ctypes.CDLL(path)
+        P = ctypes.c_void_p
+        I64 = ctypes.c_int64
+        lib.mtp_oracle_threads.restype = ctypes.c_int
+        lib.mtp_oracle_logits.argtypes = [P, I64, P, I64, I64, P]
+        lib.mtp_oracle_pair_logits.argtypes = [P, P, I64, P, P, I64, P]
+        lib.mtp_oracle_argmax.argtypes = [P, I64, P, P, I64, I64, P, P, P, P, P]
+        lib.mtp_oracle_accept.argtypes = [P, P, I64, I64, P, P]
+        lib.mtp_oracle_check_ids.argtypes = [P, I64, I64]
+        lib.mtp_oracle_pack.argtypes = [P, I64, I64, P, I64, P]
+        for f in ("mtp_oracle_logits", "mtp_oracle_pair_logits", "mtp_oracle_argmax",
+                  "mtp_oracle_accept", "mtp_oracle_check_ids", "mtp_oracle_pack"):
+            getattr(lib, f).restype = ctypes.c_int
+        self.lib = lib
+        self.path = path
+
+
+_default: Optional[_Lib] = None
+_current: Optional[_Lib] = None
+
+
+def _load():
+    global _default
+    if _current is not None:
+        return _current.lib
+    if _default is None:
+        if not os.path.exists(_LIB):
+            build(force=False)
+        _default = _Lib(_LIB)
+    return _default.lib
+
+
+class use_library:
+    """Context manager: route this module's functions to another oracle build."""
+
+    def __init__(self, path: str):
+        self._lib = _Lib(path)
+        self._prev: Optional[_Lib] = None
+
+    def __enter__(self):
+        global _current
+        self._prev, _current = _current, self._lib
+        return self
+
+    def __exit__(self, *exc):
+        global _current
+        _current = self._prev
+        return False
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != ORC_OK:
+        raise OracleError(f"{what} failed with code {rc}")
+
+
+def _p(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _bf16(a: np.ndarray) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.uint16:
+        raise TypeError("bfloat16 inputs are passed as uint16 bit patterns")
+    return a
+
+
+def threads() -> int:
+    return int(_load().mtp_oracle_threads())
+
+
+def logits(x: np.ndarray, w: np.ndarray) -> np.ndarray:
+    x = _bf16(np.atleast_2d(x))
+    w = _bf16(np.atleast_2d(w))
+    M, H = x.shape
+    N, H2 = w.shape
+    if H != H2:
+        raise ValueError("hidden sizes differ")
+    z = np.empty((M, N), dtype=np.float64)
+    _check(_load().mtp_oracle_logits(_p(x), M, _p(w), N, H, _p(z)), "logits")
+    return z
+
+
+def pair_logits(x: np.ndarray, w: np.ndarray, rows: np.ndarray, cols: np.ndarray) -> np.ndarray:
+    """z[i] = dot(x[rows[i]], w[cols[i]]) in fp64."""
+    x = _bf16(np.atleast_2d(x))
+    w = _bf16(np.atleast_2d(w))
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    cols = np.ascontiguousarray(cols, dtype=np.int64)
+    if rows.shape != cols.shape:
+        raise ValueError("rows and cols differ in length")
+    if len(rows) and (rows.min() < 0 or rows.max() >= x.shape[0] or cols.min() < 0
+                      or cols.max() >= w.shape[0]):
+        raise IndexError("pair index out of range")
+    z = np.empty(len(rows), dtype=np.float64)
+    _check(_load().mtp_oracle_pair_logits(_p(x), _p(w), x.shape[1], _p(rows), _p(cols),
+                                          len(rows), _p(z)), "pair_logits")
+    return z
+
+
+def argmax(x: np.ndarray, w: np.ndarray, ids: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+    x = _bf16(np.atleast_2d(x))
+    w = _bf16(np.atleast_2d(w))
+    M, H = x.shape
+    N = w.shape[0]
+    if w.shape[1] != H:
+        raise ValueError("hidden sizes differ")
+    if ids is not None:
+        ids = np.ascontiguousarray(ids, dtype=np.int32)
+        if ids.shape != (N,):
+            raise ValueError("ids must have one entry per table row")
+    out = {
+        "id": np.empty(M, np.int32),
+        "logit": np.empty(M, np.float32),
+        "exact": np.empty(M, np.float64),
+        "runner_id": np.empty(M, np.int32),
+        "runner_exact": np.empty(M, np.float64),
+    }
+    _check(_load().mtp_oracle_argmax(_p(x), M, _p(w), _p(ids), N, H, _p(out["id"]),
+                                     _p(out["logit"]), _p(out["exact"]), _p(out["runner_id"]),
+                                     _p(out["runner_exact"])), "argmax")
+    return out
+
+
+def check_ids(ids: np.ndarray, V: int) -> bool:
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    return _load().mtp_oracle_check_ids(_p(ids), len(ids), V) == ORC_OK
+
+
+def pack(head: np.ndarray, ids: np.ndarray) -> np.ndarray:
+    head = _bf16(head)
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    V, H = head.shape
+    table = np.empty((len(ids), H), dtype=np.uint16)
+    _check(_load().mtp_oracle_pack(_p(head), V, H, _p(ids), len(ids), _p(table)), "pack")
+    return table
+
+
+def draft(h: np.ndarray, table: np.ndarray, ids: np.ndarray) -> Dict[str, np.ndarray]:
+    """Draft step: argmax of each hidden row over the candidate table, as global ids."""
+    return argmax(h, table, ids)
+
+
+def accept(draft_ids: np.ndarray, target: np.ndarray) -> Dict[str, np.ndarray]:
+    target = np.ascontiguousarray(target, dtype=np.int32)
+    B, k1 = target.shape
+    k = k1 - 1
+    d = np.ascontiguousarray(np.asarray(draft_ids, dtype=np.int32).reshape(B, k))
+    n = np.empty(B, np.int32)
+    tok = np.empty((B, k + 1), np.int32)
+    _check(_load().mtp_oracle_accept(_p(d), _p(target), B, k, _p(n), _p(tok)), "accept")
+    return {"accept": n, "tokens": tok}
+
+
+def verify(hv: np.ndarray, head: np.ndarray, B: int, k: int,
+           draft_ids: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+    """Verify step: full-head argmax of the B*(k+1) rows (row b*(k+1)+p),
+    reshaped [B][k+1]; with drafts given, also the acceptance result."""
+    r = argmax(hv, head, None)
+    out = {key: v.reshape(B, k + 1) for key, v in r.items()}
+    if draft_ids is not None:
+        out.update(accept(draft_ids, out["id"]))
+    return out

@@ -1,0 +1,296 @@
+"""Pins for the CPU oracle: checks against values fixed by the pages, by hand,
+by exact arithmetic or by closed forms, never against the oracle itself.
+
+Each ``pin_*`` function raises AssertionError when the oracle currently
+selected in the ``oracle`` module breaks it. ``test_oracle_pins.py`` runs them
+on the real oracle; ``test_oracle_mutants.py`` runs them on oracle builds with
+a planted mistake and requires every mutant to fail at least one pin.
+"""
+
+from __future__ import annotations
+
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+
+from speculative_decoding_argmax_amd import workloads as wl
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def bf16_exact(bits: int) -> Fraction:
+    """Exact value of a bfloat16 bit pattern from its fields (sign, 8-bit
+    exponent, 7-bit fraction); independent of any float reinterpretation."""
+    bits = int(bits)
+    sign = -1 if bits >> 15 else 1
+    e = (bits >> 7) & 0xFF
+    f = bits & 0x7F
+    if e == 0xFF:
+        raise ValueError("non-finite bfloat16")
+    if e == 0:
+        mag = Fraction(f, 128) * Fraction(1, 2 ** 126)
+    else:
+        mag = (1 + Fraction(f, 128)) * (Fraction(2) ** (e - 127))
+    return sign * mag
+
+
+def exact_dot(x_bits, w_bits) -> Fraction:
+    return sum((bf16_exact(a) * bf16_exact(b) for a, b in zip(x_bits, w_bits)), Fraction(0))
+
+
+def bits_of(values) -> np.ndarray:
+    return wl.f32_to_bf16_bits(np.asarray(values, dtype=np.float32))
+
+
+def _first_max(values):
+    best = 0
+    for i, v in enumerate(values):
+        if v > values[best]:
+            best = i
+    return best
+
+
+# ---------------------------------------------------------------------------
+
+def pin_worked_logits(oracle):
+    """Hand-summed logits and picks of tests/golden/logits_worked.json."""
+    g = _golden("logits_worked.json")
+    head = bits_of(g["head"])
+    q = bits_of(g["queries"])
+    # the fixture's values are exact in bfloat16
+    assert np.array_equal(wl.bf16_bits_to_f32(head), np.asarray(g["head"], np.float32))
+    z = oracle.logits(q, head)
+    assert np.array_equal(z, np.asarray(g["logits"], np.float64)), z
+    r = oracle.argmax(q, head)
+    assert list(r["id"]) == g["full_argmax"], r["id"]
+    assert list(r["runner_id"]) == g["full_runner_up"], r["runner_id"]
+    ids = np.asarray(g["candidate_ids"], np.int32)
+    d = oracle.draft(q, oracle.pack(head, ids), ids)
+    assert list(d["id"]) == g["candidate_argmax_id"], d["id"]
+
+
+def pin_exact_rational(oracle, seed=7):
+    """fp64 logits against exact rational dot products, within the error bound
+    of a sequential sum: |z - exact| <= (H+1) * 2^-53 * sum|x_j w_j|."""
+    r = wl.rng(seed, 99)
+    for H, scale_x, scale_w in ((1, 1.0, 1.0), (8, 1.0, 0.02), (37, 3.0, 0.5), (256, 1.0, 0.02)):
+        x = bits_of(r.standard_normal((3, H)) * scale_x)
+        w = bits_of(r.standard_normal((5, H)) * scale_w)
+        z = oracle.logits(x, w)
+        for m in range(3):
+            for n in range(5):
+                ex = exact_dot(x[m], w[n])
+                bound = (H + 1) * Fraction(1, 2 ** 53) * sum(
+                    abs(bf16_exact(a) * bf16_exact(b)) for a, b in zip(x[m], w[n]))
+                assert abs(Fraction(z[m, n]) - ex) <= bound, (H, m, n, z[m, n], float(ex))
+    # selected pairs: the same bound, rows and columns taken as given
+    rows = np.array([0, 2, 1, 2], np.int64)
+    cols = np.array([4, 0, 3, 3], np.int64)
+    zp = oracle.pair_logits(x, w, rows, cols)
+    for i in range(len(rows)):
+        ex = exact_dot(x[rows[i]], w[cols[i]])
+        bound = (x.shape[1] + 1) * Fraction(1, 2 ** 53) * sum(
+            abs(bf16_exact(a) * bf16_exact(b)) for a, b in zip(x[rows[i]], w[cols[i]]))
+        assert abs(Fraction(zp[i]) - ex) <= bound, (i, zp[i], float(ex))
+    # widening covers the whole bfloat16 range: tiny, huge and subnormal values
+    specials = np.array([0x0001, 0x8001, 0x007F, 0x0080, 0x7F7F, 0xFF7F, 0x3F80, 0xBF80, 0x0000,
+                         0x8000, 0x4049, 0x3C00], dtype=np.uint16)
+    one = np.array([[0x3F80]], dtype=np.uint16)
+    zs = oracle.logits(one, specials.reshape(-1, 1))[0]
+    for b, v in zip(specials, zs):
+        assert Fraction(v) == bf16_exact(b), (hex(int(b)), v)
+
+
+def pin_exact_grid(oracle, seed=11):
+    """Inputs on the grid q/16 (|q| <= 15): logits are exact integer sums
+    sum(qx*qw)/256, so the oracle must match them bit for bit, and its pick
+    must be the first maximum of those integers."""
+    for H, N in ((4, 300), (64, 257), (5120, 40)):
+        x = wl.exact_grid_bf16((2, H), seed, 1)
+        w = wl.exact_grid_bf16((N, H), seed, 2)
+        qx = np.rint(wl.bf16_bits_to_f32(x) * 16).astype(np.int64)
+        qw = np.rint(wl.bf16_bits_to_f32(w) * 16).astype(np.int64)
+        num = qx @ qw.T          # exact integer numerators over 256
+        z = oracle.logits(x, w)
+        assert np.array_equal(z * 256.0, num.astype(np.float64))
+        r = oracle.argmax(x, w)
+        for m in range(2):
+            row = [int(v) for v in num[m]]
+            best = _first_max(row)
+            assert r["id"][m] == best, (H, m, r["id"][m], best)
+            assert r["logit"][m] == np.float32(row[best] / 256.0)
+            cand = [i for i in range(N) if i != best]
+            second = max(cand, key=lambda i: (row[i], -i))
+            assert r["runner_id"][m] == second
+            assert r["runner_exact"][m] * 256.0 == row[second]
+
+
+def pin_tie_break(oracle):
+    """All-equal, max-at-end and repeated-max rows: the lowest index wins."""
+    H = 2
+    one = bits_of([[1.0, 0.0]])
+    w = bits_of([[0.5, 9.0], [0.5, -3.0], [0.25, 0.0], [0.5, 0.0]])
+    assert oracle.argmax(one, w)["id"][0] == 0
+    w = bits_of([[0.25, 0.0], [0.125, 0.0], [0.5, 0.0]])
+    assert oracle.argmax(one, w)["id"][0] == 2
+    w = bits_of([[-1.0, 0.0], [2.0, 0.0], [-2.0, 0.0], [2.0, 1.0], [2.0, 0.0]])
+    assert oracle.argmax(one, w)["id"][0] == 1
+    # -0.0 and +0.0 are equal: lowest index
+    zero_rows = np.array([[0x8000, 0x0000], [0x0000, 0x0000]], dtype=np.uint16)
+    w = bits_of([[-1.0, 0.0]])
+    w = np.concatenate([w, zero_rows])
+    q = bits_of([[1.0, 1.0]])
+    assert oracle.argmax(q, w)["id"][0] == 1
+    # with an id map the pick is reported as the id of the first maximal row
+    ids = np.array([3, 10, 11, 40, 41], np.int32)
+    w = bits_of([[-1.0, 0.0], [2.0, 0.0], [-2.0, 0.0], [2.0, 1.0], [2.0, 0.0]])
+    assert oracle.argmax(one, w, ids)["id"][0] == 10
+    assert H == 2
+
+
+def pin_candidate_vs_full(oracle, seed=5):
+    """An argmax over the packed candidate table equals the full-table argmax
+    restricted to the candidate ids (exact logits on the q/16 grid, so the
+    restricted first maximum is known exactly)."""
+    V, H, C = 3000, 48, 700
+    W = wl.exact_grid_bf16((V, H), seed, 3)
+    h = wl.exact_grid_bf16((4, H), seed, 4)
+    ids = wl.candidate_ids(V, C, seed)
+    table = oracle.pack(W, ids)
+    assert table.shape == (C, H)
+    d = oracle.draft(h, table, ids)
+    qh = np.rint(wl.bf16_bits_to_f32(h) * 16).astype(np.int64)
+    qW = np.rint(wl.bf16_bits_to_f32(W) * 16).astype(np.int64)
+    full = qh @ qW.T
+    for m in range(4):
+        restricted = [int(full[m, i]) for i in ids]
+        assert d["id"][m] == ids[_first_max(restricted)]
+    # identity table: draft == full argmax of the same rows
+    full_r = oracle.argmax(h, W)
+    ident = np.arange(V, dtype=np.int32)
+    d_id = oracle.draft(h, oracle.pack(W, ident), ident)
+    assert np.array_equal(d_id["id"], full_r["id"])
+    for m in range(4):
+        assert full_r["id"][m] == _first_max([int(v) for v in full[m]])
+
+
+def pin_pack(oracle):
+    """Packing copies head rows ids[i]; invalid id lists are refused."""
+    V, H = 50, 16
+    head = (np.arange(V * H, dtype=np.uint32) % 65000).astype(np.uint16).reshape(V, H)
+    ids = np.array([0, 7, 8, 31, 49], np.int32)
+    t = oracle.pack(head, ids)
+    for i, v in enumerate(ids):
+        # row v of this head holds v*H .. v*H+H-1
+        assert list(t[i]) == [int(v) * H + j for j in range(H)]
+    for bad in ([1, 1], [3, 2], [-1, 4], [4, 50]):
+        assert not oracle.check_ids(np.array(bad, np.int32), V)
+        try:
+            oracle.pack(head, np.array(bad, np.int32))
+        except oracle.OracleError:
+            pass
+        else:
+            raise AssertionError(f"pack accepted ids {bad}")
+    assert oracle.check_ids(ids, V)
+
+
+def pin_worked_accept(oracle):
+    """Hand-worked acceptance cases of tests/golden/accept_worked.json."""
+    g = _golden("accept_worked.json")
+    total_acc = 0
+    total_prop = 0
+    for c in g["cases"]:
+        k = len(c["draft"])
+        tgt = np.asarray([c["target"]], np.int32)
+        r = oracle.accept(np.asarray([c["draft"]], np.int32).reshape(1, k), tgt)
+        assert int(r["accept"][0]) == c["accept"], c
+        assert list(r["tokens"][0]) == c["tokens"], (c, r["tokens"])
+        if k == g["acceptance_rate_example"]["k"]:
+            total_acc += int(r["accept"][0])
+            total_prop += k
+    ex = g["acceptance_rate_example"]
+    assert Fraction(total_acc, total_prop) == Fraction(ex["value_num"], ex["value_den"])
+
+
+def pin_accept_invariants(oracle, seed=3):
+    """0 <= n <= k; tokens[:n] == drafts[:n]; tokens[n] == target[n];
+    if n < k the draft at n disagrees; slots after n are -1; p=1 accepts all,
+    p=0 accepts none, k=0 is plain greedy."""
+    r = wl.rng(seed, 17)
+    ids = np.arange(0, 400, 3, dtype=np.int32)
+    for B, k, p in ((64, 3, 0.55), (64, 4, 0.5), (16, 1, 0.9), (32, 6, 0.7)):
+        t = r.integers(0, 400, size=(B, k + 1)).astype(np.int32)
+        d = wl.select_drafts(t, wl.agreement_draws(B, k, p, len(ids), seed + k), ids)
+        out = oracle.accept(d, t)
+        for b in range(B):
+            n = int(out["accept"][b])
+            assert 0 <= n <= k
+            assert list(out["tokens"][b, :n]) == list(d[b, :n])
+            assert out["tokens"][b, n] == t[b, n]
+            if n < k:
+                assert d[b, n] != t[b, n]
+            assert all(v == -1 for v in out["tokens"][b, n + 1:])
+    B, k = 20, 3
+    t = r.integers(0, 400, size=(B, k + 1)).astype(np.int32)
+    assert np.all(oracle.accept(t[:, :k], t)["accept"] == k)
+    d_all = wl.select_drafts(t, wl.agreement_draws(B, k, 0.0, len(ids), 1), ids)
+    assert np.all(oracle.accept(d_all, t)["accept"] == 0)
+    g = oracle.accept(np.zeros((B, 0), np.int32), t[:, :1])
+    assert np.all(g["accept"] == 0) and np.array_equal(g["tokens"][:, 0], t[:, 0])
+
+
+def pin_acceptance_law(oracle, seed=23):
+    """With i.i.d. agreement p, P(n=j) = p^j (1-p) for j < k and P(n=k) = p^k
+    (so E[n] = sum_{j=1..k} p^j). Chi-square over 40,000 seeded sequences."""
+    B = 40_000
+    ids = np.arange(1000, dtype=np.int32)
+    r = wl.rng(seed, 5)
+    for k, p in ((3, 0.55), (4, 0.5)):
+        t = r.integers(0, 1000, size=(B, k + 1)).astype(np.int32)
+        d = wl.select_drafts(t, wl.agreement_draws(B, k, p, len(ids), seed + k), ids)
+        n = oracle.accept(d, t)["accept"]
+        probs = [p ** j * (1 - p) for j in range(k)] + [p ** k]
+        obs = np.bincount(n, minlength=k + 1)
+        exp = np.asarray(probs) * B
+        chi2 = float(((obs - exp) ** 2 / exp).sum())
+        # 99.99th percentile of chi-square with k dof is below 26 for k <= 4
+        assert chi2 < 26.0, (k, p, obs, exp, chi2)
+        mean_expected = sum(p ** j for j in range(1, k + 1))
+        assert abs(n.mean() - mean_expected) < 6 * math.sqrt(n.var() / B)
+
+
+def pin_pages_layout(oracle):
+    """The pages' printed sizes fix a dense [rows][hidden] bfloat16 table."""
+    g = _golden("pages_layout.json")
+    assert g["draft_rows"] == g["ranks"] * g["rows_per_rank"]
+    rows, hidden = g["matched_shape"]
+    assert rows == g["rows_per_rank"]
+    V = rows  # one rank's share, identity ids: the table equals the head
+    head = np.zeros((V, hidden), np.uint16)
+    head[:, 0] = np.arange(V, dtype=np.uint16)
+    t = oracle.pack(head, np.arange(V, dtype=np.int32))
+    assert t.nbytes == g["extra_mib_per_rank"] * 2 ** 20
+    assert t.shape == (rows, hidden) and t.dtype == np.uint16
+    assert np.array_equal(t, head)
+
+
+ALL_PINS = [
+    pin_worked_logits,
+    pin_exact_rational,
+    pin_exact_grid,
+    pin_tie_break,
+    pin_candidate_vs_full,
+    pin_pack,
+    pin_worked_accept,
+    pin_accept_invariants,
+    pin_acceptance_law,
+    pin_pages_layout,
+]

@@ -1,0 +1,44 @@
+"""Pin strength: oracle builds with one planted mistake each must fail at
+least one pin. The mistakes are planted in a temporary copy of the oracle's
+C source, compiled on the CPU; the real oracle is untouched."""
+
+import os
+
+import pytest
+
+from tests import oracle_pins
+
+# (name, text in mtp_oracle.c, replacement)
+MUTATIONS = [
+    ("dropped_last_term", "for (int64_t j = 0; j < H; ++j) s +=", "for (int64_t j = 0; j + 1 < H; ++j) s +="),
+    ("wrong_bf16_shift", "(uint32_t)b << 16", "(uint32_t)b << 15"),
+    ("reversed_operand_index", "bf16_to_double(w[j])", "bf16_to_double(w[H - 1 - j])"),
+    ("highest_index_wins_ties", "if (best < 0 || f > best_f)", "if (best < 0 || f >= best_f)"),
+    ("argmin_instead_of_argmax", "if (best < 0 || f > best_f)", "if (best < 0 || f < best_f)"),
+    ("bonus_token_dropped", "p <= n ? target", "p < n ? target"),
+    ("accept_wrong_target_stride", "draft[b * k + n] == target[b * (k + 1) + n]", "draft[b * k + n] == target[b * k + n]"),
+    ("pack_ignores_ids", "head + (int64_t)ids[i] * H", "head + i * H"),
+    ("runner_up_may_be_top", "if (n == best) continue;", ""),
+    ("ids_may_repeat", "ids[i] <= ids[i - 1]", "ids[i] < ids[i - 1]"),
+    ("id_map_dropped", "top_id[m] = ids ? ids[best] : (int32_t)best;", "top_id[m] = (int32_t)best;"),
+    ("pair_rows_swapped", "x + rows[i] * H, w + cols[i] * H", "x + cols[i] * H, w + rows[i] * H"),
+    ("logit_not_rounded_from_pick", "top_logit[m] = best_f;", "top_logit[m] = (float)z[0];"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_mutant_fails_a_pin(oracle_mod, tmp_path, name, old, new):
+    src = open(os.path.join(os.path.dirname(oracle_mod.__file__), "mtp_oracle.c")).read()
+    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    mut = tmp_path / f"{name}.c"
+    mut.write_text(src.replace(old, new))
+    lib = oracle_mod.build(force=True, src=str(mut), out=str(tmp_path / f"lib{name}.so"))
+    failed = []
+    with oracle_mod.use_library(lib):
+        for pin in oracle_pins.ALL_PINS:
+            try:
+                pin(oracle_mod)
+            except (AssertionError, oracle_mod.OracleError, ValueError, IndexError):
+                failed.append(pin.__name__)
+                break
+    assert failed, f"mutant {name} passed every pin"
