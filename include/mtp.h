@@ -1,0 +1,184 @@
+/*
+ * mtp.h -- C ABI of the MI355X (gfx950) MTP draft / verify LM-head library.
+ *
+ * The library runs the decode-side hot path of MTP speculative decoding with
+ * greedy (argmax) acceptance, as hand-written HIP kernels:
+ *
+ *   draft   score hidden rows against a packed candidate sub-table of the
+ *           output head and return, per row, the global token id of the
+ *           highest-scoring candidate.
+ *           [Qwen3.8 Flash dual-Spark tuning log, section "read one fewer big
+ *           table" (少读一张大表): the draft path reads a 65,536-row table
+ *           picked from the 248,320-row vocabulary; each rank finds the maximum
+ *           over its candidates and exchanges the maximum score together with
+ *           its global token id.]
+ *   verify  score the k+1 verify positions of every sequence against the full
+ *           head, take each position's argmax, and accept the longest prefix
+ *           of drafts that agrees with it, plus the target's own next token.
+ *           [same section: the main model keeps verifying with the full
+ *           vocabulary; edge-inference runtime blog, section 2.1, and
+ *           long-context blog, section 5: target verification accepts several
+ *           drafted tokens per step.]
+ *
+ * Conventions shared by every entry point
+ *   - bfloat16 values are passed as their 16-bit patterns (mtp_bf16), rows
+ *     dense and row-major: element (r, j) of a [R][H] matrix is at r*H + j.
+ *   - Scores are sums of bf16*bf16 products accumulated in fp32. The argmax
+ *     picks the largest score; equal scores go to the lowest token id.
+ *   - Device pointers point to memory on the current HIP device. The caller
+ *     owns every buffer; the library allocates, frees and retains nothing.
+ *   - Calls are asynchronous on `stream` (NULL = the default stream): they
+ *     return once the kernels are enqueued, with no host synchronisation and
+ *     no allocation, so they can be recorded into a HIP graph.
+ *   - Argument errors are returned synchronously, before anything is
+ *     enqueued. MTP_ERR_HIP reports a failed launch; mtp_last_hip_error()
+ *     then gives the hipError_t (per thread). Device data is not validated
+ *     per call: candidate ids must satisfy mtp_validate_ids(), draft ids may
+ *     be any int32.
+ *   - Workspace: a caller-owned device buffer of at least the queried size,
+ *     8-byte aligned, zeroed once with mtp_workspace_init(). Every call
+ *     leaves it zeroed again, so it needs no per-call clearing. Calls that
+ *     share a workspace must be ordered on one stream; calls with distinct
+ *     workspaces may run concurrently from any threads.
+ *   - Outputs are bit-identical for identical inputs, whatever the launch
+ *     configuration.
+ */
+#ifndef MTP_H
+#define MTP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t mtp_bf16; /* bfloat16 bit pattern */
+
+typedef enum {
+  MTP_OK = 0,
+  MTP_ERR_INVALID_ARG = 1, /* null pointer, size out of range, misaligned pointer */
+  MTP_ERR_UNSUPPORTED = 2, /* a shape or configuration the kernels do not handle */
+  MTP_ERR_WORKSPACE = 3,   /* workspace missing or smaller than the query says */
+  MTP_ERR_IDS = 4,         /* candidate ids not strictly ascending or outside [0, V) */
+  MTP_ERR_HIP = 5          /* a HIP call or kernel launch failed */
+} mtp_status;
+
+/* Limits checked by every entry point. */
+#define MTP_MAX_K 15          /* drafts per sequence */
+#define MTP_MAX_ROWS 4096     /* hidden rows per call (draft M, verify B*(k+1)) */
+#define MTP_MAX_HIDDEN 16384  /* H; H must also be a multiple of 8 */
+
+/* Launch selection for the *_cfg variants (tuning, tests). Zero fields mean
+ * "choose automatically"; the plain entry points use all zeros. */
+typedef enum { MTP_PATH_AUTO = 0, MTP_PATH_VALU = 1, MTP_PATH_MFMA = 2 } mtp_path;
+typedef struct {
+  int path;          /* mtp_path */
+  int blocks_per_cu; /* workgroups per compute unit of the row-streaming grid (1..16) */
+  int reserved[6];   /* must be zero */
+} mtp_config;
+
+/* Human-readable name of a status code (static storage). */
+const char *mtp_status_string(mtp_status status);
+
+/* hipError_t of the calling thread's last MTP_ERR_HIP (0 if none). */
+int mtp_last_hip_error(void);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int mtp_version(void);
+
+/* Host check of a candidate id list: strictly ascending, every id in [0, V).
+ * ids_host: host array of C int32. Returns MTP_OK or MTP_ERR_IDS
+ * (MTP_ERR_INVALID_ARG for a null pointer or C, V <= 0). */
+mtp_status mtp_validate_ids(const int32_t *ids_host, int64_t C, int64_t V);
+
+/* Bytes of workspace needed by mtp_draft_argmax for M hidden rows, and by
+ * mtp_verify_accept for B sequences with k drafts each. 0 for arguments out
+ * of range. */
+size_t mtp_draft_workspace_bytes(int M, int64_t C, int H);
+size_t mtp_verify_workspace_bytes(int B, int k, int64_t V, int H);
+
+/* Zero `ws_bytes` bytes of a workspace on `stream` (a fill kernel, so it may
+ * be captured into a graph). ws must be 8-byte aligned, ws_bytes a multiple
+ * of 8. */
+mtp_status mtp_workspace_init(void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Pack the candidate sub-table (one-time set-up, not per call):
+ *   table[i][:] = head[ids[i]][:]  for i < C.
+ * head  device [V][H] bf16;  ids device int32 [C], strictly ascending in
+ * [0, V) (check them with mtp_validate_ids first);  table device [C][H]
+ * bf16, written. A row whose id is out of range is filled with zeros.
+ * head and table 16-byte aligned, H a multiple of 8.
+ * [Qwen3.8 Flash dual-Spark tuning log, section "read one fewer big table":
+ * the full head stays resident and a smaller table serves the draft path,
+ * about 160 MiB per machine = 32,768 rows x 2,560 x 2 bytes, i.e. dense
+ * unpadded bf16 rows.]
+ */
+mtp_status mtp_pack_candidates(const mtp_bf16 *head, int64_t V, int H, const int32_t *ids,
+                               int64_t C, mtp_bf16 *table, hipStream_t stream);
+
+/*
+ * Draft step: for each hidden row m < M,
+ *   z[m][i]       = sum_j hidden[m][j] * table[i][j]     (fp32 accumulate)
+ *   i*            = lowest i with z[m][i] = max_i z[m][i]
+ *   out_ids[m]    = ids[i*]          (ids NULL: i* itself)
+ *   out_logit[m]  = z[m][i*]         (skipped if out_logit is NULL)
+ * hidden device [M][H] bf16 (16-byte aligned); table device [C][H] bf16
+ * (16-byte aligned); ids device int32 [C] ascending, or NULL for the
+ * identity map; out_ids device int32 [M]; out_logit device float [M] or
+ * NULL; ws/ws_bytes the workspace (mtp_draft_workspace_bytes(M, C, H)).
+ * 1 <= M <= MTP_MAX_ROWS, 1 <= C < 2^31, 8 <= H <= MTP_MAX_HIDDEN, H % 8 == 0.
+ * Rows of a batch are independent: the result equals M separate calls.
+ * [Qwen3.8 Flash dual-Spark tuning log, section "read one fewer big table".]
+ */
+mtp_status mtp_draft_argmax(const mtp_bf16 *hidden, int M, int H, const mtp_bf16 *table,
+                            const int32_t *ids, int64_t C, int32_t *out_ids, float *out_logit,
+                            void *ws, size_t ws_bytes, hipStream_t stream);
+
+mtp_status mtp_draft_argmax_cfg(const mtp_bf16 *hidden, int M, int H, const mtp_bf16 *table,
+                                const int32_t *ids, int64_t C, int32_t *out_ids,
+                                float *out_logit, void *ws, size_t ws_bytes, hipStream_t stream,
+                                const mtp_config *cfg);
+
+/*
+ * Verify step with greedy acceptance, for B sequences of k drafts each.
+ *   hidden      device [B*(k+1)][H] bf16; row b*(k+1)+p is the target's
+ *               hidden state that predicts slot p of sequence b (p = 0..k).
+ *   head        device [V][H] bf16, the full output head.
+ *   draft       device int32 [B][k], the drafted tokens (unused if k == 0).
+ *   out_argmax  device int32 [B][k+1]: t[b][p] = lowest v maximising
+ *               sum_j hidden[b*(k+1)+p][j] * head[v][j] (fp32 accumulate).
+ *   out_logit   device float [B][k+1] (that maximum) or NULL.
+ *   out_accept  device int32 [B]: n_b = lowest p < k with draft[b][p] !=
+ *               t[b][p], or k if every draft agrees.
+ *   out_tokens  device int32 [B][k+1]: t[b][0..n_b] (the accepted drafts,
+ *               equal to t there, then the bonus token t[b][n_b]); slots
+ *               after n_b are -1.
+ *   ws/ws_bytes workspace (mtp_verify_workspace_bytes(B, k, V, H)).
+ * 1 <= B, 0 <= k <= MTP_MAX_K, B*(k+1) <= MTP_MAX_ROWS, 1 <= V < 2^31.
+ * k == 0 is plain greedy decoding: n_b = 0, tokens[b][0] = t[b][0].
+ * [edge-inference runtime blog, section 2.1: verification in parallel
+ * accepts more tokens than steps executed; long-context blog, section 5;
+ * Qwen3.8 Flash dual-Spark tuning log, sections "MTP guesses one more step"
+ * (k = 3 and k = 4) and "read one fewer big table" (full-vocabulary
+ * verification).]
+ */
+mtp_status mtp_verify_accept(const mtp_bf16 *hidden, int B, int k, int H, const mtp_bf16 *head,
+                             int64_t V, const int32_t *draft, int32_t *out_argmax,
+                             float *out_logit, int32_t *out_accept, int32_t *out_tokens,
+                             void *ws, size_t ws_bytes, hipStream_t stream);
+
+mtp_status mtp_verify_accept_cfg(const mtp_bf16 *hidden, int B, int k, int H,
+                                 const mtp_bf16 *head, int64_t V, const int32_t *draft,
+                                 int32_t *out_argmax, float *out_logit, int32_t *out_accept,
+                                 int32_t *out_tokens, void *ws, size_t ws_bytes,
+                                 hipStream_t stream, const mtp_config *cfg);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MTP_H */

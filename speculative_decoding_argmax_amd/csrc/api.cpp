@@ -1,0 +1,232 @@
+// C ABI of the MTP draft / verify library: argument checks, path selection and
+// launch. Every check that can fail runs before anything is enqueued.
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+#include <cstring>
+
+#include "launch.hpp"
+#include "mtp.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+mtp_status hip_fail(hipError_t e) {
+  g_last_hip_error = (int)e;
+  return MTP_ERR_HIP;
+}
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cus[kMaxDevices];
+
+// Compute units of the current device (cached per device).
+hipError_t current_cus(int *cus) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < kMaxDevices) {
+    const int v = g_cus[dev].load(std::memory_order_relaxed);
+    if (v > 0) {
+      *cus = v;
+      return hipSuccess;
+    }
+  }
+  int n = 0;
+  e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  if (n <= 0) n = 1;
+  if (dev >= 0 && dev < kMaxDevices) g_cus[dev].store(n, std::memory_order_relaxed);
+  *cus = n;
+  return hipSuccess;
+}
+
+size_t rows_workspace_bytes(int64_t M) {
+  const size_t keys = (size_t)M * 8;
+  return mtp::kWsHeader + ((keys + 255) / 256) * 256;
+}
+
+bool shape_ok(int64_t M, int64_t N, int64_t H) {
+  return M >= 1 && M <= MTP_MAX_ROWS && N >= 1 && N <= INT32_MAX && H >= 8 &&
+         H <= MTP_MAX_HIDDEN && H % 8 == 0;
+}
+
+mtp_status check_cfg(const mtp_config *cfg) {
+  if (!cfg) return MTP_OK;
+  if (cfg->path < MTP_PATH_AUTO || cfg->path > MTP_PATH_MFMA) return MTP_ERR_INVALID_ARG;
+  if (cfg->blocks_per_cu < 0 || cfg->blocks_per_cu > 16) return MTP_ERR_INVALID_ARG;
+  for (int r : cfg->reserved)
+    if (r != 0) return MTP_ERR_INVALID_ARG;
+  return MTP_OK;
+}
+
+// Score M hidden rows against N table rows and finish through `sink`.
+mtp_status run_rows(const mtp_bf16 *X, int M, int H, const mtp_bf16 *W, int64_t N,
+                    mtp::RowSink sink, hipStream_t stream, const mtp_config *cfg) {
+  const int path = cfg ? cfg->path : MTP_PATH_AUTO;
+  if (path == MTP_PATH_MFMA) return MTP_ERR_UNSUPPORTED;
+  const int nch = H / 8;
+  const int ncl = mtp::valu_ncl_for(nch);
+  if (ncl == 0) return MTP_ERR_UNSUPPORTED;
+  int cus = 0;
+  hipError_t e = current_cus(&cus);
+  if (e != hipSuccess) return hip_fail(e);
+  const int per_cu = (cfg && cfg->blocks_per_cu > 0) ? cfg->blocks_per_cu : 2;
+  mtp::ValuLaunch L;
+  L.X = X;
+  L.W = W;
+  L.M = M;
+  L.N = N;
+  L.nch = nch;
+  L.max_blocks_x = per_cu * cus;
+  L.sink = sink;
+  L.stream = stream;
+  const int mr = mtp::valu_rows_for(M, ncl);
+  e = mtp::launch_valu(L, mr, ncl);
+  if (e != hipSuccess) return hip_fail(e);
+  return MTP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *mtp_status_string(mtp_status status) {
+  switch (status) {
+    case MTP_OK: return "MTP_OK";
+    case MTP_ERR_INVALID_ARG: return "MTP_ERR_INVALID_ARG: null pointer, size out of range or misaligned pointer";
+    case MTP_ERR_UNSUPPORTED: return "MTP_ERR_UNSUPPORTED: shape or configuration not handled";
+    case MTP_ERR_WORKSPACE: return "MTP_ERR_WORKSPACE: workspace missing or too small";
+    case MTP_ERR_IDS: return "MTP_ERR_IDS: candidate ids not strictly ascending in [0, V)";
+    case MTP_ERR_HIP: return "MTP_ERR_HIP: HIP call or kernel launch failed";
+  }
+  return "unknown mtp_status";
+}
+
+int mtp_last_hip_error(void) { return g_last_hip_error; }
+
+int mtp_version(void) { return 100; }
+
+mtp_status mtp_validate_ids(const int32_t *ids_host, int64_t C, int64_t V) {
+  if (!ids_host || C <= 0 || V <= 0) return MTP_ERR_INVALID_ARG;
+  for (int64_t i = 0; i < C; ++i) {
+    if (ids_host[i] < 0 || ids_host[i] >= V) return MTP_ERR_IDS;
+    if (i > 0 && ids_host[i] <= ids_host[i - 1]) return MTP_ERR_IDS;
+  }
+  return MTP_OK;
+}
+
+size_t mtp_draft_workspace_bytes(int M, int64_t C, int H) {
+  if (!shape_ok(M, C, H)) return 0;
+  return rows_workspace_bytes(M);
+}
+
+size_t mtp_verify_workspace_bytes(int B, int k, int64_t V, int H) {
+  if (B < 1 || k < 0 || k > MTP_MAX_K) return 0;
+  const int64_t M = (int64_t)B * (k + 1);
+  if (!shape_ok(M, V, H)) return 0;
+  return rows_workspace_bytes(M);
+}
+
+mtp_status mtp_workspace_init(void *ws, size_t ws_bytes, hipStream_t stream) {
+  if (!ws || ws_bytes == 0 || ws_bytes % 8 != 0 || !aligned(ws, 8)) return MTP_ERR_INVALID_ARG;
+  hipError_t e = mtp::launch_fill_zero(ws, ws_bytes, stream);
+  if (e != hipSuccess) return hip_fail(e);
+  return MTP_OK;
+}
+
+mtp_status mtp_pack_candidates(const mtp_bf16 *head, int64_t V, int H, const int32_t *ids,
+                               int64_t C, mtp_bf16 *table, hipStream_t stream) {
+  if (!head || !ids || !table) return MTP_ERR_INVALID_ARG;
+  if (V < 1 || V > INT32_MAX || C < 1 || C > INT32_MAX || H < 8 || H > MTP_MAX_HIDDEN ||
+      H % 8 != 0)
+    return MTP_ERR_INVALID_ARG;
+  if (!aligned(head, 16) || !aligned(table, 16) || !aligned(ids, 4)) return MTP_ERR_INVALID_ARG;
+  int cus = 0;
+  hipError_t e = current_cus(&cus);
+  if (e != hipSuccess) return hip_fail(e);
+  e = mtp::launch_pack(head, V, H / 8, ids, C, table, cus, stream);
+  if (e != hipSuccess) return hip_fail(e);
+  return MTP_OK;
+}
+
+mtp_status mtp_draft_argmax_cfg(const mtp_bf16 *hidden, int M, int H, const mtp_bf16 *table,
+                                const int32_t *ids, int64_t C, int32_t *out_ids,
+                                float *out_logit, void *ws, size_t ws_bytes, hipStream_t stream,
+                                const mtp_config *cfg) {
+  if (!hidden || !table || !out_ids) return MTP_ERR_INVALID_ARG;
+  if (!shape_ok(M, C, H)) return MTP_ERR_INVALID_ARG;
+  if (!aligned(hidden, 16) || !aligned(table, 16) || !aligned(out_ids, 4) ||
+      (ids && !aligned(ids, 4)) || (out_logit && !aligned(out_logit, 4)))
+    return MTP_ERR_INVALID_ARG;
+  mtp_status st = check_cfg(cfg);
+  if (st != MTP_OK) return st;
+  if (!ws || !aligned(ws, 8)) return MTP_ERR_WORKSPACE;
+  if (ws_bytes < rows_workspace_bytes(M)) return MTP_ERR_WORKSPACE;
+  mtp::RowSink s;
+  std::memset(&s, 0, sizeof s);
+  s.ticket = (uint32_t *)ws;
+  s.keys = (unsigned long long *)((char *)ws + mtp::kWsHeader);
+  s.ids = ids;
+  s.out_ids = out_ids;
+  s.out_logit = out_logit;
+  s.M = M;
+  s.B = 0;
+  s.k = -1;
+  return run_rows(hidden, M, H, table, C, s, stream, cfg);
+}
+
+mtp_status mtp_draft_argmax(const mtp_bf16 *hidden, int M, int H, const mtp_bf16 *table,
+                            const int32_t *ids, int64_t C, int32_t *out_ids, float *out_logit,
+                            void *ws, size_t ws_bytes, hipStream_t stream) {
+  return mtp_draft_argmax_cfg(hidden, M, H, table, ids, C, out_ids, out_logit, ws, ws_bytes,
+                              stream, nullptr);
+}
+
+mtp_status mtp_verify_accept_cfg(const mtp_bf16 *hidden, int B, int k, int H,
+                                 const mtp_bf16 *head, int64_t V, const int32_t *draft,
+                                 int32_t *out_argmax, float *out_logit, int32_t *out_accept,
+                                 int32_t *out_tokens, void *ws, size_t ws_bytes,
+                                 hipStream_t stream, const mtp_config *cfg) {
+  if (!hidden || !head || !out_argmax || !out_accept || !out_tokens) return MTP_ERR_INVALID_ARG;
+  if (B < 1 || k < 0 || k > MTP_MAX_K) return MTP_ERR_INVALID_ARG;
+  if (k > 0 && !draft) return MTP_ERR_INVALID_ARG;
+  const int64_t M = (int64_t)B * (k + 1);
+  if (!shape_ok(M, V, H)) return MTP_ERR_INVALID_ARG;
+  if (!aligned(hidden, 16) || !aligned(head, 16) || !aligned(out_argmax, 4) ||
+      !aligned(out_accept, 4) || !aligned(out_tokens, 4) || (draft && !aligned(draft, 4)) ||
+      (out_logit && !aligned(out_logit, 4)))
+    return MTP_ERR_INVALID_ARG;
+  mtp_status st = check_cfg(cfg);
+  if (st != MTP_OK) return st;
+  if (!ws || !aligned(ws, 8)) return MTP_ERR_WORKSPACE;
+  if (ws_bytes < rows_workspace_bytes(M)) return MTP_ERR_WORKSPACE;
+  mtp::RowSink s;
+  std::memset(&s, 0, sizeof s);
+  s.ticket = (uint32_t *)ws;
+  s.keys = (unsigned long long *)((char *)ws + mtp::kWsHeader);
+  s.ids = nullptr;
+  s.out_ids = out_argmax;
+  s.out_logit = out_logit;
+  s.M = (int)M;
+  s.B = B;
+  s.k = k;
+  s.draft = draft;
+  s.out_accept = out_accept;
+  s.out_tokens = out_tokens;
+  return run_rows(hidden, (int)M, H, head, V, s, stream, cfg);
+}
+
+mtp_status mtp_verify_accept(const mtp_bf16 *hidden, int B, int k, int H, const mtp_bf16 *head,
+                             int64_t V, const int32_t *draft, int32_t *out_argmax,
+                             float *out_logit, int32_t *out_accept, int32_t *out_tokens,
+                             void *ws, size_t ws_bytes, hipStream_t stream) {
+  return mtp_verify_accept_cfg(hidden, B, k, H, head, V, draft, out_argmax, out_logit,
+                               out_accept, out_tokens, ws, ws_bytes, stream, nullptr);
+}
+
+}  // extern "C"

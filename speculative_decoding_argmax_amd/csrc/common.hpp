@@ -1,0 +1,156 @@
+// Device-side building blocks shared by the draft / verify kernels (gfx950).
+//
+//  * bf16 dot products on v_dot2c_f32_bf16 (two bf16 products + fp32 add),
+//  * wave64 sums on DPP and the gfx950 permlane swaps (every lane ends with
+//    the same, bit-identical total),
+//  * the (score, row) order used by every argmax: larger score first, equal
+//    scores to the lower row (rows are ascending in token id, so the lower
+//    row is the lower id), packed into one 64-bit key so a single unsigned
+//    atomic max merges workgroups,
+//  * the cross-workgroup finish: each workgroup merges its per-row winners
+//    into the workspace keys, and the last workgroup to arrive (ticket)
+//    decodes them, writes the outputs, runs greedy acceptance for verify,
+//    and clears the workspace for the next call.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mtp {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// Workspace layout: [0, 256) ticket (uint32 at offset 0), then one 64-bit key
+// per hidden row.
+constexpr size_t kWsHeader = 256;
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// acc + sum of the 8 products of two 16-byte bf16 chunks, in element order.
+__device__ __forceinline__ float dot8_bf16(const uint4 &w, const uint4 &h, float acc) {
+  acc = dot2_bf16(w.x, h.x, acc);
+  acc = dot2_bf16(w.y, h.y, acc);
+  acc = dot2_bf16(w.z, h.z, acc);
+  acc = dot2_bf16(w.w, h.w, acc);
+  return acc;
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 64 lanes; every lane returns the same bits. The pairing is the
+// same for every call, so identical inputs give identical totals.
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_f32<0xB1>(v);   // quad_perm [1,0,3,2]: lane ^ 1
+  v += dpp_f32<0x4E>(v);   // quad_perm [2,3,0,1]: lane ^ 2
+  v += dpp_f32<0x141>(v);  // row_half_mirror: quad 0 <-> quad 1 of each 8
+  v += dpp_f32<0x140>(v);  // row_mirror: half 0 <-> half 1 of each 16
+  {
+    uint32_t u = __builtin_bit_cast(uint32_t, v);
+    auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);  // rows 0<->1, 2<->3
+    v = __builtin_bit_cast(float, p[0]) + __builtin_bit_cast(float, p[1]);
+  }
+  {
+    uint32_t u = __builtin_bit_cast(uint32_t, v);
+    auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);  // halves 0<->1
+    v = __builtin_bit_cast(float, p[0]) + __builtin_bit_cast(float, p[1]);
+  }
+  return v;
+}
+
+// True if (v, i) beats (bv, bi): larger score, or equal score and lower row.
+// bi < 0 marks "no candidate yet".
+__device__ __forceinline__ bool better(float v, int64_t i, float bv, int64_t bi) {
+  return bi < 0 || v > bv || (v == bv && i < bi);
+}
+
+// Monotone map of a finite float to uint32 (-0.0 folded onto +0.0).
+__device__ __forceinline__ uint32_t order_bits(float v) {
+  uint32_t u = __builtin_bit_cast(uint32_t, v == 0.0f ? 0.0f : v);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float unorder_bits(uint32_t o) {
+  uint32_t u = (o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o;
+  return __builtin_bit_cast(float, u);
+}
+
+// Key: score order in the high word, complemented row in the low word, so the
+// unsigned maximum is the best (score, lowest row). 0 means "empty".
+__device__ __forceinline__ unsigned long long make_key(float v, uint32_t row) {
+  return ((unsigned long long)order_bits(v) << 32) | (unsigned long long)(~row);
+}
+
+struct RowSink {
+  uint32_t *ticket;          // workspace + 0
+  unsigned long long *keys;  // workspace + kWsHeader, one per hidden row
+  const int32_t *ids;        // row -> token id, or nullptr for identity
+  int32_t *out_ids;          // [M]
+  float *out_logit;          // [M] or nullptr
+  int M;
+  // verify only (k < 0 for draft)
+  int B, k;
+  const int32_t *draft;      // [B][k]
+  int32_t *out_accept;       // [B]
+  int32_t *out_tokens;       // [B][k+1]
+};
+
+// Called by every thread of every workgroup after the workgroup's per-row
+// winners for rows [m_begin, m_begin + m_count) sit in wg_val / wg_row
+// (wg_row < 0: the workgroup saw no row). Must be reached by all threads.
+__device__ __forceinline__ void finish_rows(const RowSink &s, const float *wg_val,
+                                            const int64_t *wg_row, int m_begin, int m_count) {
+  __shared__ int s_last;
+  const int tid = threadIdx.x;
+  const int nthreads = blockDim.x;
+  for (int t = tid; t < m_count; t += nthreads) {
+    if (wg_row[t] >= 0) atomicMax(&s.keys[m_begin + t], make_key(wg_val[t], (uint32_t)wg_row[t]));
+  }
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t nblocks = gridDim.x * gridDim.y * gridDim.z;
+    const uint32_t prev =
+        __hip_atomic_fetch_add(s.ticket, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = (prev == nblocks - 1);
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  for (int m = tid; m < s.M; m += nthreads) {
+    const unsigned long long key =
+        __hip_atomic_load(&s.keys[m], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    int32_t id = -1;
+    float val = __builtin_nanf("");
+    if (key != 0ull) {
+      const uint32_t row = ~(uint32_t)(key & 0xFFFFFFFFull);
+      val = unorder_bits((uint32_t)(key >> 32));
+      id = s.ids ? s.ids[row] : (int32_t)row;
+    }
+    s.out_ids[m] = id;
+    if (s.out_logit) s.out_logit[m] = val;
+    __hip_atomic_store(&s.keys[m], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (s.k >= 0) {
+    __syncthreads();  // out_ids (the target argmax) written by this workgroup
+    const int k = s.k;
+    for (int b = tid; b < s.B; b += nthreads) {
+      const int32_t *t = s.out_ids + (int64_t)b * (k + 1);
+      int n = 0;
+      while (n < k && s.draft[(int64_t)b * k + n] == t[n]) ++n;
+      s.out_accept[b] = n;
+      for (int p = 0; p <= k; ++p) s.out_tokens[(int64_t)b * (k + 1) + p] = p <= n ? t[p] : -1;
+    }
+  }
+  if (tid == 0) __hip_atomic_store(s.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace mtp

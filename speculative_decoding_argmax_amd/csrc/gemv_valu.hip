@@ -1,0 +1,214 @@
+// Row-streaming GEMV + argmax on the vector ALUs (small numbers of hidden rows).
+//
+// Each wave owns blocks of RB consecutive table rows, strided over all waves of
+// the grid so that concurrently running waves read neighbouring memory. A row is
+// split over the 64 lanes in 16-byte chunks (lane l reads chunks l, l+64, ...),
+// so every load instruction of a wave reads 1 KiB of one row, fully coalesced.
+// The lanes' slices of the MR hidden rows sit in registers for the whole kernel.
+// Per (row, hidden row) a lane accumulates its chunks with v_dot2c_f32_bf16 in
+// chunk order, then the wave sums the 64 partials (wave_sum); every lane holds
+// the total, so the running (best score, best row) is wave-uniform. Waves merge
+// through LDS, workgroups through the workspace keys (finish_rows).
+//
+// The summation order of a row's score depends only on the column index, never
+// on where the row sits in the grid, so duplicated rows score bit-identically
+// and ties resolve to the lower row.
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace mtp {
+
+constexpr int kValuThreads = 256;
+constexpr int kValuWaves = kValuThreads / kWave;
+
+// Loads RB rows x NCL chunks of this lane's slice. ROWS_OK / COLS_OK say the
+// whole block lies inside the table, so no predication is needed.
+template <int RB, int NCL, bool ROWS_OK, bool COLS_OK>
+__device__ __forceinline__ void load_block(uint4 (&w)[RB][NCL], const uint4 *__restrict__ W,
+                                           int64_t r0, int64_t N, int nch, int lane) {
+#pragma unroll
+  for (int i = 0; i < RB; ++i) {
+    const uint4 *row = W + (r0 + i) * nch + lane;
+#pragma unroll
+    for (int c = 0; c < NCL; ++c) {
+      const bool ok = (ROWS_OK || r0 + i < N) && (COLS_OK || lane + kWave * c < nch);
+      w[i][c] = ok ? row[kWave * c] : make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+}
+
+template <int MR, int NCL, int RB, bool EXACT>
+__global__ void __launch_bounds__(kValuThreads)
+    gemv_argmax_valu(const uint4 *__restrict__ X, const uint4 *__restrict__ W, int M, int64_t N,
+                     int nch, RowSink sink) {
+  __shared__ float s_val[kValuWaves][MR];
+  __shared__ int64_t s_row[kValuWaves][MR];
+  __shared__ float f_val[MR];
+  __shared__ int64_t f_row[MR];
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int m0 = blockIdx.y * MR;
+
+  uint4 h[MR][NCL];
+#pragma unroll
+  for (int r = 0; r < MR; ++r) {
+#pragma unroll
+    for (int c = 0; c < NCL; ++c) {
+      const int col = lane + kWave * c;
+      h[r][c] = (m0 + r < M && (EXACT || col < nch)) ? X[(int64_t)(m0 + r) * nch + col]
+                                                     : make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+
+  float bv[MR];
+  int64_t bi[MR];
+#pragma unroll
+  for (int r = 0; r < MR; ++r) {
+    bv[r] = 0.0f;
+    bi[r] = -1;
+  }
+
+  const int64_t stride = (int64_t)gridDim.x * kValuWaves * RB;
+  for (int64_t r0 = ((int64_t)blockIdx.x * kValuWaves + wave) * RB; r0 < N; r0 += stride) {
+    uint4 w[RB][NCL];
+    if (r0 + RB <= N)
+      load_block<RB, NCL, true, EXACT>(w, W, r0, N, nch, lane);
+    else
+      load_block<RB, NCL, false, EXACT>(w, W, r0, N, nch, lane);
+    float acc[MR][RB];
+#pragma unroll
+    for (int r = 0; r < MR; ++r)
+#pragma unroll
+      for (int i = 0; i < RB; ++i) acc[r][i] = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NCL; ++c)
+#pragma unroll
+      for (int i = 0; i < RB; ++i)
+#pragma unroll
+        for (int r = 0; r < MR; ++r) acc[r][i] = dot8_bf16(w[i][c], h[r][c], acc[r][i]);
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+#pragma unroll
+      for (int r = 0; r < MR; ++r) {
+        const float s = wave_sum(acc[r][i]);
+        if (r0 + i < N && better(s, r0 + i, bv[r], bi[r])) {
+          bv[r] = s;
+          bi[r] = r0 + i;
+        }
+      }
+    }
+  }
+
+  if (lane == 0) {
+#pragma unroll
+    for (int r = 0; r < MR; ++r) {
+      s_val[wave][r] = bv[r];
+      s_row[wave][r] = bi[r];
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < MR) {
+    const int r = threadIdx.x;
+    float v = s_val[0][r];
+    int64_t ix = s_row[0][r];
+    for (int q = 1; q < kValuWaves; ++q) {
+      if (s_row[q][r] >= 0 && better(s_val[q][r], s_row[q][r], v, ix)) {
+        v = s_val[q][r];
+        ix = s_row[q][r];
+      }
+    }
+    f_val[r] = v;
+    f_row[r] = ix;
+  }
+  __syncthreads();
+  finish_rows(sink, f_val, f_row, m0, min(MR, M - m0));
+}
+
+// Rows per wave iteration: about 16 chunk loads (16 KiB per wave) in flight.
+template <int NCL>
+constexpr int valu_rows_per_iter() {
+  return NCL >= 16 ? 1 : (16 / NCL);
+}
+
+template <int MR, int NCL>
+static hipError_t launch_mr_ncl(const ValuLaunch &L) {
+  constexpr int RB = valu_rows_per_iter<NCL>();
+  const int64_t row_blocks = (L.N + RB - 1) / RB;
+  const int64_t want = (row_blocks + kValuWaves - 1) / kValuWaves;
+  const int gx = (int)(want < L.max_blocks_x ? want : L.max_blocks_x);
+  const int gy = (L.M + MR - 1) / MR;
+  if (L.nch == NCL * kWave)
+    hipLaunchKernelGGL((gemv_argmax_valu<MR, NCL, RB, true>), dim3(gx, gy), dim3(kValuThreads), 0,
+                       L.stream, (const uint4 *)L.X, (const uint4 *)L.W, L.M, L.N, L.nch, L.sink);
+  else
+    hipLaunchKernelGGL((gemv_argmax_valu<MR, NCL, RB, false>), dim3(gx, gy), dim3(kValuThreads),
+                       0, L.stream, (const uint4 *)L.X, (const uint4 *)L.W, L.M, L.N, L.nch,
+                       L.sink);
+  return hipGetLastError();
+}
+
+// Chunks per lane that have an instantiation; a request rounds up to the next.
+static const int kNclSteps[] = {1, 2, 3, 4, 5, 6, 8, 10, 12, 16, 20, 24, 32};
+
+int valu_ncl_for(int nch) {
+  const int need = (nch + kWave - 1) / kWave;
+  for (int n : kNclSteps)
+    if (n >= need) return n;
+  return 0;
+}
+
+int valu_rows_for(int M, int ncl) {
+  // hidden slices stay in registers: MR * NCL chunks of 4 VGPRs each, <= 128 VGPRs
+  int mr = 1;
+  while (mr < 8 && mr < M && (2 * mr) * ncl <= 32) mr *= 2;
+  return mr;
+}
+
+template <int MR>
+static hipError_t dispatch_ncl(int ncl, const ValuLaunch &L) {
+  switch (ncl) {
+#define MTP_NCL_CASE(n) \
+  case n:               \
+    if constexpr (MR * n <= 32) return launch_mr_ncl<MR, n>(L); \
+    break;
+    MTP_NCL_CASE(1)
+    MTP_NCL_CASE(2)
+    MTP_NCL_CASE(3)
+    MTP_NCL_CASE(4)
+    MTP_NCL_CASE(5)
+    MTP_NCL_CASE(6)
+    MTP_NCL_CASE(8)
+    MTP_NCL_CASE(10)
+    MTP_NCL_CASE(12)
+    MTP_NCL_CASE(16)
+    MTP_NCL_CASE(20)
+    MTP_NCL_CASE(24)
+    MTP_NCL_CASE(32)
+#undef MTP_NCL_CASE
+    default:
+      break;
+  }
+  return hipErrorInvalidValue;
+}
+
+int valu_total_blocks(const ValuLaunch &L, int mr, int ncl) {
+  const int rb = ncl >= 16 ? 1 : 16 / ncl;
+  const int64_t row_blocks = (L.N + rb - 1) / rb;
+  const int64_t want = (row_blocks + kValuWaves - 1) / kValuWaves;
+  const int gx = (int)(want < L.max_blocks_x ? want : L.max_blocks_x);
+  return gx * ((L.M + mr - 1) / mr);
+}
+
+hipError_t launch_valu(const ValuLaunch &L, int mr, int ncl) {
+  switch (mr) {
+    case 1: return dispatch_ncl<1>(ncl, L);
+    case 2: return dispatch_ncl<2>(ncl, L);
+    case 4: return dispatch_ncl<4>(ncl, L);
+    case 8: return dispatch_ncl<8>(ncl, L);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace mtp

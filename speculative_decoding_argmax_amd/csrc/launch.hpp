@@ -1,0 +1,34 @@
+// Internal launchers of the HIP kernels (host side). Not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace mtp {
+
+struct ValuLaunch {
+  const void *X;     // hidden [M][H] bf16
+  const void *W;     // table / head [N][H] bf16
+  int M;
+  int64_t N;
+  int nch;           // H / 8 (16-byte chunks per row)
+  int max_blocks_x;  // cap on workgroups along the row dimension
+  RowSink sink;
+  hipStream_t stream;
+};
+
+// Chunks-per-lane instantiation covering nch 16-byte chunks (0: too wide).
+int valu_ncl_for(int nch);
+// Hidden rows per workgroup for M rows at that width.
+int valu_rows_for(int M, int ncl);
+// Workgroups a launch will use (the ticket counts them).
+int valu_total_blocks(const ValuLaunch &L, int mr, int ncl);
+hipError_t launch_valu(const ValuLaunch &L, int mr, int ncl);
+
+hipError_t launch_pack(const void *head, int64_t V, int nch, const int32_t *ids, int64_t C,
+                       void *table, int num_cus, hipStream_t stream);
+hipError_t launch_fill_zero(void *ws, size_t bytes, hipStream_t stream);
+
+}  // namespace mtp

@@ -1,0 +1,244 @@
+"""Python binding of the MTP draft / verify C ABI (``include/mtp.h``).
+
+Argument marshalling only: tensors are passed as device pointers taken from
+``data_ptr()``, the stream is torch's current HIP stream, and every step of the
+path runs in the library's kernels. The library is loaded from
+``speculative_decoding_argmax_amd/lib/libmtp.so`` (build it with
+``python -m speculative_decoding_argmax_amd.build``); importing this module
+raises if it is missing.
+
+Function names match the C entry points. bfloat16 tensors may be passed as
+``torch.bfloat16`` or as ``torch.int16`` / ``torch.uint16`` bit patterns.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import List, Optional
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "lib", "libmtp.so")
+HEADER = os.path.join(os.path.dirname(_PKG), "include", "mtp.h")
+
+MTP_OK = 0
+MTP_ERR_INVALID_ARG = 1
+MTP_ERR_UNSUPPORTED = 2
+MTP_ERR_WORKSPACE = 3
+MTP_ERR_IDS = 4
+MTP_ERR_HIP = 5
+
+MTP_PATH_AUTO = 0
+MTP_PATH_VALU = 1
+MTP_PATH_MFMA = 2
+
+MTP_MAX_K = 15
+MTP_MAX_ROWS = 4096
+MTP_MAX_HIDDEN = 16384
+
+
+class MTPError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)}"
+                         + (f" (hipError {last_hip_error()})" if status == MTP_ERR_HIP else ""))
+
+
+class mtp_config(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int), ("blocks_per_cu", ctypes.c_int),
+                ("reserved", ctypes.c_int * 6)]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"HIP library not built: {LIB_PATH} is missing "
+            "(run python -m speculative_decoding_argmax_amd.build)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    I = ctypes.c_int
+    I64 = ctypes.c_int64
+    S = ctypes.c_size_t
+    sig = {
+        "mtp_status_string": ([I], ctypes.c_char_p),
+        "mtp_last_hip_error": ([], I),
+        "mtp_version": ([], I),
+        "mtp_validate_ids": ([P, I64, I64], I),
+        "mtp_draft_workspace_bytes": ([I, I64, I], S),
+        "mtp_verify_workspace_bytes": ([I, I, I64, I], S),
+        "mtp_workspace_init": ([P, S, P], I),
+        "mtp_pack_candidates": ([P, I64, I, P, I64, P, P], I),
+        "mtp_draft_argmax": ([P, I, I, P, P, I64, P, P, P, S, P], I),
+        "mtp_draft_argmax_cfg": ([P, I, I, P, P, I64, P, P, P, S, P, P], I),
+        "mtp_verify_accept": ([P, I, I, I, P, I64, P, P, P, P, P, P, S, P], I),
+        "mtp_verify_accept_cfg": ([P, I, I, I, P, I64, P, P, P, P, P, P, S, P, P], I),
+    }
+    for name, (args, res) in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = res
+    return lib
+
+
+lib = _load()
+
+
+def header_symbols(path: str = HEADER) -> List[str]:
+    """Entry points declared in include/mtp.h."""
+    text = open(path).read()
+    return sorted(set(re.findall(r"\b(mtp_[a-z0-9_]+)\s*\(", text)))
+
+
+def status_string(status: int) -> str:
+    return lib.mtp_status_string(int(status)).decode()
+
+
+def last_hip_error() -> int:
+    return int(lib.mtp_last_hip_error())
+
+
+def _check(status: int, what: str) -> None:
+    if status != MTP_OK:
+        raise MTPError(status, what)
+
+
+# --- tensor marshalling ---------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t, what: str, dtypes, device: bool = True, allow_none: bool = False):
+    if t is None:
+        if allow_none:
+            return None
+        raise ValueError(f"{what} is required")
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what} must be a torch.Tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{what}: dtype {t.dtype} not in {dtypes}")
+    if device and not t.is_cuda:
+        raise ValueError(f"{what} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _bf16_types():
+    torch = _torch()
+    out = [torch.bfloat16, torch.int16]
+    if hasattr(torch, "uint16"):
+        out.append(torch.uint16)
+    return tuple(out)
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _cfg(path: int = MTP_PATH_AUTO, blocks_per_cu: int = 0):
+    c = mtp_config()
+    c.path = path
+    c.blocks_per_cu = blocks_per_cu
+    return c
+
+
+# --- entry points ---------------------------------------------------------------
+
+def mtp_validate_ids(ids_host, V: int) -> int:
+    """Host check of candidate ids (numpy int32 array or CPU tensor). Returns the status."""
+    import numpy as np
+    a = np.ascontiguousarray(np.asarray(ids_host), dtype=np.int32)
+    return int(lib.mtp_validate_ids(a.ctypes.data_as(ctypes.c_void_p), a.size, int(V)))
+
+
+def mtp_draft_workspace_bytes(M: int, C: int, H: int) -> int:
+    return int(lib.mtp_draft_workspace_bytes(M, C, H))
+
+
+def mtp_verify_workspace_bytes(B: int, k: int, V: int, H: int) -> int:
+    return int(lib.mtp_verify_workspace_bytes(B, k, V, H))
+
+
+def alloc_workspace(nbytes: int, device=None, stream=None):
+    """Allocate (torch) and zero (mtp_workspace_init) a workspace of nbytes."""
+    torch = _torch()
+    n = max(8, (int(nbytes) + 7) // 8 * 8)
+    ws = torch.empty(n // 8, dtype=torch.int64, device=device or "cuda")
+    mtp_workspace_init(ws, stream=stream)
+    return ws
+
+
+def mtp_workspace_init(ws, stream=None) -> None:
+    torch = _torch()
+    p = _ptr(ws, "ws", (torch.int64, torch.uint8, torch.int32))
+    _check(lib.mtp_workspace_init(p, ws.numel() * ws.element_size(), _stream(stream)),
+           "mtp_workspace_init")
+
+
+def mtp_pack_candidates(head, ids, table, stream=None) -> None:
+    torch = _torch()
+    V, H = head.shape
+    C = ids.numel()
+    if tuple(table.shape) != (C, H):
+        raise ValueError("table must be [C][H]")
+    _check(lib.mtp_pack_candidates(_ptr(head, "head", _bf16_types()), V, H,
+                                   _ptr(ids, "ids", (torch.int32,)), C,
+                                   _ptr(table, "table", _bf16_types()), _stream(stream)),
+           "mtp_pack_candidates")
+
+
+def mtp_draft_argmax(hidden, table, ids, out_ids, out_logit=None, ws=None, stream=None,
+                     path: int = MTP_PATH_AUTO, blocks_per_cu: int = 0) -> None:
+    """Draft GEMV + argmax: out_ids[m] = ids[argmax_i hidden[m] . table[i]]."""
+    torch = _torch()
+    M, H = hidden.shape
+    C, H2 = table.shape
+    if H != H2:
+        raise ValueError("hidden and table widths differ")
+    if ids is not None and ids.numel() != C:
+        raise ValueError("ids must have C entries")
+    if out_ids.numel() != M or (out_logit is not None and out_logit.numel() != M):
+        raise ValueError("outputs must have M entries")
+    if ws is None:
+        ws = alloc_workspace(mtp_draft_workspace_bytes(M, C, H), hidden.device, stream)
+    cfg = _cfg(path, blocks_per_cu)
+    _check(lib.mtp_draft_argmax_cfg(
+        _ptr(hidden, "hidden", _bf16_types()), M, H, _ptr(table, "table", _bf16_types()),
+        _ptr(ids, "ids", (torch.int32,), allow_none=True), C,
+        _ptr(out_ids, "out_ids", (torch.int32,)),
+        _ptr(out_logit, "out_logit", (torch.float32,), allow_none=True),
+        _ptr(ws, "ws", (torch.int64, torch.uint8, torch.int32)), ws.numel() * ws.element_size(),
+        _stream(stream), ctypes.byref(cfg)), "mtp_draft_argmax")
+
+
+def mtp_verify_accept(hidden, head, draft, B: int, k: int, out_argmax, out_accept, out_tokens,
+                      out_logit=None, ws=None, stream=None, path: int = MTP_PATH_AUTO,
+                      blocks_per_cu: int = 0) -> None:
+    """Verify GEMM + per-row argmax + greedy acceptance (see include/mtp.h)."""
+    torch = _torch()
+    Mv, H = hidden.shape
+    V, H2 = head.shape
+    if H != H2 or Mv != B * (k + 1):
+        raise ValueError("hidden must be [B*(k+1)][H] with the head's H")
+    if out_argmax.numel() != Mv or out_tokens.numel() != Mv or out_accept.numel() != B:
+        raise ValueError("output sizes do not match B and k")
+    if draft is not None and draft.numel() != B * k:
+        raise ValueError("draft must be [B][k]")
+    if ws is None:
+        ws = alloc_workspace(mtp_verify_workspace_bytes(B, k, V, H), hidden.device, stream)
+    cfg = _cfg(path, blocks_per_cu)
+    _check(lib.mtp_verify_accept_cfg(
+        _ptr(hidden, "hidden", _bf16_types()), B, k, H, _ptr(head, "head", _bf16_types()), V,
+        _ptr(draft, "draft", (torch.int32,), allow_none=(k == 0)),
+        _ptr(out_argmax, "out_argmax", (torch.int32,)),
+        _ptr(out_logit, "out_logit", (torch.float32,), allow_none=True),
+        _ptr(out_accept, "out_accept", (torch.int32,)),
+        _ptr(out_tokens, "out_tokens", (torch.int32,)),
+        _ptr(ws, "ws", (torch.int64, torch.uint8, torch.int32)), ws.numel() * ws.element_size(),
+        _stream(stream), ctypes.byref(cfg)), "mtp_verify_accept")

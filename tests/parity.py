@@ -1,0 +1,150 @@
+"""Helpers of the GPU parity tests: device upload, the HIP calls, and the
+comparison rules against the CPU oracle.
+
+Comparison rules (floating point decides an integer here, so ties need care):
+  * a row is a near-tie row when the oracle's runner-up logit is within
+    1e-3 * |max| of the maximum;
+  * outside near-tie rows the GPU's token id must equal the oracle's;
+  * inside them the GPU's pick g must score within 1e-3 * |max| of the
+    maximum under the oracle (z[g] >= max - 1e-3 * |max|);
+  * rows built to hold an exact tie (duplicated head rows) are strict: the
+    duplicated rows score bit-identically on both sides, so the lower id wins;
+  * the returned logit must be within 2e-3 * |z[g]| of the oracle's logit of
+    the GPU's own pick;
+  * acceptance is compared exactly against the oracle's acceptance applied to
+    the GPU's (validated) verify argmax.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+from typing import Dict, Optional, Sequence
+
+import numpy as np
+
+import oracle
+from speculative_decoding_argmax_amd import workloads as wl
+
+NEAR_TIE_REL = 1e-3
+LOGIT_REL = 2e-3
+
+
+def torch_mod():
+    import torch
+    return torch
+
+
+def dev_bf16(a: np.ndarray):
+    torch = torch_mod()
+    a = np.ascontiguousarray(a, dtype=np.uint16)
+    return torch.from_numpy(a.view(np.int16)).to("cuda")
+
+
+def dev_i32(a: np.ndarray):
+    torch = torch_mod()
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to("cuda")
+
+
+def gpu_draft(h_dev, table_dev, ids_dev, **kw):
+    torch = torch_mod()
+    from speculative_decoding_argmax_amd import mtp
+    M = h_dev.shape[0]
+    out_ids = torch.full((M,), -7, dtype=torch.int32, device="cuda")
+    out_logit = torch.full((M,), float("nan"), dtype=torch.float32, device="cuda")
+    mtp.mtp_draft_argmax(h_dev, table_dev, ids_dev, out_ids, out_logit, **kw)
+    torch.cuda.synchronize()
+    return out_ids.cpu().numpy(), out_logit.cpu().numpy()
+
+
+def gpu_verify(hv_dev, head_dev, draft: np.ndarray, B: int, k: int, **kw):
+    torch = torch_mod()
+    from speculative_decoding_argmax_amd import mtp
+    Mv = B * (k + 1)
+    d = dev_i32(np.asarray(draft, np.int32).reshape(B, k)) if k > 0 else None
+    out_argmax = torch.full((B, k + 1), -7, dtype=torch.int32, device="cuda")
+    out_logit = torch.full((B, k + 1), float("nan"), dtype=torch.float32, device="cuda")
+    out_accept = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    out_tokens = torch.full((B, k + 1), -7, dtype=torch.int32, device="cuda")
+    mtp.mtp_verify_accept(hv_dev, head_dev, d, B, k, out_argmax, out_accept, out_tokens,
+                          out_logit, **kw)
+    torch.cuda.synchronize()
+    assert Mv == out_argmax.numel()
+    return {"argmax": out_argmax.cpu().numpy(), "logit": out_logit.cpu().numpy(),
+            "accept": out_accept.cpu().numpy(), "tokens": out_tokens.cpu().numpy()}
+
+
+@dataclasses.dataclass
+class RowReport:
+    rows: int = 0
+    exact: int = 0
+    near_tie_rows: int = 0
+    near_tie_diff: int = 0
+    max_logit_rel: float = 0.0
+
+
+def check_rows(gpu_ids: np.ndarray, gpu_logit: np.ndarray, orc: Dict[str, np.ndarray],
+               x: np.ndarray, w: np.ndarray, ids: Optional[np.ndarray],
+               rows: Optional[Sequence[int]] = None, strict: Sequence[int] = (),
+               x_rows: Optional[Sequence[int]] = None, check_logit: bool = True) -> RowReport:
+    """Check GPU picks against oracle results.
+
+    gpu_ids/gpu_logit: GPU outputs for all rows; orc: oracle.argmax output
+    for ``rows`` (all rows if None); x: hidden rows (all), w: table rows;
+    ids: table row -> id (None: identity); strict: rows that must match
+    exactly (injected exact ties)."""
+    rows = list(range(len(gpu_ids))) if rows is None else list(rows)
+    rep = RowReport()
+    strict = set(strict)
+    for j, m in enumerate(rows):
+        g = int(gpu_ids[m])
+        top = float(orc["exact"][j])
+        runner = float(orc["runner_exact"][j])
+        tol = NEAR_TIE_REL * abs(top)
+        near = runner >= top - tol
+        rep.rows += 1
+        rep.near_tie_rows += int(near)
+        if ids is None:
+            assert 0 <= g < w.shape[0], (m, g)
+            grow = g
+        else:
+            grow = int(np.searchsorted(ids, g))
+            assert grow < len(ids) and ids[grow] == g, f"row {m}: GPU id {g} is not a candidate"
+        if g == int(orc["id"][j]):
+            rep.exact += 1
+            zg = top
+        else:
+            assert m not in strict, f"row {m}: exact-tie row picked {g}, oracle {orc['id'][j]}"
+            assert near, (f"row {m}: GPU id {g} != oracle {orc['id'][j]} outside a near tie "
+                          f"(max {top}, runner-up {runner})")
+            zg = float(oracle.pair_logits(x, w, np.array([m if x_rows is None else x_rows[j]]),
+                                          np.array([grow]))[0])
+            assert zg >= top - tol, f"row {m}: GPU pick scores {zg}, oracle max {top}"
+            rep.near_tie_diff += 1
+        if check_logit:
+            rel = abs(float(gpu_logit[m]) - zg) / max(abs(zg), 1e-30)
+            rep.max_logit_rel = max(rep.max_logit_rel, rel)
+            assert rel <= LOGIT_REL, f"row {m}: logit {gpu_logit[m]} vs oracle {zg}"
+    return rep
+
+
+def check_accept(gpu: Dict[str, np.ndarray], draft: np.ndarray, B: int, k: int) -> None:
+    """Acceptance outputs equal the oracle's acceptance of the GPU argmax."""
+    exp = oracle.accept(np.asarray(draft, np.int32).reshape(B, k), gpu["argmax"].reshape(B, k + 1))
+    assert np.array_equal(gpu["accept"].reshape(B), exp["accept"]), (gpu["accept"], exp["accept"])
+    assert np.array_equal(gpu["tokens"].reshape(B, k + 1), exp["tokens"])
+
+
+def exact_logit_match(gpu_ids, gpu_logit, x, w, ids):
+    """For exact-grid inputs: the oracle's logits are exact, so the GPU's
+    ids must match the oracle's exactly and its logits bit for bit."""
+    orc = oracle.argmax(x, w, ids)
+    assert np.array_equal(gpu_ids, orc["id"]), (gpu_ids, orc["id"])
+    assert np.array_equal(gpu_logit.astype(np.float32), orc["logit"]), (gpu_logit, orc["logit"])
+    return orc
+
+
+def make_drafts(t_oracle: np.ndarray, wk: wl.Workload, ids: np.ndarray) -> np.ndarray:
+    """Drafts with the workload's agreement law against the oracle target."""
+    if wk.p is None:
+        return wl.uniform_drafts(wk.B, wk.k, ids, wk.seed)
+    return wl.select_drafts(t_oracle, wl.agreement_draws(wk.B, wk.k, wk.p, len(ids), wk.seed), ids)

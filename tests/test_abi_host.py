@@ -1,0 +1,126 @@
+"""The C ABI on the host: the library loads, exports every entry point the
+header declares, and refuses bad arguments before anything reaches the GPU.
+No call here passes validation, so nothing is ever launched."""
+
+import ctypes
+
+import numpy as np
+import pytest
+
+from speculative_decoding_argmax_amd import mtp
+
+P = ctypes.c_void_p
+FAKE = P(0x10000)        # non-null, 64 KiB aligned; never dereferenced
+FAKE_ODD = P(0x10002)    # 2-byte aligned only
+
+
+def test_exports_every_header_symbol():
+    names = mtp.header_symbols()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(mtp.lib, n), n
+
+
+def test_status_strings_and_version():
+    for s in range(6):
+        assert mtp.status_string(s).startswith("MTP_")
+    assert mtp.lib.mtp_version() >= 100
+    assert mtp.last_hip_error() == 0
+
+
+def test_validate_ids():
+    assert mtp.mtp_validate_ids(np.array([0, 5, 9]), 10) == mtp.MTP_OK
+    assert mtp.mtp_validate_ids(np.array([0, 5, 5]), 10) == mtp.MTP_ERR_IDS
+    assert mtp.mtp_validate_ids(np.array([3, 2]), 10) == mtp.MTP_ERR_IDS
+    assert mtp.mtp_validate_ids(np.array([0, 10]), 10) == mtp.MTP_ERR_IDS
+    assert mtp.mtp_validate_ids(np.array([-1, 4]), 10) == mtp.MTP_ERR_IDS
+    assert mtp.lib.mtp_validate_ids(None, 3, 10) == mtp.MTP_ERR_INVALID_ARG
+
+
+def test_workspace_sizes():
+    assert mtp.mtp_draft_workspace_bytes(1, 65536, 2048) == 512
+    assert mtp.mtp_draft_workspace_bytes(32, 65536, 5120) == 512
+    assert mtp.mtp_draft_workspace_bytes(33, 65536, 5120) == 768
+    assert mtp.mtp_verify_workspace_bytes(32, 4, 248320, 5120) == 256 + 1280
+    assert mtp.mtp_verify_workspace_bytes(1, 0, 10, 8) == 512
+    for bad in ((0, 10, 8), (1, 0, 8), (1, 10, 12), (1, 10, 4), (4097, 10, 8), (1, 10, 16392)):
+        assert mtp.mtp_draft_workspace_bytes(*bad) == 0, bad
+    assert mtp.mtp_verify_workspace_bytes(1, 16, 10, 8) == 0
+    assert mtp.mtp_verify_workspace_bytes(1, -1, 10, 8) == 0
+    assert mtp.mtp_verify_workspace_bytes(0, 3, 10, 8) == 0
+
+
+def _draft(hidden=FAKE, M=1, H=64, table=FAKE, ids=FAKE, C=100, out_ids=FAKE, out_logit=None,
+           ws=FAKE, ws_bytes=4096, cfg=None):
+    args = [hidden, M, H, table, ids, C, out_ids, out_logit, ws, ws_bytes, None]
+    if cfg is None:
+        return mtp.lib.mtp_draft_argmax(*args)
+    return mtp.lib.mtp_draft_argmax_cfg(*args, ctypes.byref(cfg))
+
+
+def _verify(hidden=FAKE, B=1, k=3, H=64, head=FAKE, V=100, draft=FAKE, out_argmax=FAKE,
+            out_logit=None, out_accept=FAKE, out_tokens=FAKE, ws=FAKE, ws_bytes=4096, cfg=None):
+    args = [hidden, B, k, H, head, V, draft, out_argmax, out_logit, out_accept, out_tokens, ws,
+            ws_bytes, None]
+    if cfg is None:
+        return mtp.lib.mtp_verify_accept(*args)
+    return mtp.lib.mtp_verify_accept_cfg(*args, ctypes.byref(cfg))
+
+
+INVALID = mtp.MTP_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [
+    dict(hidden=None), dict(table=None), dict(out_ids=None), dict(M=0), dict(M=4097),
+    dict(C=0), dict(C=2 ** 31), dict(H=0), dict(H=12), dict(H=16392), dict(hidden=FAKE_ODD),
+    dict(table=FAKE_ODD), dict(out_ids=P(0x10001)), dict(ids=P(0x10002)),
+    dict(out_logit=P(0x10003)),
+])
+def test_draft_rejects_bad_arguments(kw):
+    assert _draft(**kw) == INVALID
+
+
+def test_draft_workspace_errors():
+    assert _draft(ws=None) == mtp.MTP_ERR_WORKSPACE
+    assert _draft(ws=P(0x10004)) == mtp.MTP_ERR_WORKSPACE
+    assert _draft(M=33, ws_bytes=512) == mtp.MTP_ERR_WORKSPACE
+
+
+def test_draft_rejects_bad_config():
+    c = mtp.mtp_config()
+    c.path = 7
+    assert _draft(cfg=c) == INVALID
+    c = mtp.mtp_config()
+    c.blocks_per_cu = 17
+    assert _draft(cfg=c) == INVALID
+    c = mtp.mtp_config()
+    c.reserved[2] = 1
+    assert _draft(cfg=c) == INVALID
+
+
+@pytest.mark.parametrize("kw", [
+    dict(hidden=None), dict(head=None), dict(out_argmax=None), dict(out_accept=None),
+    dict(out_tokens=None), dict(B=0), dict(k=-1), dict(k=16), dict(draft=None),
+    dict(B=1025, k=3), dict(V=0), dict(H=20), dict(head=FAKE_ODD), dict(out_tokens=P(0x10001)),
+])
+def test_verify_rejects_bad_arguments(kw):
+    assert _verify(**kw) == INVALID
+
+
+def test_verify_workspace_errors():
+    assert _verify(ws=None) == mtp.MTP_ERR_WORKSPACE
+    assert _verify(B=64, k=3, ws_bytes=2048) == mtp.MTP_ERR_WORKSPACE
+
+
+def test_pack_and_init_reject_bad_arguments():
+    f = mtp.lib.mtp_pack_candidates
+    assert f(None, 10, 8, FAKE, 2, FAKE, None) == INVALID
+    assert f(FAKE, 10, 12, FAKE, 2, FAKE, None) == INVALID
+    assert f(FAKE, 0, 8, FAKE, 2, FAKE, None) == INVALID
+    assert f(FAKE, 10, 8, FAKE, 0, FAKE, None) == INVALID
+    assert f(FAKE_ODD, 10, 8, FAKE, 2, FAKE, None) == INVALID
+    g = mtp.lib.mtp_workspace_init
+    assert g(None, 64, None) == INVALID
+    assert g(FAKE, 0, None) == INVALID
+    assert g(FAKE, 12, None) == INVALID
+    assert g(P(0x10004), 64, None) == INVALID

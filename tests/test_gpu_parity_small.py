@@ -1,0 +1,222 @@
+"""GPU parity on small and edge-case inputs: exact-arithmetic inputs (bit-exact
+logits), ragged sizes, id maps, ties, determinism, workspace reset, packing,
+and the one-exchange sharding rule. Every call goes through the C ABI."""
+
+import numpy as np
+import pytest
+
+import oracle
+from speculative_decoding_argmax_amd import workloads as wl
+from tests.parity import (check_accept, check_rows, dev_bf16, dev_i32, exact_logit_match,
+                          gpu_draft, gpu_verify, make_drafts)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as t
+    assert t.cuda.is_available(), "GPU tests need a HIP device"
+    return t
+
+
+@pytest.fixture(scope="module")
+def mtp(torch):
+    from speculative_decoding_argmax_amd import mtp as m
+    return m
+
+
+def test_tiny_workload(torch, mtp):
+    """Tiny: H=256, V=4096, C=1024, three draft calls and one verify (k=3)."""
+    wk = wl.workload("tiny")
+    W = wl.head_weights(wk.V, wk.H, wk.seed)
+    ids = wl.candidate_ids(wk.V, wk.C, wk.seed)
+    table = oracle.pack(W, ids)
+    W_d, ids_d = dev_bf16(W), dev_i32(ids)
+    table_d = torch.empty((wk.C, wk.H), dtype=torch.int16, device="cuda")
+    mtp.mtp_pack_candidates(W_d, ids_d, table_d)
+    assert np.array_equal(table_d.cpu().numpy().view(np.uint16), table)
+    for call in range(wk.draft_calls):
+        h = wl.hidden_states(wk.Md, wk.H, wk.seed, block=call)
+        g_ids, g_logit = gpu_draft(dev_bf16(h), table_d, ids_d)
+        check_rows(g_ids, g_logit, oracle.draft(h, table, ids), h, table, ids)
+    hv = wl.hidden_states(wk.Mv, wk.H, wk.seed, block=100)
+    orc = oracle.argmax(hv, W)
+    drafts = make_drafts(orc["id"].reshape(wk.B, wk.k + 1), wk, ids)
+    g = gpu_verify(dev_bf16(hv), W_d, drafts, wk.B, wk.k)
+    check_rows(g["argmax"].ravel(), g["logit"].ravel(), orc, hv, W, None)
+    check_accept(g, drafts, wk.B, wk.k)
+
+
+EXACT_SHAPES = [  # (M, N, H)
+    (1, 1, 8), (1, 1000, 8), (3, 4097, 256), (1, 70001, 2048), (4, 12345, 2560),
+    (8, 3001, 4096), (2, 999, 5120), (1, 257, 16384), (9, 2000, 512), (32, 5000, 1024),
+    (5, 777, 3000), (1, 65, 24),
+]
+
+
+@pytest.mark.parametrize("M,N,H", EXACT_SHAPES)
+@pytest.mark.parametrize("with_ids", [False, True])
+def test_draft_exact_grid(torch, mtp, M, N, H, with_ids):
+    """Inputs on the q/16 grid: every fp32 sum is exact in any order, so the
+    GPU logits must equal the oracle's bit for bit and the many exact ties
+    must go to the lowest id."""
+    seed = 1000 + M * 7 + N + H
+    x = wl.exact_grid_bf16((M, H), seed, 1)
+    w = wl.exact_grid_bf16((N, H), seed, 2)
+    ids = np.sort(wl.rng(seed, 3).choice(3 * N + 5, size=N, replace=False)).astype(np.int32) \
+        if with_ids else None
+    g_ids, g_logit = gpu_draft(dev_bf16(x), dev_bf16(w), None if ids is None else dev_i32(ids))
+    exact_logit_match(g_ids, g_logit, x, w, ids)
+
+
+@pytest.mark.parametrize("B,k,H,V", [(1, 3, 256, 4096), (3, 2, 1024, 5003), (2, 15, 512, 3001),
+                                     (8, 3, 4096, 20000), (1, 0, 2048, 777), (5, 1, 8, 300)])
+def test_verify_exact_grid(torch, mtp, B, k, H, V):
+    seed = 77 + B + k + H + V
+    hv = wl.exact_grid_bf16((B * (k + 1), H), seed, 1)
+    W = wl.exact_grid_bf16((V, H), seed, 2)
+    orc = oracle.argmax(hv, W)
+    t = orc["id"].reshape(B, k + 1)
+    ids = np.arange(V, dtype=np.int32)
+    drafts = wl.select_drafts(t, wl.agreement_draws(B, k, 0.6, V, seed), ids)
+    g = gpu_verify(dev_bf16(hv), dev_bf16(W), drafts, B, k)
+    assert np.array_equal(g["argmax"].ravel(), orc["id"])
+    assert np.array_equal(g["logit"].ravel().astype(np.float32), orc["logit"])
+    exp = oracle.accept(drafts, t)
+    assert np.array_equal(g["accept"], exp["accept"])
+    assert np.array_equal(g["tokens"], exp["tokens"])
+
+
+def test_verify_special_drafts(torch, mtp):
+    """All drafts right -> accept k with the bonus; all wrong -> accept 0;
+    drafts outside the vocabulary are just disagreements."""
+    B, k, H, V = 4, 3, 512, 3000
+    hv = wl.exact_grid_bf16((B * (k + 1), H), 5, 1)
+    W = wl.exact_grid_bf16((V, H), 5, 2)
+    t = oracle.argmax(hv, W)["id"].reshape(B, k + 1)
+    W_d, hv_d = dev_bf16(W), dev_bf16(hv)
+    g = gpu_verify(hv_d, W_d, t[:, :k], B, k)
+    assert np.all(g["accept"] == k) and np.array_equal(g["tokens"], t)
+    bad = np.where(t[:, :k] == 0, 1, -t[:, :k] - 5).astype(np.int32)
+    bad[1, 0] = 2 ** 31 - 1
+    g = gpu_verify(hv_d, W_d, bad, B, k)
+    assert np.all(g["accept"] == 0)
+    assert np.array_equal(g["tokens"][:, 0], t[:, 0]) and np.all(g["tokens"][:, 1:] == -1)
+
+
+def test_duplicate_rows_tie_to_lowest_id(torch, mtp):
+    """Random N(0,0.02) head with the winner's row copied below and above it:
+    the copies score bit-identically on the GPU and the lowest id wins."""
+    V, H, M = 30000, 2048, 3
+    W = wl.head_weights(V, H, 42)
+    h = wl.hidden_states(M, H, 42)
+    win = oracle.argmax(h, W)["id"]
+    for m in range(M):
+        j1 = int(win[m])
+        lo = (j1 * 7919 + 13) % max(j1, 1) if j1 > 0 else None
+        hi = j1 + 1 + (j1 * 104729) % (V - j1 - 1) if j1 < V - 1 else None
+        for j2 in (lo, hi):
+            if j2 is not None and j2 != j1:
+                W[j2] = W[j1]
+    orc = oracle.argmax(h, W)
+    for m in range(M):
+        assert orc["runner_exact"][m] == orc["exact"][m]      # the tie holds
+    g_ids, g_logit = gpu_draft(dev_bf16(h), dev_bf16(W), None)
+    check_rows(g_ids, g_logit, orc, h, W, None, strict=range(M))
+    ids = np.arange(V, dtype=np.int32)
+    g = gpu_verify(dev_bf16(np.concatenate([h, h[:1]])), dev_bf16(W), np.zeros((1, 3), np.int32),
+                   1, 3)
+    assert list(g["argmax"].ravel()[:3]) == list(orc["id"])
+    del ids
+
+
+def test_determinism_across_launch_shapes(torch, mtp):
+    """Bit-identical outputs for repeated calls and any grid size."""
+    V, H = 50000, 2048
+    W = wl.head_weights(V, H, 9)
+    h = wl.hidden_states(4, H, 9)
+    W_d, h_d = dev_bf16(W), dev_bf16(h)
+    ref = None
+    for bpc in (0, 1, 2, 3, 4, 8, 16, 0):
+        r = gpu_draft(h_d, W_d, None, blocks_per_cu=bpc)
+        if ref is None:
+            ref = r
+        assert np.array_equal(r[0], ref[0])
+        assert np.array_equal(r[1].view(np.uint32), ref[1].view(np.uint32))
+    check_rows(ref[0], ref[1], oracle.argmax(h, W), h, W, None)
+    vref = None
+    for bpc in (1, 2, 5, 16):
+        g = gpu_verify(h_d, W_d, np.zeros((1, 3), np.int32), 1, 3, blocks_per_cu=bpc)
+        if vref is None:
+            vref = g
+        assert np.array_equal(g["argmax"], vref["argmax"])
+        assert np.array_equal(g["logit"].view(np.uint32), vref["logit"].view(np.uint32))
+
+
+def test_workspace_left_zeroed(torch, mtp):
+    V, H, M = 9000, 1024, 5
+    W_d = dev_bf16(wl.head_weights(V, H, 3))
+    h_d = dev_bf16(wl.hidden_states(M, H, 3))
+    nbytes = mtp.mtp_draft_workspace_bytes(M, V, H)
+    ws = torch.full((nbytes // 8 + 4,), -1, dtype=torch.int64, device="cuda")
+    mtp.mtp_workspace_init(ws)
+    torch.cuda.synchronize()
+    assert int(ws.abs().sum()) == 0
+    out = torch.empty(M, dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        mtp.mtp_draft_argmax(h_d, W_d, None, out, None, ws=ws)
+        torch.cuda.synchronize()
+        assert int(ws.abs().sum()) == 0
+    B, k = 2, 3
+    nbytes = mtp.mtp_verify_workspace_bytes(B, k, V, H)
+    ws = torch.zeros((nbytes // 8,), dtype=torch.int64, device="cuda")
+    hv_d = dev_bf16(wl.hidden_states(B * (k + 1), H, 4))
+    a = torch.empty((B, k + 1), dtype=torch.int32, device="cuda")
+    acc = torch.empty(B, dtype=torch.int32, device="cuda")
+    tok = torch.empty((B, k + 1), dtype=torch.int32, device="cuda")
+    d = torch.zeros((B, k), dtype=torch.int32, device="cuda")
+    mtp.mtp_verify_accept(hv_d, W_d, d, B, k, a, acc, tok, ws=ws)
+    torch.cuda.synchronize()
+    assert int(ws.abs().sum()) == 0
+
+
+def test_pack_candidates(torch, mtp):
+    V, H, C = 20000, 2560, 5000
+    W = wl.head_weights(V, H, 8)
+    ids = wl.candidate_ids(V, C, 8)
+    table_d = torch.empty((C, H), dtype=torch.int16, device="cuda")
+    mtp.mtp_pack_candidates(dev_bf16(W), dev_i32(ids), table_d)
+    torch.cuda.synchronize()
+    assert np.array_equal(table_d.cpu().numpy().view(np.uint16), oracle.pack(W, ids))
+    # ids outside [0, V) are documented to yield zero rows, never a read
+    bad = np.array([5, -3, V, 7], np.int32)
+    t2 = torch.full((4, H), 3, dtype=torch.int16, device="cuda")
+    mtp.mtp_pack_candidates(dev_bf16(W), dev_i32(bad), t2)
+    t2 = t2.cpu().numpy().view(np.uint16)
+    assert np.array_equal(t2[0], W[5]) and np.array_equal(t2[3], W[7])
+    assert not t2[1].any() and not t2[2].any()
+
+
+@pytest.mark.parametrize("G", [2, 3, 4])
+def test_shard_exchange_equals_unsharded(torch, mtp, G):
+    """Split the candidate table into G contiguous shards (one per would-be
+    rank), run the draft call per shard with its id slice, and merge the G
+    (score, id) pairs with the same rule: the result equals the unsharded
+    call bit for bit."""
+    V, H, C, M = 60000, 2048, 24000, 3
+    W = wl.head_weights(V, H, 31)
+    ids = wl.candidate_ids(V, C, 31)
+    table = oracle.pack(W, ids)
+    h_d = dev_bf16(wl.hidden_states(M, H, 31))
+    full = gpu_draft(h_d, dev_bf16(table), dev_i32(ids))
+    bounds = np.linspace(0, C, G + 1).astype(int)
+    parts = [gpu_draft(h_d, dev_bf16(table[a:b]), dev_i32(ids[a:b]))
+             for a, b in zip(bounds[:-1], bounds[1:])]
+    for m in range(M):
+        best_id, best_v = None, None
+        for pid, pv in parts:
+            if best_id is None or pv[m] > best_v or (pv[m] == best_v and pid[m] < best_id):
+                best_id, best_v = int(pid[m]), pv[m]
+        assert best_id == int(full[0][m])
+        assert np.float32(best_v).view(np.uint32) == np.float32(full[1][m]).view(np.uint32)
