@@ -1,8 +1,8 @@
 // Device-side building blocks shared by the draft / verify kernels (gfx950).
 //
 //  * bf16 dot products on v_dot2c_f32_bf16 (two bf16 products + fp32 add),
-//  * wave64 sums on DPP and the gfx950 permlane swaps (every lane ends with
-//    the same, bit-identical total),
+//  * wave64 sums on DPP and lane reads (every lane ends with the same,
+//    bit-identical total),
 //  * the (score, row) order used by every argmax: larger score first, equal
 //    scores to the lower row (rows are ascending in token id, so the lower
 //    row is the lower id), packed into one 64-bit key so a single unsigned
@@ -46,24 +46,23 @@ __device__ __forceinline__ float dpp_f32(float v) {
       float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
 }
 
-// Sum over the 64 lanes; every lane returns the same bits. The pairing is the
-// same for every call, so identical inputs give identical totals.
+// Sum over the 64 lanes; every lane returns the same bits. Within each 16-lane
+// row a DPP butterfly leaves the row's sum in all its lanes; the four row sums
+// are then read out (v_readlane) and added as (r0 + r1) + (r2 + r3). The
+// pairing never changes, so identical inputs give identical totals.
+// (The gfx950 permlane16/32 swaps are not used here: with both operands the
+// same value, the compiler folds the two swap results into one.)
 __device__ __forceinline__ float wave_sum(float v) {
   v += dpp_f32<0xB1>(v);   // quad_perm [1,0,3,2]: lane ^ 1
   v += dpp_f32<0x4E>(v);   // quad_perm [2,3,0,1]: lane ^ 2
   v += dpp_f32<0x141>(v);  // row_half_mirror: quad 0 <-> quad 1 of each 8
   v += dpp_f32<0x140>(v);  // row_mirror: half 0 <-> half 1 of each 16
-  {
-    uint32_t u = __builtin_bit_cast(uint32_t, v);
-    auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);  // rows 0<->1, 2<->3
-    v = __builtin_bit_cast(float, p[0]) + __builtin_bit_cast(float, p[1]);
-  }
-  {
-    uint32_t u = __builtin_bit_cast(uint32_t, v);
-    auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);  // halves 0<->1
-    v = __builtin_bit_cast(float, p[0]) + __builtin_bit_cast(float, p[1]);
-  }
-  return v;
+  const int u = __builtin_bit_cast(int, v);
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(u, 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(u, 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(u, 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(u, 48));
+  return (r0 + r1) + (r2 + r3);
 }
 
 // True if (v, i) beats (bv, bi): larger score, or equal score and lower row.
