@@ -1,0 +1,284 @@
+#!/usr/bin/env python3
+"""Throughput of the MTP draft / verify LM-head path on one MI355X.
+
+One step is one MTP round of the workload: its draft calls (GEMV + argmax over
+the packed candidate table) followed by one verify call (GEMM + per-row argmax
++ greedy acceptance over the full head). Default workload: MTP3 single stream,
+H=2048, 248,320-row head, 65,536-row candidate table, 3 draft calls (M=1) and
+one verify call (M=4).
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME]
+
+Inputs are seeded synthetic data (N(0,0.02) bf16 head, N(0,1) bf16 hidden
+states, seeded sorted candidate subset), resident in HBM before timing. The
+draft calls of one step read three different copies of the candidate table, so
+no call is served from the 256 MB Infinity Cache by its predecessor; the
+verify head (>= 1 GB) cannot stay cached between steps. Kernel durations come
+from HIP events recorded around every launch on the launch stream inside the
+timed region. Prints one JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("draft/verify calls/s and achieved HBM GB/s (% peak) at 248,320-vocab, 64K draft")
+HBM_PEAK_GBPS = 8000.0
+KERNEL_SOURCES = ("common.hpp", "gemv_valu.hip", "gemm_mfma.hip", "launch.hpp", "api.cpp")
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="mtp3_single")
+    ap.add_argument("--table-copies", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="wall-clock budget of the CPU oracle sample")
+    return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "speculative_decoding_argmax_amd", "csrc")
+    for name in KERNEL_SOURCES:
+        p = os.path.join(csrc, name)
+        if os.path.exists(p):
+            h.update(name.encode())
+            h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of
+    this kernel and workload, if it was taken from the current sources."""
+    p = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_pmc.txt")
+    if not os.path.exists(p):
+        return None
+    text = open(p).read()
+    m_hash = re.search(r"^kernel_source_hash:\s*(\S+)", text, re.M)
+    m_bytes = re.search(r"^hbm_bytes_per_launch:\s*([0-9.eE+]+)", text, re.M)
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
+        return None
+    return float(m_bytes.group(1))
+
+
+def main() -> int:
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this path has no "
+              "multi-GPU mode; the sharded design is described in DESIGN.md.", file=sys.stderr)
+        return 2
+    import torch
+
+    from speculative_decoding_argmax_amd import mtp
+    from speculative_decoding_argmax_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a HIP device", file=sys.stderr)
+        return 2
+    wk = wl.workload(args.workload)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    t0 = time.time()
+    head = wl.head_weights(wk.V, wk.H, wk.seed)
+    ids = wl.candidate_ids(wk.V, wk.C, wk.seed)
+    hiddens = [wl.hidden_states(wk.Md, wk.H, wk.seed, block=c) for c in range(wk.draft_calls)]
+    hv = wl.hidden_states(wk.Mv, wk.H, wk.seed, block=100)
+
+    def up(a, dt=np.int16):
+        return torch.from_numpy(np.ascontiguousarray(a).view(dt)).to(dev)
+
+    head_d = up(head)
+    ids_d = up(ids, np.int32)
+    tables = []
+    for _ in range(max(1, args.table_copies)):
+        t = torch.empty((wk.C, wk.H), dtype=torch.int16, device=dev)
+        mtp.mtp_pack_candidates(head_d, ids_d, t)
+        tables.append(t)
+    h_d = [up(h) for h in hiddens]
+    hv_d = up(hv)
+    out_ids = [torch.empty(wk.Md, dtype=torch.int32, device=dev) for _ in range(wk.draft_calls)]
+    out_logit = [torch.empty(wk.Md, dtype=torch.float32, device=dev)
+                 for _ in range(wk.draft_calls)]
+    ws_d = mtp.alloc_workspace(mtp.mtp_draft_workspace_bytes(wk.Md, wk.C, wk.H), dev)
+    ws_v = mtp.alloc_workspace(mtp.mtp_verify_workspace_bytes(wk.B, wk.k, wk.V, wk.H), dev)
+    v_arg = torch.empty((wk.B, wk.k + 1), dtype=torch.int32, device=dev)
+    v_logit = torch.empty((wk.B, wk.k + 1), dtype=torch.float32, device=dev)
+    v_acc = torch.empty(wk.B, dtype=torch.int32, device=dev)
+    v_tok = torch.empty((wk.B, wk.k + 1), dtype=torch.int32, device=dev)
+    # drafts with the workload's agreement rate against the target's argmax
+    # (taken from one untimed verify call; the timed calls only read them)
+    zero_d = torch.zeros((wk.B, wk.k), dtype=torch.int32, device=dev)
+    mtp.mtp_verify_accept(hv_d, head_d, zero_d, wk.B, wk.k, v_arg, v_acc, v_tok, v_logit, ws=ws_v)
+    torch.cuda.synchronize()
+    t_now = v_arg.cpu().numpy()
+    if wk.p is None:
+        drafts = wl.uniform_drafts(wk.B, wk.k, ids, wk.seed)
+    else:
+        drafts = wl.select_drafts(t_now, wl.agreement_draws(wk.B, wk.k, wk.p, wk.C, wk.seed), ids)
+    drafts_d = up(drafts, np.int32)
+    setup_s = time.time() - t0
+
+    n_tab = len(tables)
+
+    def step(i: int, ev=None):
+        for c in range(wk.draft_calls):
+            if ev is not None:
+                ev[0][c].record(stream)
+            mtp.mtp_draft_argmax(h_d[c], tables[(i * wk.draft_calls + c) % n_tab], ids_d,
+                                 out_ids[c], out_logit[c], ws=ws_d)
+            if ev is not None:
+                ev[1][c].record(stream)
+        if ev is not None:
+            ev[2].record(stream)
+        mtp.mtp_verify_accept(hv_d, head_d, drafts_d, wk.B, wk.k, v_arg, v_acc, v_tok, v_logit,
+                              ws=ws_v)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = []
+    for _ in range(K):
+        evs.append(([torch.cuda.Event(enable_timing=True) for _ in range(wk.draft_calls)],
+                    [torch.cuda.Event(enable_timing=True) for _ in range(wk.draft_calls)],
+                    torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)))
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(K):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    t_total = time.perf_counter() - t_start
+
+    draft_ms = [evs[i][0][c].elapsed_time(evs[i][1][c]) for i in range(K)
+                for c in range(wk.draft_calls)]
+    verify_ms = [evs[i][2].elapsed_time(evs[i][3]) for i in range(K)]
+
+    # Untimed context: the same calls without per-launch events, and the
+    # draft call re-reading one table (Infinity Cache may serve part of it).
+    torch.cuda.synchronize()
+    tq = time.perf_counter()
+    for i in range(K):
+        step(i)
+    torch.cuda.synchronize()
+    t_noev = time.perf_counter() - tq
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(K):
+        mtp.mtp_draft_argmax(h_d[0], tables[0], ids_d, out_ids[0], out_logit[0], ws=ws_d)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    warm_draft_us = e0.elapsed_time(e1) * 1000.0 / K
+
+    H, C, V, Md, Mv = wk.H, wk.C, wk.V, wk.Md, wk.Mv
+    # algorithmic bytes: weight rows + hidden rows + small outputs (winner ids,
+    # logits; verify also reads drafts and writes acceptance)
+    draft_bytes = C * H * 2 + Md * H * 2 + Md * (4 + 4 + 4)
+    verify_bytes = V * H * 2 + Mv * H * 2 + wk.B * wk.k * 4 + Mv * (4 + 4 + 4) + wk.B * 4
+    d_us = statistics.mean(draft_ms) * 1000.0
+    v_us = statistics.mean(verify_ms) * 1000.0
+    calls_per_step = wk.draft_calls + 1
+    value = calls_per_step * K / t_total
+
+    def stats(ms, nbytes):
+        us = [m * 1000.0 for m in ms]
+        mean = statistics.mean(us)
+        q = np.percentile(us, [10, 50, 90])
+        return {"us_mean": round(mean, 2), "us_p10": round(float(q[0]), 2),
+                "us_p50": round(float(q[1]), 2), "us_p90": round(float(q[2]), 2),
+                "calls_per_s": round(1e6 / mean, 1), "bytes": int(nbytes),
+                "GBps": round(nbytes / mean / 1e3, 1),
+                "frac_peak": round(nbytes / mean / 1e3 / HBM_PEAK_GBPS, 4)}
+
+    draft_stats = stats(draft_ms, draft_bytes)
+    verify_stats = stats(verify_ms, verify_bytes)
+    # dominant kernel of the step: the one with more time per step
+    if v_us >= d_us * wk.draft_calls:
+        dom_name, dom_bytes, dom_us = "verify", verify_bytes, v_us
+    else:
+        dom_name, dom_bytes, dom_us = "draft", draft_bytes, d_us
+    traffic = measured_traffic(dom_name, wk.name)
+    achieved = dom_bytes / dom_us / 1e3
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": traffic, "kernel": dom_name,
+                "algorithmic_bytes_per_launch": int(dom_bytes)}
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "calls/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_total * 1000.0 / K, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{wk.name}: {wk.draft_calls} draft calls (M={Md}, {C}-row table) + 1 "
+                        f"verify call (M={Mv}, {V}-row head), H={H}",
+            "H": H, "V": V, "C": C, "B": wk.B, "k": wk.k, "draft_calls": wk.draft_calls,
+            "accumulate": "f32", "table_copies": n_tab, "seed": wk.seed,
+        },
+        "calls": {"draft": draft_stats, "verify": verify_stats},
+        "context": {
+            "ms_per_step_without_kernel_events": round(t_noev * 1000.0 / K, 4),
+            "draft_same_table_us": round(warm_draft_us, 2),
+            "setup_s": round(setup_s, 1),
+        },
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wk, head, ids, hiddens, hv, drafts,
+                                              args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def cpu_baseline(wk, head, ids, hiddens, hv, drafts, budget_s):
+    """The CPU oracle on the same step: its draft calls and verify call,
+    repeated until the time budget is spent (at least once)."""
+    import oracle
+    table = oracle.pack(head, ids)
+    times = []
+    t_begin = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        for h in hiddens:
+            oracle.draft(h, table, ids)
+        oracle.verify(hv, head, wk.B, wk.k, drafts)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_begin >= budget_s:
+            break
+    step_s = statistics.median(times)
+    return {"value": round((wk.draft_calls + 1) / step_s, 3), "unit": "calls/s",
+            "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"{len(times)} full {wk.name} step(s) ({wk.draft_calls} draft + 1 verify "
+                      f"call), median {step_s:.3f} s per step"}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

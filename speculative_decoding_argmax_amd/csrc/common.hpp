@@ -105,28 +105,44 @@ struct RowSink {
 // Called by every thread of every workgroup after the workgroup's per-row
 // winners for rows [m_begin, m_begin + m_count) sit in wg_val / wg_row
 // (wg_row < 0: the workgroup saw no row). Must be reached by all threads.
+//
+// All cross-workgroup traffic goes through atomic read-modify-writes, which
+// the hardware performs at the memory's coherence point, so no agent-scope
+// fence is needed (on a multi-XCD gfx950 such a fence writes back and
+// invalidates the whole L2 of the XCD, once per workgroup). Ordering: every
+// key update returns its old value before the workgroup's barrier (the
+// returned value feeds an LDS write), and only then does one thread take a
+// ticket; the last ticket holder reads the keys with atomic exchanges, which
+// also clear them for the next call.
 __device__ __forceinline__ void finish_rows(const RowSink &s, const float *wg_val,
                                             const int64_t *wg_row, int m_begin, int m_count) {
   __shared__ int s_last;
+  __shared__ int s_seen;
   const int tid = threadIdx.x;
   const int nthreads = blockDim.x;
+  if (tid == 0) s_seen = 0;
+  __syncthreads();
   for (int t = tid; t < m_count; t += nthreads) {
-    if (wg_row[t] >= 0) atomicMax(&s.keys[m_begin + t], make_key(wg_val[t], (uint32_t)wg_row[t]));
+    if (wg_row[t] >= 0) {
+      const unsigned long long key = make_key(wg_val[t], (uint32_t)wg_row[t]);
+      const unsigned long long old = __hip_atomic_fetch_max(&s.keys[m_begin + t], key,
+                                                            __ATOMIC_RELAXED,
+                                                            __HIP_MEMORY_SCOPE_AGENT);
+      if (old >= key) s_seen = 1;  // consumes the returned value
+    }
   }
-  __threadfence();
   __syncthreads();
   if (tid == 0) {
     const uint32_t nblocks = gridDim.x * gridDim.y * gridDim.z;
     const uint32_t prev =
-        __hip_atomic_fetch_add(s.ticket, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(s.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_last = (prev == nblocks - 1);
   }
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
   for (int m = tid; m < s.M; m += nthreads) {
     const unsigned long long key =
-        __hip_atomic_load(&s.keys[m], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_exchange(&s.keys[m], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     int32_t id = -1;
     float val = __builtin_nanf("");
     if (key != 0ull) {
@@ -136,7 +152,6 @@ __device__ __forceinline__ void finish_rows(const RowSink &s, const float *wg_va
     }
     s.out_ids[m] = id;
     if (s.out_logit) s.out_logit[m] = val;
-    __hip_atomic_store(&s.keys[m], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   if (s.k >= 0) {
     __syncthreads();  // out_ids (the target argmax) written by this workgroup
@@ -149,7 +164,7 @@ __device__ __forceinline__ void finish_rows(const RowSink &s, const float *wg_va
       for (int p = 0; p <= k; ++p) s.out_tokens[(int64_t)b * (k + 1) + p] = p <= n ? t[p] : -1;
     }
   }
-  if (tid == 0) __hip_atomic_store(s.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) __hip_atomic_exchange(s.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace mtp
