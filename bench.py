@@ -139,30 +139,25 @@ def main() -> int:
     n_tab = len(tables)
 
     def step(i: int, ev=None):
+        # ev: (before drafts, after drafts = before verify, after verify)
+        if ev is not None:
+            ev[0].record(stream)
         for c in range(wk.draft_calls):
-            if ev is not None:
-                ev[0][c].record(stream)
             mtp.mtp_draft_argmax(h_d[c], tables[(i * wk.draft_calls + c) % n_tab], ids_d,
                                  out_ids[c], out_logit[c], ws=ws_d)
-            if ev is not None:
-                ev[1][c].record(stream)
         if ev is not None:
-            ev[2].record(stream)
+            ev[1].record(stream)
         mtp.mtp_verify_accept(hv_d, head_d, drafts_d, wk.B, wk.k, v_arg, v_acc, v_tok, v_logit,
                               ws=ws_v)
         if ev is not None:
-            ev[3].record(stream)
+            ev[2].record(stream)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
     K = args.steps
-    evs = []
-    for _ in range(K):
-        evs.append(([torch.cuda.Event(enable_timing=True) for _ in range(wk.draft_calls)],
-                    [torch.cuda.Event(enable_timing=True) for _ in range(wk.draft_calls)],
-                    torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)))
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(K)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(K):
@@ -170,9 +165,10 @@ def main() -> int:
     torch.cuda.synchronize()
     t_total = time.perf_counter() - t_start
 
-    draft_ms = [evs[i][0][c].elapsed_time(evs[i][1][c]) for i in range(K)
-                for c in range(wk.draft_calls)]
-    verify_ms = [evs[i][2].elapsed_time(evs[i][3]) for i in range(K)]
+    # per-call durations: the draft block's span over its calls (inter-kernel
+    # gaps included), the verify launch's own span
+    draft_ms = [evs[i][0].elapsed_time(evs[i][1]) / wk.draft_calls for i in range(K)]
+    verify_ms = [evs[i][1].elapsed_time(evs[i][2]) for i in range(K)]
 
     # Untimed context: the same calls without per-launch events, and the
     # draft call re-reading one table (Infinity Cache may serve part of it).

@@ -75,7 +75,9 @@ mtp_status run_rows(const mtp_bf16 *X, int M, int H, const mtp_bf16 *W, int64_t 
   int cus = 0;
   hipError_t e = current_cus(&cus);
   if (e != hipSuccess) return hip_fail(e);
-  const int per_cu = (cfg && cfg->blocks_per_cu > 0) ? cfg->blocks_per_cu : 2;
+  // one resident workgroup per CU for rows up to 2,560 wide, two beyond
+  // (prefetching variant; measured best on MI355X at the workload shapes)
+  const int per_cu = (cfg && cfg->blocks_per_cu > 0) ? cfg->blocks_per_cu : (ncl <= 5 ? 1 : 2);
   mtp::ValuLaunch L;
   L.X = X;
   L.W = W;
@@ -83,6 +85,7 @@ mtp_status run_rows(const mtp_bf16 *X, int M, int H, const mtp_bf16 *W, int64_t 
   L.N = N;
   L.nch = nch;
   L.max_blocks_x = per_cu * cus;
+  L.prefetch = true;
   L.sink = sink;
   L.stream = stream;
   const int mr = mtp::valu_rows_for(M, ncl);

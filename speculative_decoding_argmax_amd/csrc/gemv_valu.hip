@@ -22,6 +22,15 @@ namespace mtp {
 constexpr int kValuThreads = 256;
 constexpr int kValuWaves = kValuThreads / kWave;
 
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+// Weight rows are read exactly once per call: non-temporal loads keep them
+// from displacing the hidden vector and the workspace in the caches.
+__device__ __forceinline__ uint4 load_stream(const uint4 *p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // Loads RB rows x NCL chunks of this lane's slice. ROWS_OK / COLS_OK say the
 // whole block lies inside the table, so no predication is needed.
 template <int RB, int NCL, bool ROWS_OK, bool COLS_OK>
@@ -33,12 +42,24 @@ __device__ __forceinline__ void load_block(uint4 (&w)[RB][NCL], const uint4 *__r
 #pragma unroll
     for (int c = 0; c < NCL; ++c) {
       const bool ok = (ROWS_OK || r0 + i < N) && (COLS_OK || lane + kWave * c < nch);
-      w[i][c] = ok ? row[kWave * c] : make_uint4(0u, 0u, 0u, 0u);
+      w[i][c] = ok ? load_stream(row + kWave * c) : make_uint4(0u, 0u, 0u, 0u);
     }
   }
 }
 
-template <int MR, int NCL, int RB, bool EXACT>
+template <int RB, int NCL, bool EXACT>
+__device__ __forceinline__ void load_rows(uint4 (&w)[RB][NCL], const uint4 *__restrict__ W,
+                                          int64_t r0, int64_t N, int nch, int lane) {
+  if (r0 + RB <= N)
+    load_block<RB, NCL, true, EXACT>(w, W, r0, N, nch, lane);
+  else
+    load_block<RB, NCL, false, EXACT>(w, W, r0, N, nch, lane);
+}
+
+// MR hidden rows, NCL 16-byte chunks per lane and row, RB table rows per wave
+// iteration; PF: the next iteration's rows are loaded before this one's are
+// reduced; EXACT: H == NCL * 512 (no column predication).
+template <int MR, int NCL, int RB, bool PF, bool EXACT>
 __global__ void __launch_bounds__(kValuThreads)
     gemv_argmax_valu(const uint4 *__restrict__ X, const uint4 *__restrict__ W, int M, int64_t N,
                      int nch, RowSink sink) {
@@ -71,12 +92,21 @@ __global__ void __launch_bounds__(kValuThreads)
   }
 
   const int64_t stride = (int64_t)gridDim.x * kValuWaves * RB;
-  for (int64_t r0 = ((int64_t)blockIdx.x * kValuWaves + wave) * RB; r0 < N; r0 += stride) {
+  // wave-uniform row cursor, kept in scalar registers
+  int64_t r0 = ((int64_t)blockIdx.x * kValuWaves + __builtin_amdgcn_readfirstlane(wave)) * RB;
+  uint4 nxt[RB][NCL];
+  if (PF && r0 < N) load_rows<RB, NCL, EXACT>(nxt, W, r0, N, nch, lane);
+  for (; r0 < N; r0 += stride) {
     uint4 w[RB][NCL];
-    if (r0 + RB <= N)
-      load_block<RB, NCL, true, EXACT>(w, W, r0, N, nch, lane);
-    else
-      load_block<RB, NCL, false, EXACT>(w, W, r0, N, nch, lane);
+    if (PF) {
+#pragma unroll
+      for (int i = 0; i < RB; ++i)
+#pragma unroll
+        for (int c = 0; c < NCL; ++c) w[i][c] = nxt[i][c];
+      if (r0 + stride < N) load_rows<RB, NCL, EXACT>(nxt, W, r0 + stride, N, nch, lane);
+    } else {
+      load_rows<RB, NCL, EXACT>(w, W, r0, N, nch, lane);
+    }
     float acc[MR][RB];
 #pragma unroll
     for (int r = 0; r < MR; ++r)
@@ -126,27 +156,42 @@ __global__ void __launch_bounds__(kValuThreads)
   finish_rows(sink, f_val, f_row, m0, min(MR, M - m0));
 }
 
-// Rows per wave iteration: about 16 chunk loads (16 KiB per wave) in flight.
+// Two instantiated variants per (MR, NCL): RB rows per iteration with no
+// prefetch (about 16 chunk loads in flight per wave), and the default: one or
+// two rows per iteration with the next iteration's rows already in flight
+// (measured on MI355X: 41 us for 65,536 x 2,048 and 144 us for the
+// 248,320 x 2,048 verify with 4 hidden rows, at one workgroup per CU).
 template <int NCL>
-constexpr int valu_rows_per_iter() {
-  return NCL >= 16 ? 1 : (16 / NCL);
+constexpr int valu_rb_plain() {
+  return NCL >= 16 ? 1 : (16 / NCL > 4 ? 4 : 16 / NCL);
+}
+template <int NCL>
+constexpr int valu_rb_prefetch() {
+  return NCL <= 5 ? 2 : 1;
 }
 
-template <int MR, int NCL>
-static hipError_t launch_mr_ncl(const ValuLaunch &L) {
-  constexpr int RB = valu_rows_per_iter<NCL>();
+template <int MR, int NCL, int RB, bool PF>
+static hipError_t launch_variant(const ValuLaunch &L) {
   const int64_t row_blocks = (L.N + RB - 1) / RB;
   const int64_t want = (row_blocks + kValuWaves - 1) / kValuWaves;
   const int gx = (int)(want < L.max_blocks_x ? want : L.max_blocks_x);
   const int gy = (L.M + MR - 1) / MR;
   if (L.nch == NCL * kWave)
-    hipLaunchKernelGGL((gemv_argmax_valu<MR, NCL, RB, true>), dim3(gx, gy), dim3(kValuThreads), 0,
-                       L.stream, (const uint4 *)L.X, (const uint4 *)L.W, L.M, L.N, L.nch, L.sink);
+    hipLaunchKernelGGL((gemv_argmax_valu<MR, NCL, RB, PF, true>), dim3(gx, gy),
+                       dim3(kValuThreads), 0, L.stream, (const uint4 *)L.X, (const uint4 *)L.W,
+                       L.M, L.N, L.nch, L.sink);
   else
-    hipLaunchKernelGGL((gemv_argmax_valu<MR, NCL, RB, false>), dim3(gx, gy), dim3(kValuThreads),
-                       0, L.stream, (const uint4 *)L.X, (const uint4 *)L.W, L.M, L.N, L.nch,
-                       L.sink);
+    hipLaunchKernelGGL((gemv_argmax_valu<MR, NCL, RB, PF, false>), dim3(gx, gy),
+                       dim3(kValuThreads), 0, L.stream, (const uint4 *)L.X, (const uint4 *)L.W,
+                       L.M, L.N, L.nch, L.sink);
   return hipGetLastError();
+}
+
+template <int MR, int NCL>
+static hipError_t launch_mr_ncl(const ValuLaunch &L) {
+  if (L.prefetch)
+    return launch_variant<MR, NCL, valu_rb_prefetch<NCL>(), true>(L);
+  return launch_variant<MR, NCL, valu_rb_plain<NCL>(), false>(L);
 }
 
 // Chunks per lane that have an instantiation; a request rounds up to the next.
@@ -194,7 +239,7 @@ static hipError_t dispatch_ncl(int ncl, const ValuLaunch &L) {
 }
 
 int valu_total_blocks(const ValuLaunch &L, int mr, int ncl) {
-  const int rb = ncl >= 16 ? 1 : 16 / ncl;
+  const int rb = L.prefetch ? (ncl <= 5 ? 2 : 1) : (ncl >= 16 ? 1 : (16 / ncl > 4 ? 4 : 16 / ncl));
   const int64_t row_blocks = (L.N + rb - 1) / rb;
   const int64_t want = (row_blocks + kValuWaves - 1) / kValuWaves;
   const int gx = (int)(want < L.max_blocks_x ? want : L.max_blocks_x);

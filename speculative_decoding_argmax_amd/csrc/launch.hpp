@@ -15,6 +15,7 @@ struct ValuLaunch {
   int64_t N;
   int nch;           // H / 8 (16-byte chunks per row)
   int max_blocks_x;  // cap on workgroups along the row dimension
+  bool prefetch;     // prefetching variant (fewer rows per iteration)
   RowSink sink;
   hipStream_t stream;
 };
