@@ -36,7 +36,11 @@ sys.path.insert(0, ROOT)
 
 METRIC = ("draft/verify calls/s and achieved HBM GB/s (% peak) at 248,320-vocab, 64K draft")
 HBM_PEAK_GBPS = 8000.0
-KERNEL_SOURCES = ("common.hpp", "gemv_valu.hip", "gemm_mfma.hip", "launch.hpp", "api.cpp")
+# sources that define each path's kernels and their launch configuration
+KERNEL_SOURCES = {
+    "valu": ("common.hpp", "gemv_valu.hip", "launch.hpp", "api.cpp"),
+    "mfma": ("common.hpp", "gemm_mfma.hip", "launch.hpp", "api.cpp"),
+}
 
 
 def parse_args():
@@ -52,10 +56,10 @@ def parse_args():
     return ap.parse_args()
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(path: str) -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "speculative_decoding_argmax_amd", "csrc")
-    for name in KERNEL_SOURCES:
+    for name in KERNEL_SOURCES[path]:
         p = os.path.join(csrc, name)
         if os.path.exists(p):
             h.update(name.encode())
@@ -63,7 +67,7 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel: str, workload: str):
+def measured_traffic(kernel: str, workload: str, path: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary of
     this kernel and workload, if it was taken from the current sources."""
     p = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_pmc.txt")
@@ -72,7 +76,7 @@ def measured_traffic(kernel: str, workload: str):
     text = open(p).read()
     m_hash = re.search(r"^kernel_source_hash:\s*(\S+)", text, re.M)
     m_bytes = re.search(r"^hbm_bytes_per_launch:\s*([0-9.eE+]+)", text, re.M)
-    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash(path):
         return None
     return float(m_bytes.group(1))
 
@@ -213,7 +217,9 @@ def main() -> int:
         dom_name, dom_bytes, dom_us = "verify", verify_bytes, v_us
     else:
         dom_name, dom_bytes, dom_us = "draft", draft_bytes, d_us
-    traffic = measured_traffic(dom_name, wk.name)
+    # rows <= 8 per call run on the vector-ALU kernel at these widths
+    dom_rows = wk.Mv if dom_name == "verify" else wk.Md
+    traffic = measured_traffic(dom_name, wk.name, "valu" if dom_rows <= 8 else "mfma")
     achieved = dom_bytes / dom_us / 1e3
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),

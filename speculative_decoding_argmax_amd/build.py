@@ -24,7 +24,9 @@ LIB = os.path.join(LIB_DIR, "libmtp.so")
 ARCH = "gfx950"
 
 # No packed-fp32 instructions: compile ordinary float code to scalar fp32 ops.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Register arrays stay in registers (never promoted to LDS).
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                "-mllvm", "--disable-promote-alloca-to-lds"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
           "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC]
 

@@ -65,31 +65,48 @@ mtp_status check_cfg(const mtp_config *cfg) {
 }
 
 // Score M hidden rows against N table rows and finish through `sink`.
+// Path: the vector-ALU kernel while one pass keeps every hidden row's slice in
+// registers (few rows), the matrix-core kernel beyond.
 mtp_status run_rows(const mtp_bf16 *X, int M, int H, const mtp_bf16 *W, int64_t N,
                     mtp::RowSink sink, hipStream_t stream, const mtp_config *cfg) {
-  const int path = cfg ? cfg->path : MTP_PATH_AUTO;
-  if (path == MTP_PATH_MFMA) return MTP_ERR_UNSUPPORTED;
   const int nch = H / 8;
   const int ncl = mtp::valu_ncl_for(nch);
-  if (ncl == 0) return MTP_ERR_UNSUPPORTED;
+  int path = cfg ? cfg->path : MTP_PATH_AUTO;
+  if (path == MTP_PATH_AUTO)
+    path = (ncl != 0 && mtp::valu_rows_for(M, ncl) >= M) ? MTP_PATH_VALU : MTP_PATH_MFMA;
   int cus = 0;
   hipError_t e = current_cus(&cus);
   if (e != hipSuccess) return hip_fail(e);
-  // one resident workgroup per CU for rows up to 2,560 wide, two beyond
-  // (prefetching variant; measured best on MI355X at the workload shapes)
-  const int per_cu = (cfg && cfg->blocks_per_cu > 0) ? cfg->blocks_per_cu : (ncl <= 5 ? 1 : 2);
-  mtp::ValuLaunch L;
-  L.X = X;
-  L.W = W;
-  L.M = M;
-  L.N = N;
-  L.nch = nch;
-  L.max_blocks_x = per_cu * cus;
-  L.prefetch = true;
-  L.sink = sink;
-  L.stream = stream;
-  const int mr = mtp::valu_rows_for(M, ncl);
-  e = mtp::launch_valu(L, mr, ncl);
+  if (path == MTP_PATH_VALU) {
+    if (ncl == 0) return MTP_ERR_UNSUPPORTED;
+    // one resident workgroup per CU for rows up to 2,560 wide, two beyond
+    // (prefetching variant; measured best on MI355X at the workload shapes)
+    const int per_cu =
+        (cfg && cfg->blocks_per_cu > 0) ? cfg->blocks_per_cu : (ncl <= 5 ? 1 : 2);
+    mtp::ValuLaunch L;
+    L.X = X;
+    L.W = W;
+    L.M = M;
+    L.N = N;
+    L.nch = nch;
+    L.max_blocks_x = per_cu * cus;
+    L.prefetch = true;
+    L.sink = sink;
+    L.stream = stream;
+    e = mtp::launch_valu(L, mtp::valu_rows_for(M, ncl), ncl);
+  } else {
+    const int per_cu = (cfg && cfg->blocks_per_cu > 0) ? cfg->blocks_per_cu : 2;
+    mtp::MfmaLaunch L;
+    L.X = X;
+    L.W = W;
+    L.M = M;
+    L.N = N;
+    L.nch = nch;
+    L.max_blocks_x = per_cu * cus;
+    L.sink = sink;
+    L.stream = stream;
+    e = mtp::launch_mfma(L, mtp::mfma_nb_for(M));
+  }
   if (e != hipSuccess) return hip_fail(e);
   return MTP_OK;
 }

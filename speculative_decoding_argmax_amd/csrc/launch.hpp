@@ -28,6 +28,21 @@ int valu_rows_for(int M, int ncl);
 int valu_total_blocks(const ValuLaunch &L, int mr, int ncl);
 hipError_t launch_valu(const ValuLaunch &L, int mr, int ncl);
 
+struct MfmaLaunch {
+  const void *X;     // hidden [M][H] bf16
+  const void *W;     // table / head [N][H] bf16
+  int M;
+  int64_t N;
+  int nch;           // H / 8
+  int max_blocks_x;  // cap on workgroups along the table
+  RowSink sink;
+  hipStream_t stream;
+};
+
+// Column blocks of 16 hidden rows per pass for M rows.
+int mfma_nb_for(int M);
+hipError_t launch_mfma(const MfmaLaunch &L, int nb);
+
 hipError_t launch_pack(const void *head, int64_t V, int nch, const int32_t *ids, int64_t C,
                        void *table, int num_cus, hipStream_t stream);
 hipError_t launch_fill_zero(void *ws, size_t bytes, hipStream_t stream);

@@ -51,28 +51,36 @@ def test_tiny_workload(torch, mtp):
 EXACT_SHAPES = [  # (M, N, H)
     (1, 1, 8), (1, 1000, 8), (3, 4097, 256), (1, 70001, 2048), (4, 12345, 2560),
     (8, 3001, 4096), (2, 999, 5120), (1, 257, 16384), (9, 2000, 512), (32, 5000, 1024),
-    (5, 777, 3000), (1, 65, 24),
+    (5, 777, 3000), (1, 65, 24), (16, 1025, 640), (17, 333, 1032), (48, 2049, 4096),
+    (160, 1111, 5120), (161, 300, 256), (64, 4000, 2048),
 ]
+
+
+PATHS = {"auto": 0, "valu": 1, "mfma": 2}
 
 
 @pytest.mark.parametrize("M,N,H", EXACT_SHAPES)
 @pytest.mark.parametrize("with_ids", [False, True])
-def test_draft_exact_grid(torch, mtp, M, N, H, with_ids):
+@pytest.mark.parametrize("path", ["auto", "valu", "mfma"])
+def test_draft_exact_grid(torch, mtp, M, N, H, with_ids, path):
     """Inputs on the q/16 grid: every fp32 sum is exact in any order, so the
     GPU logits must equal the oracle's bit for bit and the many exact ties
-    must go to the lowest id."""
+    must go to the lowest id (both kernel paths)."""
     seed = 1000 + M * 7 + N + H
     x = wl.exact_grid_bf16((M, H), seed, 1)
     w = wl.exact_grid_bf16((N, H), seed, 2)
     ids = np.sort(wl.rng(seed, 3).choice(3 * N + 5, size=N, replace=False)).astype(np.int32) \
         if with_ids else None
-    g_ids, g_logit = gpu_draft(dev_bf16(x), dev_bf16(w), None if ids is None else dev_i32(ids))
+    g_ids, g_logit = gpu_draft(dev_bf16(x), dev_bf16(w), None if ids is None else dev_i32(ids),
+                               path=PATHS[path])
     exact_logit_match(g_ids, g_logit, x, w, ids)
 
 
 @pytest.mark.parametrize("B,k,H,V", [(1, 3, 256, 4096), (3, 2, 1024, 5003), (2, 15, 512, 3001),
-                                     (8, 3, 4096, 20000), (1, 0, 2048, 777), (5, 1, 8, 300)])
-def test_verify_exact_grid(torch, mtp, B, k, H, V):
+                                     (8, 3, 4096, 20000), (1, 0, 2048, 777), (5, 1, 8, 300),
+                                     (32, 4, 5120, 3000), (40, 3, 1024, 999)])
+@pytest.mark.parametrize("path", ["auto", "mfma"])
+def test_verify_exact_grid(torch, mtp, B, k, H, V, path):
     seed = 77 + B + k + H + V
     hv = wl.exact_grid_bf16((B * (k + 1), H), seed, 1)
     W = wl.exact_grid_bf16((V, H), seed, 2)
@@ -80,7 +88,7 @@ def test_verify_exact_grid(torch, mtp, B, k, H, V):
     t = orc["id"].reshape(B, k + 1)
     ids = np.arange(V, dtype=np.int32)
     drafts = wl.select_drafts(t, wl.agreement_draws(B, k, 0.6, V, seed), ids)
-    g = gpu_verify(dev_bf16(hv), dev_bf16(W), drafts, B, k)
+    g = gpu_verify(dev_bf16(hv), dev_bf16(W), drafts, B, k, path=PATHS[path])
     assert np.array_equal(g["argmax"].ravel(), orc["id"])
     assert np.array_equal(g["logit"].ravel().astype(np.float32), orc["logit"])
     exp = oracle.accept(drafts, t)
@@ -105,10 +113,11 @@ def test_verify_special_drafts(torch, mtp):
     assert np.array_equal(g["tokens"][:, 0], t[:, 0]) and np.all(g["tokens"][:, 1:] == -1)
 
 
-def test_duplicate_rows_tie_to_lowest_id(torch, mtp):
+@pytest.mark.parametrize("path,M", [("auto", 3), ("mfma", 3), ("mfma", 40)])
+def test_duplicate_rows_tie_to_lowest_id(torch, mtp, path, M):
     """Random N(0,0.02) head with the winner's row copied below and above it:
     the copies score bit-identically on the GPU and the lowest id wins."""
-    V, H, M = 30000, 2048, 3
+    V, H = 30000, 2048
     W = wl.head_weights(V, H, 42)
     h = wl.hidden_states(M, H, 42)
     win = oracle.argmax(h, W)["id"]
@@ -122,32 +131,35 @@ def test_duplicate_rows_tie_to_lowest_id(torch, mtp):
     orc = oracle.argmax(h, W)
     for m in range(M):
         assert orc["runner_exact"][m] == orc["exact"][m]      # the tie holds
-    g_ids, g_logit = gpu_draft(dev_bf16(h), dev_bf16(W), None)
+    g_ids, g_logit = gpu_draft(dev_bf16(h), dev_bf16(W), None, path=PATHS[path])
     check_rows(g_ids, g_logit, orc, h, W, None, strict=range(M))
-    ids = np.arange(V, dtype=np.int32)
-    g = gpu_verify(dev_bf16(np.concatenate([h, h[:1]])), dev_bf16(W), np.zeros((1, 3), np.int32),
-                   1, 3)
-    assert list(g["argmax"].ravel()[:3]) == list(orc["id"])
-    del ids
+    if M == 3:
+        g = gpu_verify(dev_bf16(np.concatenate([h, h[:1]])), dev_bf16(W),
+                       np.zeros((1, 3), np.int32), 1, 3, path=PATHS[path])
+        assert list(g["argmax"].ravel()[:3]) == list(orc["id"])
 
 
-def test_determinism_across_launch_shapes(torch, mtp):
+@pytest.mark.parametrize("path,M", [("auto", 4), ("mfma", 4), ("mfma", 33)])
+def test_determinism_across_launch_shapes(torch, mtp, path, M):
     """Bit-identical outputs for repeated calls and any grid size."""
     V, H = 50000, 2048
     W = wl.head_weights(V, H, 9)
-    h = wl.hidden_states(4, H, 9)
+    h = wl.hidden_states(M, H, 9)
     W_d, h_d = dev_bf16(W), dev_bf16(h)
     ref = None
     for bpc in (0, 1, 2, 3, 4, 8, 16, 0):
-        r = gpu_draft(h_d, W_d, None, blocks_per_cu=bpc)
+        r = gpu_draft(h_d, W_d, None, blocks_per_cu=bpc, path=PATHS[path])
         if ref is None:
             ref = r
         assert np.array_equal(r[0], ref[0])
         assert np.array_equal(r[1].view(np.uint32), ref[1].view(np.uint32))
     check_rows(ref[0], ref[1], oracle.argmax(h, W), h, W, None)
+    if M != 4:
+        return
     vref = None
     for bpc in (1, 2, 5, 16):
-        g = gpu_verify(h_d, W_d, np.zeros((1, 3), np.int32), 1, 3, blocks_per_cu=bpc)
+        g = gpu_verify(h_d, W_d, np.zeros((1, 3), np.int32), 1, 3, blocks_per_cu=bpc,
+                       path=PATHS[path])
         if vref is None:
             vref = g
         assert np.array_equal(g["argmax"], vref["argmax"])
