@@ -74,6 +74,8 @@ typedef enum {
 /* Launch selection for the *_cfg variants (tuning, tests). Zero fields mean
  * "choose automatically"; the plain entry points use all zeros. */
 typedef enum { MTP_PATH_AUTO = 0, MTP_PATH_VALU = 1, MTP_PATH_MFMA = 2 } mtp_path;
+/* (Row-major tables: AUTO picks the vector-ALU kernel for few hidden rows and
+ * the matrix-core kernel beyond. Tiled tables always use the matrix cores.) */
 typedef struct {
   int path;          /* mtp_path */
   int blocks_per_cu; /* workgroups per compute unit of the row-streaming grid (1..16) */
@@ -176,6 +178,63 @@ mtp_status mtp_verify_accept_cfg(const mtp_bf16 *hidden, int B, int k, int H,
                                  int32_t *out_argmax, float *out_logit, int32_t *out_accept,
                                  int32_t *out_tokens, void *ws, size_t ws_bytes,
                                  hipStream_t stream, const mtp_config *cfg);
+
+/*
+ * Tiled tables (batched rows).
+ *
+ * When one call scores many hidden rows (a batch of sequences), the table
+ * rows feed the matrix cores, whose operand is 16 table rows x 32 columns. The
+ * tiled layout stores a table so that each such operand is 1 KiB contiguous
+ * and every 64-row tile is one contiguous stream:
+ *   rows are padded with zero rows to Rp = ceil(R / 64) * 64, columns with
+ *   zeros to Hp = ceil(H / 128) * 128; S = Hp / 32;
+ *   16-byte element e of the buffer (lane = e % 64, f = e / 64, rb = f % 4,
+ *   s = (f / 4) % S, t = f / (4 S)) holds the 8 bf16 values of row
+ *   64 t + 16 rb + lane % 16, columns 32 s + 8 (lane / 16) .. + 8.
+ * The values are the row-major table's; only their order differs. A tiled
+ * call computes the same sums as the row-major call on the same table (up to
+ * fp32 summation order, which can move a pick only inside a near tie). Size:
+ * mtp_tiled_bytes(R, H) = Rp * Hp * 2 bytes (0 if out of range).
+ * Like the packed candidate table, the tiled form is built once (the full
+ * head for verification, the candidate table for drafting) and stays
+ * resident. [Qwen3.8 Flash dual-Spark tuning log, section "read one fewer big
+ * table": both the full head and the small draft table are kept in memory.]
+ */
+size_t mtp_tiled_bytes(int64_t rows, int H);
+
+/* Build a tiled table from the row-major head [V][H] (device): rows ids[i]
+ * (ids device int32 [C], strictly ascending in [0, V)), or, with ids NULL,
+ * the first C rows (C <= V; C == V tiles the whole head). tiled: device,
+ * 16-byte aligned, tiled_bytes >= mtp_tiled_bytes(C, H); written. Rows
+ * whose id is out of range are zero. */
+mtp_status mtp_pack_tiled(const mtp_bf16 *head, int64_t V, int H, const int32_t *ids, int64_t C,
+                          void *tiled, size_t tiled_bytes, hipStream_t stream);
+
+/* mtp_draft_argmax on a tiled candidate table (C rows, built by
+ * mtp_pack_tiled); arguments and results as mtp_draft_argmax. */
+mtp_status mtp_draft_argmax_tiled(const mtp_bf16 *hidden, int M, int H, const void *table_tiled,
+                                  const int32_t *ids, int64_t C, int32_t *out_ids,
+                                  float *out_logit, void *ws, size_t ws_bytes,
+                                  hipStream_t stream);
+mtp_status mtp_draft_argmax_tiled_cfg(const mtp_bf16 *hidden, int M, int H,
+                                      const void *table_tiled, const int32_t *ids, int64_t C,
+                                      int32_t *out_ids, float *out_logit, void *ws,
+                                      size_t ws_bytes, hipStream_t stream,
+                                      const mtp_config *cfg);
+
+/* mtp_verify_accept on a tiled head (V rows, built by mtp_pack_tiled with
+ * ids NULL and C == V); arguments and results as mtp_verify_accept. */
+mtp_status mtp_verify_accept_tiled(const mtp_bf16 *hidden, int B, int k, int H,
+                                   const void *head_tiled, int64_t V, const int32_t *draft,
+                                   int32_t *out_argmax, float *out_logit, int32_t *out_accept,
+                                   int32_t *out_tokens, void *ws, size_t ws_bytes,
+                                   hipStream_t stream);
+mtp_status mtp_verify_accept_tiled_cfg(const mtp_bf16 *hidden, int B, int k, int H,
+                                       const void *head_tiled, int64_t V, const int32_t *draft,
+                                       int32_t *out_argmax, float *out_logit,
+                                       int32_t *out_accept, int32_t *out_tokens, void *ws,
+                                       size_t ws_bytes, hipStream_t stream,
+                                       const mtp_config *cfg);
 
 #ifdef __cplusplus
 }

@@ -111,6 +111,103 @@ mtp_status run_rows(const mtp_bf16 *X, int M, int H, const mtp_bf16 *W, int64_t 
   return MTP_OK;
 }
 
+// Score M hidden rows against N rows of a tiled table.
+mtp_status run_rows_tiled(const mtp_bf16 *X, int M, int H, const void *WT, int64_t N,
+                          mtp::RowSink sink, hipStream_t stream, const mtp_config *cfg) {
+  if (cfg && cfg->path == MTP_PATH_VALU) return MTP_ERR_UNSUPPORTED;
+  int cus = 0;
+  hipError_t e = current_cus(&cus);
+  if (e != hipSuccess) return hip_fail(e);
+  const int per_cu = (cfg && cfg->blocks_per_cu > 0) ? cfg->blocks_per_cu : 1;
+  mtp::DmaLaunch L;
+  L.X = X;
+  L.WT = WT;
+  L.M = M;
+  L.N = N;
+  L.nch = H / 8;
+  L.S = mtp::tiled_cols(H) / 32;
+  L.max_blocks_x = per_cu * cus;
+  L.sink = sink;
+  L.stream = stream;
+  e = mtp::launch_dma(L, mtp::dma_nb_for(M));
+  if (e != hipSuccess) return hip_fail(e);
+  return MTP_OK;
+}
+
+size_t tiled_bytes_of(int64_t rows, int H) {
+  if (rows < 1 || rows > INT32_MAX || H < 8 || H > MTP_MAX_HIDDEN || H % 8 != 0) return 0;
+  return (size_t)mtp::tiled_rows(rows) * (size_t)mtp::tiled_cols(H) * 2;
+}
+
+mtp_status check_draft_args(const mtp_bf16 *hidden, int M, int H, const void *table,
+                            const int32_t *ids, int64_t C, const int32_t *out_ids,
+                            const float *out_logit, const void *ws, size_t ws_bytes,
+                            const mtp_config *cfg) {
+  if (!hidden || !table || !out_ids) return MTP_ERR_INVALID_ARG;
+  if (!shape_ok(M, C, H)) return MTP_ERR_INVALID_ARG;
+  if (!aligned(hidden, 16) || !aligned(table, 16) || !aligned(out_ids, 4) ||
+      (ids && !aligned(ids, 4)) || (out_logit && !aligned(out_logit, 4)))
+    return MTP_ERR_INVALID_ARG;
+  mtp_status st = check_cfg(cfg);
+  if (st != MTP_OK) return st;
+  if (!ws || !aligned(ws, 8)) return MTP_ERR_WORKSPACE;
+  if (ws_bytes < rows_workspace_bytes(M)) return MTP_ERR_WORKSPACE;
+  return MTP_OK;
+}
+
+mtp::RowSink draft_sink(void *ws, const int32_t *ids, int32_t *out_ids, float *out_logit, int M) {
+  mtp::RowSink s;
+  std::memset(&s, 0, sizeof s);
+  s.ticket = (uint32_t *)ws;
+  s.keys = (unsigned long long *)((char *)ws + mtp::kWsHeader);
+  s.ids = ids;
+  s.out_ids = out_ids;
+  s.out_logit = out_logit;
+  s.M = M;
+  s.B = 0;
+  s.k = -1;
+  return s;
+}
+
+mtp_status check_verify_args(const mtp_bf16 *hidden, int B, int k, int H, const void *head,
+                             int64_t V, const int32_t *draft, const int32_t *out_argmax,
+                             const float *out_logit, const int32_t *out_accept,
+                             const int32_t *out_tokens, const void *ws, size_t ws_bytes,
+                             const mtp_config *cfg) {
+  if (!hidden || !head || !out_argmax || !out_accept || !out_tokens) return MTP_ERR_INVALID_ARG;
+  if (B < 1 || k < 0 || k > MTP_MAX_K) return MTP_ERR_INVALID_ARG;
+  if (k > 0 && !draft) return MTP_ERR_INVALID_ARG;
+  const int64_t M = (int64_t)B * (k + 1);
+  if (!shape_ok(M, V, H)) return MTP_ERR_INVALID_ARG;
+  if (!aligned(hidden, 16) || !aligned(head, 16) || !aligned(out_argmax, 4) ||
+      !aligned(out_accept, 4) || !aligned(out_tokens, 4) || (draft && !aligned(draft, 4)) ||
+      (out_logit && !aligned(out_logit, 4)))
+    return MTP_ERR_INVALID_ARG;
+  mtp_status st = check_cfg(cfg);
+  if (st != MTP_OK) return st;
+  if (!ws || !aligned(ws, 8)) return MTP_ERR_WORKSPACE;
+  if (ws_bytes < rows_workspace_bytes(M)) return MTP_ERR_WORKSPACE;
+  return MTP_OK;
+}
+
+mtp::RowSink verify_sink(void *ws, int B, int k, const int32_t *draft, int32_t *out_argmax,
+                         float *out_logit, int32_t *out_accept, int32_t *out_tokens) {
+  mtp::RowSink s;
+  std::memset(&s, 0, sizeof s);
+  s.ticket = (uint32_t *)ws;
+  s.keys = (unsigned long long *)((char *)ws + mtp::kWsHeader);
+  s.ids = nullptr;
+  s.out_ids = out_argmax;
+  s.out_logit = out_logit;
+  s.M = B * (k + 1);
+  s.B = B;
+  s.k = k;
+  s.draft = draft;
+  s.out_accept = out_accept;
+  s.out_tokens = out_tokens;
+  return s;
+}
+
 }  // namespace
 
 extern "C" {
@@ -178,26 +275,11 @@ mtp_status mtp_draft_argmax_cfg(const mtp_bf16 *hidden, int M, int H, const mtp_
                                 const int32_t *ids, int64_t C, int32_t *out_ids,
                                 float *out_logit, void *ws, size_t ws_bytes, hipStream_t stream,
                                 const mtp_config *cfg) {
-  if (!hidden || !table || !out_ids) return MTP_ERR_INVALID_ARG;
-  if (!shape_ok(M, C, H)) return MTP_ERR_INVALID_ARG;
-  if (!aligned(hidden, 16) || !aligned(table, 16) || !aligned(out_ids, 4) ||
-      (ids && !aligned(ids, 4)) || (out_logit && !aligned(out_logit, 4)))
-    return MTP_ERR_INVALID_ARG;
-  mtp_status st = check_cfg(cfg);
+  mtp_status st =
+      check_draft_args(hidden, M, H, table, ids, C, out_ids, out_logit, ws, ws_bytes, cfg);
   if (st != MTP_OK) return st;
-  if (!ws || !aligned(ws, 8)) return MTP_ERR_WORKSPACE;
-  if (ws_bytes < rows_workspace_bytes(M)) return MTP_ERR_WORKSPACE;
-  mtp::RowSink s;
-  std::memset(&s, 0, sizeof s);
-  s.ticket = (uint32_t *)ws;
-  s.keys = (unsigned long long *)((char *)ws + mtp::kWsHeader);
-  s.ids = ids;
-  s.out_ids = out_ids;
-  s.out_logit = out_logit;
-  s.M = M;
-  s.B = 0;
-  s.k = -1;
-  return run_rows(hidden, M, H, table, C, s, stream, cfg);
+  return run_rows(hidden, M, H, table, C, draft_sink(ws, ids, out_ids, out_logit, M), stream,
+                  cfg);
 }
 
 mtp_status mtp_draft_argmax(const mtp_bf16 *hidden, int M, int H, const mtp_bf16 *table,
@@ -212,33 +294,12 @@ mtp_status mtp_verify_accept_cfg(const mtp_bf16 *hidden, int B, int k, int H,
                                  int32_t *out_argmax, float *out_logit, int32_t *out_accept,
                                  int32_t *out_tokens, void *ws, size_t ws_bytes,
                                  hipStream_t stream, const mtp_config *cfg) {
-  if (!hidden || !head || !out_argmax || !out_accept || !out_tokens) return MTP_ERR_INVALID_ARG;
-  if (B < 1 || k < 0 || k > MTP_MAX_K) return MTP_ERR_INVALID_ARG;
-  if (k > 0 && !draft) return MTP_ERR_INVALID_ARG;
-  const int64_t M = (int64_t)B * (k + 1);
-  if (!shape_ok(M, V, H)) return MTP_ERR_INVALID_ARG;
-  if (!aligned(hidden, 16) || !aligned(head, 16) || !aligned(out_argmax, 4) ||
-      !aligned(out_accept, 4) || !aligned(out_tokens, 4) || (draft && !aligned(draft, 4)) ||
-      (out_logit && !aligned(out_logit, 4)))
-    return MTP_ERR_INVALID_ARG;
-  mtp_status st = check_cfg(cfg);
+  mtp_status st = check_verify_args(hidden, B, k, H, head, V, draft, out_argmax, out_logit,
+                                    out_accept, out_tokens, ws, ws_bytes, cfg);
   if (st != MTP_OK) return st;
-  if (!ws || !aligned(ws, 8)) return MTP_ERR_WORKSPACE;
-  if (ws_bytes < rows_workspace_bytes(M)) return MTP_ERR_WORKSPACE;
-  mtp::RowSink s;
-  std::memset(&s, 0, sizeof s);
-  s.ticket = (uint32_t *)ws;
-  s.keys = (unsigned long long *)((char *)ws + mtp::kWsHeader);
-  s.ids = nullptr;
-  s.out_ids = out_argmax;
-  s.out_logit = out_logit;
-  s.M = (int)M;
-  s.B = B;
-  s.k = k;
-  s.draft = draft;
-  s.out_accept = out_accept;
-  s.out_tokens = out_tokens;
-  return run_rows(hidden, (int)M, H, head, V, s, stream, cfg);
+  return run_rows(hidden, B * (k + 1), H, head, V,
+                  verify_sink(ws, B, k, draft, out_argmax, out_logit, out_accept, out_tokens),
+                  stream, cfg);
 }
 
 mtp_status mtp_verify_accept(const mtp_bf16 *hidden, int B, int k, int H, const mtp_bf16 *head,
@@ -247,6 +308,70 @@ mtp_status mtp_verify_accept(const mtp_bf16 *hidden, int B, int k, int H, const 
                              void *ws, size_t ws_bytes, hipStream_t stream) {
   return mtp_verify_accept_cfg(hidden, B, k, H, head, V, draft, out_argmax, out_logit,
                                out_accept, out_tokens, ws, ws_bytes, stream, nullptr);
+}
+
+size_t mtp_tiled_bytes(int64_t rows, int H) { return tiled_bytes_of(rows, H); }
+
+mtp_status mtp_pack_tiled(const mtp_bf16 *head, int64_t V, int H, const int32_t *ids, int64_t C,
+                          void *tiled, size_t tiled_bytes, hipStream_t stream) {
+  if (!head || !tiled) return MTP_ERR_INVALID_ARG;
+  if (V < 1 || V > INT32_MAX || C < 1 || C > INT32_MAX || (!ids && C > V)) return MTP_ERR_INVALID_ARG;
+  const size_t need = tiled_bytes_of(C, H);
+  if (need == 0) return MTP_ERR_INVALID_ARG;
+  if (!aligned(head, 16) || !aligned(tiled, 16) || (ids && !aligned(ids, 4)))
+    return MTP_ERR_INVALID_ARG;
+  if (tiled_bytes < need) return MTP_ERR_INVALID_ARG;
+  int cus = 0;
+  hipError_t e = current_cus(&cus);
+  if (e != hipSuccess) return hip_fail(e);
+  e = mtp::launch_pack_tiled(head, V, H / 8, ids, C, mtp::tiled_cols(H) / 32, tiled, cus,
+                             stream);
+  if (e != hipSuccess) return hip_fail(e);
+  return MTP_OK;
+}
+
+mtp_status mtp_draft_argmax_tiled_cfg(const mtp_bf16 *hidden, int M, int H,
+                                      const void *table_tiled, const int32_t *ids, int64_t C,
+                                      int32_t *out_ids, float *out_logit, void *ws,
+                                      size_t ws_bytes, hipStream_t stream,
+                                      const mtp_config *cfg) {
+  mtp_status st = check_draft_args(hidden, M, H, table_tiled, ids, C, out_ids, out_logit, ws,
+                                   ws_bytes, cfg);
+  if (st != MTP_OK) return st;
+  return run_rows_tiled(hidden, M, H, table_tiled, C, draft_sink(ws, ids, out_ids, out_logit, M),
+                        stream, cfg);
+}
+
+mtp_status mtp_draft_argmax_tiled(const mtp_bf16 *hidden, int M, int H, const void *table_tiled,
+                                  const int32_t *ids, int64_t C, int32_t *out_ids,
+                                  float *out_logit, void *ws, size_t ws_bytes,
+                                  hipStream_t stream) {
+  return mtp_draft_argmax_tiled_cfg(hidden, M, H, table_tiled, ids, C, out_ids, out_logit, ws,
+                                    ws_bytes, stream, nullptr);
+}
+
+mtp_status mtp_verify_accept_tiled_cfg(const mtp_bf16 *hidden, int B, int k, int H,
+                                       const void *head_tiled, int64_t V, const int32_t *draft,
+                                       int32_t *out_argmax, float *out_logit,
+                                       int32_t *out_accept, int32_t *out_tokens, void *ws,
+                                       size_t ws_bytes, hipStream_t stream,
+                                       const mtp_config *cfg) {
+  mtp_status st = check_verify_args(hidden, B, k, H, head_tiled, V, draft, out_argmax, out_logit,
+                                    out_accept, out_tokens, ws, ws_bytes, cfg);
+  if (st != MTP_OK) return st;
+  return run_rows_tiled(
+      hidden, B * (k + 1), H, head_tiled, V,
+      verify_sink(ws, B, k, draft, out_argmax, out_logit, out_accept, out_tokens), stream, cfg);
+}
+
+mtp_status mtp_verify_accept_tiled(const mtp_bf16 *hidden, int B, int k, int H,
+                                   const void *head_tiled, int64_t V, const int32_t *draft,
+                                   int32_t *out_argmax, float *out_logit, int32_t *out_accept,
+                                   int32_t *out_tokens, void *ws, size_t ws_bytes,
+                                   hipStream_t stream) {
+  return mtp_verify_accept_tiled_cfg(hidden, B, k, H, head_tiled, V, draft, out_argmax,
+                                     out_logit, out_accept, out_tokens, ws, ws_bytes, stream,
+                                     nullptr);
 }
 
 }  // extern "C"

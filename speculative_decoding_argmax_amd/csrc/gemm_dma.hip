@@ -1,0 +1,299 @@
+// Skinny GEMM + per-row argmax on the matrix cores, fed by LDS DMA from a
+// table stored in the 64-row tiled layout (mtp.h, "Tiled tables").
+//
+// Tiled layout: rows are grouped in tiles of 64 (zero rows pad the last tile),
+// columns in steps of 32 (zero columns pad H to a multiple of 128). Tile t,
+// step s holds four 1 KiB fragments, one per 16-row block rb, and fragment
+// (t, s, rb) is exactly the A operand of v_mfma_f32_16x16x32_bf16 for table
+// rows 64t + 16rb + [0, 16) and columns 32s + [0, 32): lane l = j + 16g holds
+// row 64t + 16rb + j, columns 32s + 8g + [0, 8). Fragments are ordered
+// (t, s, rb), so a 64-row tile is one contiguous stream and every K chunk of it
+// is one contiguous block.
+//
+// A workgroup of WV waves owns tiles of WV * RW * 16 table rows, grid-strided
+// over the table. Each K chunk (KS steps of 32 columns) of a tile is copied
+// into LDS by global_load_lds_dwordx4 (one 1 KiB fragment per instruction,
+// straight from HBM, no registers): the RBT * KS weight fragments and, gathered
+// from the row-major hidden block, the KS * NB hidden fragments (operand B,
+// 16 hidden rows x 32 columns each). Chunks rotate through NBUF LDS slots: the
+// copy of chunk it + NBUF - 1 is in flight while chunk it is multiplied. Each
+// wave owns RW 16-row blocks and all NB 16-row blocks of hidden rows; lanes
+// keep the best (logit, row) of their hidden row, then lanes and waves merge
+// through LDS and finish_rows merges workgroups.
+//
+// Synchronisation: each slot is its own __shared__ array and the loop is
+// unrolled by NBUF, so the compiler can see that reads of slot it do not alias
+// the copies into other slots and leaves those copies in flight. Before
+// reading a slot, every wave waits (s_waitcnt vmcnt) until its own copies into
+// that slot have landed (all waves issue the same number of copies per chunk,
+// so the count of younger copies is a constant), then all waves meet at a
+// plain s_barrier (no fence, which would wait for every copy in flight). The
+// barrier also orders the next copy into a slot after every wave's reads of
+// that slot's previous chunk.
+//
+// Every logit sums its columns in one order (chunks, then steps, ascending;
+// the MFMA's fixed in-step order), whatever the row's tile or position, so
+// duplicated rows score bit-identically and ties go to the lower row.
+
+#include <type_traits>
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace mtp {
+
+typedef __bf16 bf16x8_dma_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_dma_t __attribute__((ext_vector_type(4)));
+
+#define MTP_LDS(p) ((__attribute__((address_space(3))) void *)(p))
+
+__device__ __forceinline__ f32x4_dma_t mfma16_dma(const uint4 &a, const uint4 &b,
+                                                  f32x4_dma_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_dma_t, a),
+                                                 __builtin_bit_cast(bf16x8_dma_t, b), c, 0, 0,
+                                                 0);
+}
+
+__device__ __forceinline__ bool better_row(float v, int i, float bv, int bi) {
+  return bi < 0 || v > bv || (v == bv && i < bi);
+}
+
+// Workgroup barrier without a memory fence (a fence would wait for every copy
+// in flight). The empty asm statements keep the compiler from moving memory
+// accesses across it.
+__device__ __forceinline__ void barrier_no_fence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// s_waitcnt with vmcnt(n) and no wait on the other counters (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// NB: 16-row blocks of hidden rows; RW: 16-row table blocks per wave; KS:
+// 32-column steps per chunk; NBUF: LDS slots (3 or 4); WV: waves per group.
+template <int NB, int RW, int KS, int NBUF, int WV>
+__global__ void __launch_bounds__(WV * 64)
+    gemm_argmax_dma(const uint4 *__restrict__ X, const uint4 *__restrict__ WT, int M, int N,
+                    int nch, int S, RowSink sink) {
+  constexpr int RBT = WV * RW;                 // 16-row blocks per workgroup tile
+  constexpr int TV = RBT * 16;                 // table rows per workgroup tile
+  constexpr int AF = RBT * KS;                 // weight fragments per chunk
+  constexpr int FR = AF + KS * NB;             // fragments per chunk
+  constexpr int PER_WAVE = (FR + WV - 1) / WV; // copies per wave per chunk
+  static_assert(NBUF >= 3 && NBUF <= 4, "three or four slots");
+  static_assert(RBT % 4 == 0, "workgroup tiles are whole 64-row tiles");
+  static_assert(FR * 64 * 16 >= WV * NB * 64 * 4, "merge scratch fits a slot");
+  __shared__ uint4 slot0[FR * 64];
+  __shared__ uint4 slot1[FR * 64];
+  __shared__ uint4 slot2[FR * 64];
+  __shared__ uint4 slot3[NBUF > 3 ? FR * 64 : 1];
+  __shared__ float f_val[NB * 16];
+  __shared__ int64_t f_row[NB * 16];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int j = lane & 15;
+  const int g = lane >> 4;
+  const int m0 = blockIdx.y * NB * 16;
+  const int nchunks = S / KS;                  // S is a multiple of 4
+  const int ntiles = (N + TV - 1) / TV;
+  const int my_tiles = blockIdx.x < ntiles ? (ntiles - 1 - blockIdx.x) / gridDim.x + 1 : 0;
+  const int total = my_tiles * nchunks;
+  const int nrb = ((N + 63) / 64) * 4;         // 16-row blocks stored (padded)
+
+  auto slot = [&](auto tag) -> uint4 * {
+    constexpr int SL = decltype(tag)::value;
+    if constexpr (SL == 0) return slot0;
+    else if constexpr (SL == 1) return slot1;
+    else if constexpr (SL == 2) return slot2;
+    else return slot3;
+  };
+
+  // Copy chunk `it` into a slot. Fragment f < AF: weights, step f / RBT of the
+  // chunk, 16-row block f % RBT of the tile; f >= AF: hidden fragment for step
+  // (f - AF) / NB, hidden block (f - AF) % NB. Every wave issues PER_WAVE
+  // copies; surplus ones repeat the last fragment (same bytes, same place).
+  auto issue = [&](auto tag, int it) {
+    uint4 *base = slot(tag);
+    const int tile = blockIdx.x + (it / nchunks) * gridDim.x;
+    const int c = it % nchunks;
+#pragma unroll
+    for (int q = 0; q < PER_WAVE; ++q) {
+      int f = wave + WV * q;
+      f = f < FR ? f : FR - 1;
+      const uint4 *src;
+      if (f < AF) {
+        const int s = f / RBT;
+        int rb = tile * RBT + f % RBT;
+        rb = rb < nrb ? rb : nrb - 1;          // past the table: valid, never reported
+        src = WT + (((int64_t)(rb >> 2) * S + c * KS + s) * 4 + (rb & 3)) * kWave + lane;
+      } else {
+        const int fb = f - AF;
+        const int s = fb / NB;
+        const int nb = fb - s * NB;
+        // hidden rows past M and columns past H read valid addresses: the
+        // extra hidden columns are never reported, and past H the weights
+        // are zero
+        const int m = min(m0 + nb * 16 + j, M - 1);
+        const int col = min((c * KS + s) * 4 + g, nch - 1);
+        src = X + (int64_t)m * nch + col;
+      }
+      __builtin_amdgcn_global_load_lds((const void *)src, MTP_LDS(base + f * kWave), 16, 0, 0);
+    }
+  };
+
+  f32x4_dma_t acc[RW][NB];
+#pragma unroll
+  for (int rw = 0; rw < RW; ++rw)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[rw][nb] = f32x4_dma_t{0.f, 0.f, 0.f, 0.f};
+  float bv[NB];
+  int bi[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    bv[nb] = 0.f;
+    bi[nb] = -1;
+  }
+
+  if (0 < total) issue(std::integral_constant<int, 0>{}, 0);
+  if (1 < total) issue(std::integral_constant<int, 1>{}, 1);
+  if constexpr (NBUF > 3) {
+    if (2 < total) issue(std::integral_constant<int, 2>{}, 2);
+  }
+
+  auto body = [&](auto tag, int it) {
+    constexpr int SL = decltype(tag)::value;
+    // copies younger than this chunk's: chunks it+1 .. it+NBUF-2
+    if (it + NBUF - 2 < total)
+      wait_vmcnt<(NBUF - 2) * PER_WAVE>();
+    else
+      wait_vmcnt<0>();
+    barrier_no_fence();
+    if (it + NBUF - 1 < total) issue(std::integral_constant<int, (SL + NBUF - 1) % NBUF>{}, it + NBUF - 1);
+    const uint4 *A = slot(tag);
+    const uint4 *Bf = A + AF * kWave;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      uint4 a[RW];
+#pragma unroll
+      for (int rw = 0; rw < RW; ++rw) a[rw] = A[(s * RBT + wave * RW + rw) * kWave + lane];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const uint4 b = Bf[(s * NB + nb) * kWave + lane];
+#pragma unroll
+        for (int rw = 0; rw < RW; ++rw) acc[rw][nb] = mfma16_dma(a[rw], b, acc[rw][nb]);
+      }
+    }
+    if (it % nchunks == nchunks - 1) {
+      const int tile = blockIdx.x + (it / nchunks) * gridDim.x;
+      const int vbase = tile * TV + wave * RW * 16 + 4 * g;
+#pragma unroll
+      for (int rw = 0; rw < RW; ++rw) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int v = vbase + rw * 16 + r;
+            const float z = acc[rw][nb][r];
+            if (v < N && better_row(z, v, bv[nb], bi[nb])) {
+              bv[nb] = z;
+              bi[nb] = v;
+            }
+          }
+          acc[rw][nb] = f32x4_dma_t{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+    }
+  };
+
+  for (int it = 0; it < total; it += NBUF) {
+    body(std::integral_constant<int, 0>{}, it);
+    if (it + 1 < total) body(std::integral_constant<int, 1>{}, it + 1);
+    if (it + 2 < total) body(std::integral_constant<int, 2>{}, it + 2);
+    if constexpr (NBUF > 3) {
+      if (it + 3 < total) body(std::integral_constant<int, 3>{}, it + 3);
+    }
+  }
+  wait_vmcnt<0>();
+  __syncthreads();
+
+  // Merge the 4 * WV candidates of each hidden row (slots are free now).
+  float *red_v = reinterpret_cast<float *>(slot0);
+  int *red_i = reinterpret_cast<int *>(slot1);
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    red_v[(wave * NB + nb) * kWave + lane] = bv[nb];
+    red_i[(wave * NB + nb) * kWave + lane] = bi[nb];
+  }
+  __syncthreads();
+  if (tid < NB * 16) {
+    const int nb = tid >> 4;
+    const int jj = tid & 15;
+    float v = 0.f;
+    int ix = -1;
+    for (int w = 0; w < WV; ++w) {
+      for (int gg = 0; gg < 4; ++gg) {
+        const int o = (w * NB + nb) * kWave + jj + 16 * gg;
+        if (red_i[o] >= 0 && better_row(red_v[o], red_i[o], v, ix)) {
+          v = red_v[o];
+          ix = red_i[o];
+        }
+      }
+    }
+    f_val[tid] = v;
+    f_row[tid] = ix;
+  }
+  __syncthreads();
+  const int mcount = M - m0 < NB * 16 ? M - m0 : NB * 16;
+  finish_rows(sink, f_val, f_row, m0, mcount);
+}
+
+// Padded sizes of the tiled layout.
+int64_t tiled_rows(int64_t rows) { return (rows + 63) / 64 * 64; }
+int tiled_cols(int H) { return (H + 127) / 128 * 128; }
+
+template <int NB, int RW, int KS, int NBUF, int WV>
+static hipError_t launch_dma_cfg(const DmaLaunch &L) {
+  constexpr int TV = WV * RW * 16;
+  const int64_t ntiles = (L.N + TV - 1) / TV;
+  const int gx = (int)(ntiles < L.max_blocks_x ? ntiles : L.max_blocks_x);
+  const int gy = (L.M + NB * 16 - 1) / (NB * 16);
+  hipLaunchKernelGGL((gemm_argmax_dma<NB, RW, KS, NBUF, WV>), dim3(gx, gy), dim3(WV * 64), 0,
+                     L.stream, (const uint4 *)L.X, (const uint4 *)L.WT, L.M, (int)L.N, L.nch,
+                     L.S, L.sink);
+  return hipGetLastError();
+}
+
+// Hidden-row blocks per pass: M rounds up to an instantiated count (at most
+// 160 rows per pass; more rows take several passes over the table).
+static const int kDmaNbSteps[] = {1, 2, 3, 4, 6, 8, 10};
+
+int dma_nb_for(int M) {
+  const int need = (M + 15) / 16;
+  for (int n : kDmaNbSteps)
+    if (n >= need) return n;
+  return 10;
+}
+
+// Instantiated shapes (measured on MI355X at the workload shapes; none spills
+// registers, every one fits the 160 KiB LDS).
+hipError_t launch_dma(const DmaLaunch &L, int nb) {
+  switch (nb) {
+    case 1: return launch_dma_cfg<1, 1, 4, 3, 4>(L);
+    case 2: return launch_dma_cfg<2, 1, 4, 4, 4>(L);
+    case 3: return launch_dma_cfg<3, 1, 2, 4, 8>(L);
+    case 4: return launch_dma_cfg<4, 1, 2, 4, 8>(L);
+    case 6: return launch_dma_cfg<6, 2, 2, 3, 8>(L);
+    case 8: return launch_dma_cfg<8, 2, 2, 3, 8>(L);
+    case 10: return launch_dma_cfg<10, 2, 2, 3, 8>(L);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace mtp

@@ -43,6 +43,25 @@ struct MfmaLaunch {
 int mfma_nb_for(int M);
 hipError_t launch_mfma(const MfmaLaunch &L, int nb);
 
+struct DmaLaunch {
+  const void *X;     // hidden [M][H] bf16, row-major
+  const void *WT;    // table in the 64-row tiled layout
+  int M;
+  int64_t N;         // table rows (before padding)
+  int nch;           // H / 8
+  int S;             // 32-column steps per padded row (tiled_cols(H) / 32)
+  int max_blocks_x;
+  RowSink sink;
+  hipStream_t stream;
+};
+
+int64_t tiled_rows(int64_t rows);
+int tiled_cols(int H);
+int dma_nb_for(int M);
+hipError_t launch_dma(const DmaLaunch &L, int nb);
+hipError_t launch_pack_tiled(const void *head, int64_t V, int nch, const int32_t *ids,
+                             int64_t C, int S, void *tiled, int num_cus, hipStream_t stream);
+
 hipError_t launch_pack(const void *head, int64_t V, int nch, const int32_t *ids, int64_t C,
                        void *table, int num_cus, hipStream_t stream);
 hipError_t launch_fill_zero(void *ws, size_t bytes, hipStream_t stream);

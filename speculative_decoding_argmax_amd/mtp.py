@@ -73,6 +73,12 @@ def _load() -> ctypes.CDLL:
         "mtp_draft_argmax_cfg": ([P, I, I, P, P, I64, P, P, P, S, P, P], I),
         "mtp_verify_accept": ([P, I, I, I, P, I64, P, P, P, P, P, P, S, P], I),
         "mtp_verify_accept_cfg": ([P, I, I, I, P, I64, P, P, P, P, P, P, S, P, P], I),
+        "mtp_tiled_bytes": ([I64, I], S),
+        "mtp_pack_tiled": ([P, I64, I, P, I64, P, S, P], I),
+        "mtp_draft_argmax_tiled": ([P, I, I, P, P, I64, P, P, P, S, P], I),
+        "mtp_draft_argmax_tiled_cfg": ([P, I, I, P, P, I64, P, P, P, S, P, P], I),
+        "mtp_verify_accept_tiled": ([P, I, I, I, P, I64, P, P, P, P, P, P, S, P], I),
+        "mtp_verify_accept_tiled_cfg": ([P, I, I, I, P, I64, P, P, P, P, P, P, S, P, P], I),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -242,3 +248,87 @@ def mtp_verify_accept(hidden, head, draft, B: int, k: int, out_argmax, out_accep
         _ptr(out_tokens, "out_tokens", (torch.int32,)),
         _ptr(ws, "ws", (torch.int64, torch.uint8, torch.int32)), ws.numel() * ws.element_size(),
         _stream(stream), ctypes.byref(cfg)), "mtp_verify_accept")
+
+
+# --- tiled tables -------------------------------------------------------------
+
+def mtp_tiled_bytes(rows: int, H: int) -> int:
+    return int(lib.mtp_tiled_bytes(rows, H))
+
+
+def alloc_tiled(rows: int, H: int, device=None):
+    """Device buffer (uint8) sized for a tiled table of `rows` rows."""
+    torch = _torch()
+    n = mtp_tiled_bytes(rows, H)
+    if n == 0:
+        raise ValueError("rows or H out of range")
+    return torch.empty(n, dtype=torch.uint8, device=device or "cuda")
+
+
+def mtp_pack_tiled(head, ids, tiled, C: Optional[int] = None, stream=None) -> None:
+    """Lay out rows ids[i] of the row-major head (or, ids None, its first C
+    rows) in the tiled layout of include/mtp.h."""
+    torch = _torch()
+    V, H = head.shape
+    if ids is not None:
+        C = ids.numel()
+    elif C is None:
+        C = V
+    _check(lib.mtp_pack_tiled(_ptr(head, "head", _bf16_types()), V, H,
+                              _ptr(ids, "ids", (torch.int32,), allow_none=True), C,
+                              _ptr(tiled, "tiled", (torch.uint8, torch.int16, torch.int32)),
+                              tiled.numel() * tiled.element_size(), _stream(stream)),
+           "mtp_pack_tiled")
+
+
+def mtp_draft_argmax_tiled(hidden, table_tiled, C: int, ids, out_ids, out_logit=None, ws=None,
+                           stream=None, blocks_per_cu: int = 0) -> None:
+    """Draft GEMV + argmax over a tiled candidate table of C rows."""
+    torch = _torch()
+    M, H = hidden.shape
+    if table_tiled.numel() * table_tiled.element_size() < mtp_tiled_bytes(C, H):
+        raise ValueError("tiled table smaller than mtp_tiled_bytes(C, H)")
+    if ids is not None and ids.numel() != C:
+        raise ValueError("ids must have C entries")
+    if out_ids.numel() != M or (out_logit is not None and out_logit.numel() != M):
+        raise ValueError("outputs must have M entries")
+    if ws is None:
+        ws = alloc_workspace(mtp_draft_workspace_bytes(M, C, H), hidden.device, stream)
+    cfg = _cfg(MTP_PATH_AUTO, blocks_per_cu)
+    _check(lib.mtp_draft_argmax_tiled_cfg(
+        _ptr(hidden, "hidden", _bf16_types()), M, H,
+        _ptr(table_tiled, "table_tiled", (torch.uint8, torch.int16, torch.int32)),
+        _ptr(ids, "ids", (torch.int32,), allow_none=True), C,
+        _ptr(out_ids, "out_ids", (torch.int32,)),
+        _ptr(out_logit, "out_logit", (torch.float32,), allow_none=True),
+        _ptr(ws, "ws", (torch.int64, torch.uint8, torch.int32)), ws.numel() * ws.element_size(),
+        _stream(stream), ctypes.byref(cfg)), "mtp_draft_argmax_tiled")
+
+
+def mtp_verify_accept_tiled(hidden, head_tiled, V: int, draft, B: int, k: int, out_argmax,
+                            out_accept, out_tokens, out_logit=None, ws=None, stream=None,
+                            blocks_per_cu: int = 0) -> None:
+    """Verify GEMM + argmax + acceptance over a tiled head of V rows."""
+    torch = _torch()
+    Mv, H = hidden.shape
+    if Mv != B * (k + 1):
+        raise ValueError("hidden must be [B*(k+1)][H]")
+    if head_tiled.numel() * head_tiled.element_size() < mtp_tiled_bytes(V, H):
+        raise ValueError("tiled head smaller than mtp_tiled_bytes(V, H)")
+    if out_argmax.numel() != Mv or out_tokens.numel() != Mv or out_accept.numel() != B:
+        raise ValueError("output sizes do not match B and k")
+    if draft is not None and draft.numel() != B * k:
+        raise ValueError("draft must be [B][k]")
+    if ws is None:
+        ws = alloc_workspace(mtp_verify_workspace_bytes(B, k, V, H), hidden.device, stream)
+    cfg = _cfg(MTP_PATH_AUTO, blocks_per_cu)
+    _check(lib.mtp_verify_accept_tiled_cfg(
+        _ptr(hidden, "hidden", _bf16_types()), B, k, H,
+        _ptr(head_tiled, "head_tiled", (torch.uint8, torch.int16, torch.int32)), V,
+        _ptr(draft, "draft", (torch.int32,), allow_none=(k == 0)),
+        _ptr(out_argmax, "out_argmax", (torch.int32,)),
+        _ptr(out_logit, "out_logit", (torch.float32,), allow_none=True),
+        _ptr(out_accept, "out_accept", (torch.int32,)),
+        _ptr(out_tokens, "out_tokens", (torch.int32,)),
+        _ptr(ws, "ws", (torch.int64, torch.uint8, torch.int32)), ws.numel() * ws.element_size(),
+        _stream(stream), ctypes.byref(cfg)), "mtp_verify_accept_tiled")

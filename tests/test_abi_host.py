@@ -124,3 +124,38 @@ def test_pack_and_init_reject_bad_arguments():
     assert g(FAKE, 0, None) == INVALID
     assert g(FAKE, 12, None) == INVALID
     assert g(P(0x10004), 64, None) == INVALID
+
+
+def test_tiled_sizes():
+    assert mtp.mtp_tiled_bytes(65536, 2048) == 65536 * 2048 * 2
+    assert mtp.mtp_tiled_bytes(248320, 5120) == 248320 * 5120 * 2
+    assert mtp.mtp_tiled_bytes(100, 24) == 128 * 128 * 2
+    assert mtp.mtp_tiled_bytes(1, 2560) == 64 * 2560 * 2
+    assert mtp.mtp_tiled_bytes(0, 8) == 0
+    assert mtp.mtp_tiled_bytes(10, 12) == 0
+    assert mtp.mtp_tiled_bytes(10, 16392) == 0
+
+
+def test_tiled_entry_points_reject_bad_arguments():
+    f = mtp.lib.mtp_pack_tiled
+    need = mtp.mtp_tiled_bytes(100, 64)
+    assert f(None, 100, 64, None, 100, FAKE, need, None) == INVALID
+    assert f(FAKE, 100, 64, None, 101, FAKE, need, None) == INVALID     # C > V without ids
+    assert f(FAKE, 100, 64, None, 100, FAKE, need - 16, None) == INVALID
+    assert f(FAKE, 100, 60, None, 100, FAKE, need, None) == INVALID
+    assert f(FAKE_ODD, 100, 64, None, 100, FAKE, need, None) == INVALID
+    d = mtp.lib.mtp_draft_argmax_tiled
+    assert d(None, 1, 64, FAKE, None, 100, FAKE, None, FAKE, 4096, None) == INVALID
+    assert d(FAKE, 0, 64, FAKE, None, 100, FAKE, None, FAKE, 4096, None) == INVALID
+    assert d(FAKE, 1, 64, FAKE_ODD, None, 100, FAKE, None, FAKE, 4096, None) == INVALID
+    assert d(FAKE, 1, 64, FAKE, None, 100, FAKE, None, None, 4096, None) == mtp.MTP_ERR_WORKSPACE
+    c = mtp.mtp_config()
+    c.path = mtp.MTP_PATH_VALU
+    assert mtp.lib.mtp_draft_argmax_tiled_cfg(FAKE, 1, 64, FAKE, None, 100, FAKE, None, FAKE,
+                                              4096, None, ctypes.byref(c)) == \
+        mtp.MTP_ERR_UNSUPPORTED
+    v = mtp.lib.mtp_verify_accept_tiled
+    assert v(FAKE, 1, 16, 64, FAKE, 100, FAKE, FAKE, None, FAKE, FAKE, FAKE, 4096, None) == INVALID
+    assert v(FAKE, 1, 3, 64, None, 100, FAKE, FAKE, None, FAKE, FAKE, FAKE, 4096, None) == INVALID
+    assert v(FAKE, 1, 3, 64, FAKE, 100, FAKE, FAKE, None, FAKE, FAKE, FAKE, 16, None) == \
+        mtp.MTP_ERR_WORKSPACE
