@@ -40,6 +40,7 @@ HBM_PEAK_GBPS = 8000.0
 KERNEL_SOURCES = {
     "valu": ("common.hpp", "gemv_valu.hip", "launch.hpp", "api.cpp"),
     "mfma": ("common.hpp", "gemm_mfma.hip", "launch.hpp", "api.cpp"),
+    "dma": ("common.hpp", "gemm_dma.hip", "launch.hpp", "api.cpp"),
 }
 
 
@@ -50,6 +51,9 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="mtp3_single")
     ap.add_argument("--table-copies", type=int, default=3)
+    ap.add_argument("--layout", choices=("auto", "rows", "tiled"), default="auto",
+                    help="table layout: row-major, or the 64-row tiled layout of include/mtp.h "
+                         "(auto: rows when every call has at most 8 hidden rows)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall-clock budget of the CPU oracle sample")
@@ -109,13 +113,25 @@ def main() -> int:
     def up(a, dt=np.int16):
         return torch.from_numpy(np.ascontiguousarray(a).view(dt)).to(dev)
 
+    layout = args.layout
+    if layout == "auto":
+        layout = "rows" if max(wk.Md, wk.Mv) <= 8 else "tiled"
     head_d = up(head)
     ids_d = up(ids, np.int32)
     tables = []
     for _ in range(max(1, args.table_copies)):
-        t = torch.empty((wk.C, wk.H), dtype=torch.int16, device=dev)
-        mtp.mtp_pack_candidates(head_d, ids_d, t)
+        if layout == "rows":
+            t = torch.empty((wk.C, wk.H), dtype=torch.int16, device=dev)
+            mtp.mtp_pack_candidates(head_d, ids_d, t)
+        else:
+            t = mtp.alloc_tiled(wk.C, wk.H, dev)
+            mtp.mtp_pack_tiled(head_d, ids_d, t)
         tables.append(t)
+    if layout == "tiled":
+        head_v = mtp.alloc_tiled(wk.V, wk.H, dev)
+        mtp.mtp_pack_tiled(head_d, None, head_v, C=wk.V)
+    else:
+        head_v = head_d
     h_d = [up(h) for h in hiddens]
     hv_d = up(hv)
     out_ids = [torch.empty(wk.Md, dtype=torch.int32, device=dev) for _ in range(wk.draft_calls)]
@@ -129,8 +145,23 @@ def main() -> int:
     v_tok = torch.empty((wk.B, wk.k + 1), dtype=torch.int32, device=dev)
     # drafts with the workload's agreement rate against the target's argmax
     # (taken from one untimed verify call; the timed calls only read them)
+    def draft_call(c, table):
+        if layout == "rows":
+            mtp.mtp_draft_argmax(h_d[c], table, ids_d, out_ids[c], out_logit[c], ws=ws_d)
+        else:
+            mtp.mtp_draft_argmax_tiled(h_d[c], table, wk.C, ids_d, out_ids[c], out_logit[c],
+                                       ws=ws_d)
+
+    def verify_call(drafts_dev):
+        if layout == "rows":
+            mtp.mtp_verify_accept(hv_d, head_v, drafts_dev, wk.B, wk.k, v_arg, v_acc, v_tok,
+                                  v_logit, ws=ws_v)
+        else:
+            mtp.mtp_verify_accept_tiled(hv_d, head_v, wk.V, drafts_dev, wk.B, wk.k, v_arg, v_acc,
+                                        v_tok, v_logit, ws=ws_v)
+
     zero_d = torch.zeros((wk.B, wk.k), dtype=torch.int32, device=dev)
-    mtp.mtp_verify_accept(hv_d, head_d, zero_d, wk.B, wk.k, v_arg, v_acc, v_tok, v_logit, ws=ws_v)
+    verify_call(zero_d)
     torch.cuda.synchronize()
     t_now = v_arg.cpu().numpy()
     if wk.p is None:
@@ -147,12 +178,10 @@ def main() -> int:
         if ev is not None:
             ev[0].record(stream)
         for c in range(wk.draft_calls):
-            mtp.mtp_draft_argmax(h_d[c], tables[(i * wk.draft_calls + c) % n_tab], ids_d,
-                                 out_ids[c], out_logit[c], ws=ws_d)
+            draft_call(c, tables[(i * wk.draft_calls + c) % n_tab])
         if ev is not None:
             ev[1].record(stream)
-        mtp.mtp_verify_accept(hv_d, head_d, drafts_d, wk.B, wk.k, v_arg, v_acc, v_tok, v_logit,
-                              ws=ws_v)
+        verify_call(drafts_d)
         if ev is not None:
             ev[2].record(stream)
 
@@ -185,7 +214,7 @@ def main() -> int:
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for i in range(K):
-        mtp.mtp_draft_argmax(h_d[0], tables[0], ids_d, out_ids[0], out_logit[0], ws=ws_d)
+        draft_call(0, tables[0])
     e1.record(stream)
     torch.cuda.synchronize()
     warm_draft_us = e0.elapsed_time(e1) * 1000.0 / K
@@ -217,9 +246,11 @@ def main() -> int:
         dom_name, dom_bytes, dom_us = "verify", verify_bytes, v_us
     else:
         dom_name, dom_bytes, dom_us = "draft", draft_bytes, d_us
-    # rows <= 8 per call run on the vector-ALU kernel at these widths
+    # row-major calls with few rows run on the vector-ALU kernel; tiled ones
+    # on the DMA-fed matrix-core kernel
     dom_rows = wk.Mv if dom_name == "verify" else wk.Md
-    traffic = measured_traffic(dom_name, wk.name, "valu" if dom_rows <= 8 else "mfma")
+    path = "dma" if layout == "tiled" else ("valu" if dom_rows <= 8 else "mfma")
+    traffic = measured_traffic(dom_name, wk.name, path)
     achieved = dom_bytes / dom_us / 1e3
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
@@ -243,7 +274,7 @@ def main() -> int:
             "workload": f"{wk.name}: {wk.draft_calls} draft calls (M={Md}, {C}-row table) + 1 "
                         f"verify call (M={Mv}, {V}-row head), H={H}",
             "H": H, "V": V, "C": C, "B": wk.B, "k": wk.k, "draft_calls": wk.draft_calls,
-            "accumulate": "f32", "table_copies": n_tab, "seed": wk.seed,
+            "accumulate": "f32", "table_copies": n_tab, "seed": wk.seed, "layout": layout,
         },
         "calls": {"draft": draft_stats, "verify": verify_stats},
         "context": {

@@ -35,11 +35,43 @@ def _pack(torch, mtp, W_d, ids, H):
     return t
 
 
+class _Tiled:
+    """Draft/verify through the tiled-table entry points."""
+
+    def __init__(self, torch, mtp, W_d, ids_d, C, V, H):
+        self.torch, self.mtp, self.C, self.V = torch, mtp, C, V
+        self.table = mtp.alloc_tiled(C, H)
+        mtp.mtp_pack_tiled(W_d, ids_d, self.table)
+        self.head = mtp.alloc_tiled(V, H)
+        mtp.mtp_pack_tiled(W_d, None, self.head, C=V)
+
+    def draft(self, h_d, ids_d):
+        torch = self.torch
+        M = h_d.shape[0]
+        oi = torch.full((M,), -7, dtype=torch.int32, device="cuda")
+        ol = torch.full((M,), float("nan"), dtype=torch.float32, device="cuda")
+        self.mtp.mtp_draft_argmax_tiled(h_d, self.table, self.C, ids_d, oi, ol)
+        torch.cuda.synchronize()
+        return oi.cpu().numpy(), ol.cpu().numpy()
+
+    def verify(self, hv_d, drafts, B, k):
+        torch = self.torch
+        a = torch.full((B, k + 1), -7, dtype=torch.int32, device="cuda")
+        lg = torch.full((B, k + 1), float("nan"), dtype=torch.float32, device="cuda")
+        acc = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+        tok = torch.full((B, k + 1), -7, dtype=torch.int32, device="cuda")
+        self.mtp.mtp_verify_accept_tiled(hv_d, self.head, self.V, dev_i32(drafts), B, k, a, acc,
+                                         tok, lg)
+        torch.cuda.synchronize()
+        return {"argmax": a.cpu().numpy(), "logit": lg.cpu().numpy(),
+                "accept": acc.cpu().numpy(), "tokens": tok.cpu().numpy()}
+
+
 def _drafts_and_verify(torch, mtp, wk, W, draft_rows=None, verify_seqs=None, strict_draft=(),
-                       strict_verify=()):
+                       strict_verify=(), layout="rows"):
     """Run the workload's draft calls and its verify call; check sampled rows
     (None: all) against the oracle."""
-    print(f"[{wk.name}] H={wk.H} V={wk.V} C={wk.C} B={wk.B} k={wk.k}", flush=True)
+    print(f"[{wk.name}] H={wk.H} V={wk.V} C={wk.C} B={wk.B} k={wk.k} layout={layout}", flush=True)
     ids = wl.candidate_ids(wk.V, wk.C, wk.seed)
     table = oracle.pack(W, ids)
     W_d = dev_bf16(W)
@@ -47,10 +79,14 @@ def _drafts_and_verify(torch, mtp, wk, W, draft_rows=None, verify_seqs=None, str
     assert np.array_equal(table_d[:64].cpu().numpy().view(np.uint16), table[:64])
     assert np.array_equal(table_d[-64:].cpu().numpy().view(np.uint16), table[-64:])
     ids_d = dev_i32(ids)
+    tiled = _Tiled(torch, mtp, W_d, ids_d, wk.C, wk.V, wk.H) if layout == "tiled" else None
     reports = []
     for call in range(wk.draft_calls):
         h = wl.hidden_states(wk.Md, wk.H, wk.seed, block=call)
-        g_ids, g_logit = gpu_draft(dev_bf16(h), table_d, ids_d)
+        if tiled is None:
+            g_ids, g_logit = gpu_draft(dev_bf16(h), table_d, ids_d)
+        else:
+            g_ids, g_logit = tiled.draft(dev_bf16(h), ids_d)
         assert np.isin(g_ids, ids).all()
         rows = list(range(wk.Md)) if draft_rows is None else sorted(
             set(draft_rows) | {r for c, r in strict_draft if c == call})
@@ -72,7 +108,10 @@ def _drafts_and_verify(torch, mtp, wk, W, draft_rows=None, verify_seqs=None, str
     if verify_seqs is not None:
         others = [b for b in range(wk.B) if b not in seqs]
         drafts[others] = wl.uniform_drafts(wk.B, wk.k, ids, wk.seed + 1)[others]
-    g = gpu_verify(dev_bf16(hv), W_d, drafts, wk.B, wk.k)
+    if tiled is None:
+        g = gpu_verify(dev_bf16(hv), W_d, drafts, wk.B, wk.k)
+    else:
+        g = tiled.verify(dev_bf16(hv), drafts, wk.B, wk.k)
     strict = [i for i, r in enumerate(vrows) if r in set(strict_verify)]
     reports.append(check_rows(g["argmax"].ravel()[vrows], g["logit"].ravel()[vrows], orc_v,
                               hv[vrows], W, None, strict=strict))
@@ -133,15 +172,17 @@ def test_draft_head_ablation(torch, mtp):
 
 
 @pytest.mark.timeout(900)
-def test_batched_verify(torch, mtp):
+@pytest.mark.parametrize("layout", ["rows", "tiled"])
+def test_batched_verify(torch, mtp, layout):
     """H=4096: draft calls with 8 rows (x3), verify 8 sequences x 4 = 32 rows."""
     wk = wl.workload("batched_verify")
     W = wl.head_weights(wk.V, wk.H, wk.seed)
-    _drafts_and_verify(torch, mtp, wk, W)
+    _drafts_and_verify(torch, mtp, wk, W, layout=layout)
 
 
 @pytest.mark.timeout(900)
-def test_mtp4_large_with_exact_ties(torch, mtp):
+@pytest.mark.parametrize("layout", ["rows", "tiled"])
+def test_mtp4_large_with_exact_ties(torch, mtp, layout):
     """H=5120: draft calls with 32 rows (x4), verify 32 x 5 = 160 rows, p=0.5;
     1% of verify rows and of first-call draft rows hold an exact tie (the
     winner's head row copied to a partner id before packing, half of the
@@ -174,4 +215,5 @@ def test_mtp4_large_with_exact_ties(torch, mtp):
     assert list(chk["id"]) == [min(p) for p in pairs[:len(vt.rows)]]
     strict_draft = [(0, int(r)) for r in dt.rows]
     _drafts_and_verify(torch, mtp, wk, W, draft_rows=[0, 13, 31], verify_seqs=[0, 11, 31],
-                       strict_draft=strict_draft, strict_verify=[int(r) for r in vt.rows])
+                       strict_draft=strict_draft, strict_verify=[int(r) for r in vt.rows],
+                       layout=layout)
