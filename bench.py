@@ -38,9 +38,9 @@ METRIC = ("draft/verify calls/s and achieved HBM GB/s (% peak) at 248,320-vocab,
 HBM_PEAK_GBPS = 8000.0
 # sources that define each path's kernels and their launch configuration
 KERNEL_SOURCES = {
-    "valu": ("common.hpp", "gemv_valu.hip", "launch.hpp", "api.cpp"),
-    "mfma": ("common.hpp", "gemm_mfma.hip", "launch.hpp", "api.cpp"),
-    "dma": ("common.hpp", "gemm_dma.hip", "launch.hpp", "api.cpp"),
+    "valu": ("common.hpp", "gemv_valu.hip", "launch.hpp"),
+    "mfma": ("common.hpp", "gemm_mfma.hip", "launch.hpp"),
+    "dma": ("common.hpp", "gemm_dma.hip", "launch.hpp"),
 }
 
 
