@@ -55,6 +55,12 @@ def _load() -> ctypes.CDLL:
         raise ImportError(
             f"HIP library not built: {LIB_PATH} is missing "
             "(run python -m speculative_decoding_argmax_amd.build)")
+    # One HIP runtime per process: torch ships its own libamdhip64.so.7. If
+    # the library were loaded first, the dynamic linker would bind it to the
+    # system copy, torch would then bring in a second runtime, and the
+    # library's launches would find no device. Importing torch first makes
+    # the library bind to the runtime that owns torch's memory and streams.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     P = ctypes.c_void_p
     I = ctypes.c_int

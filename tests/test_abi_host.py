@@ -159,3 +159,20 @@ def test_tiled_entry_points_reject_bad_arguments():
     assert v(FAKE, 1, 3, 64, None, 100, FAKE, FAKE, None, FAKE, FAKE, FAKE, 4096, None) == INVALID
     assert v(FAKE, 1, 3, 64, FAKE, 100, FAKE, FAKE, None, FAKE, FAKE, FAKE, 16, None) == \
         mtp.MTP_ERR_WORKSPACE
+
+
+def test_one_hip_runtime_per_process():
+    """Importing the binding first must not load a second HIP runtime next to
+    torch's own (the library's launches would then find no device)."""
+    import subprocess
+    import sys
+    code = ("from speculative_decoding_argmax_amd import mtp\n"
+            "import torch\n"
+            "paths = {l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}\n"
+            "print(len(paths), sorted(paths))\n")
+    root = __import__("os").path.dirname(__import__("os").path.dirname(__file__))
+    out = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True,
+                         timeout=300)
+    assert out.returncode == 0, out.stderr
+    n = int(out.stdout.split()[0])
+    assert n == 1, out.stdout

@@ -70,7 +70,7 @@ def test_pack_tiled_bad_ids_are_zero(torch, mtp):
 TILED_SHAPES = [  # (M, N, H)
     (1, 1, 8), (1, 1000, 8), (3, 4097, 256), (8, 3001, 4096), (2, 999, 5120), (16, 1025, 640),
     (17, 333, 1032), (32, 5000, 1024), (48, 2049, 4096), (64, 4000, 2048), (100, 700, 512),
-    (160, 1111, 5120), (161, 300, 256), (1, 257, 16384),
+    (160, 1111, 5120), (161, 300, 256), (1, 257, 16384), (90, 1500, 1024), (130, 2100, 768),
 ]
 
 
