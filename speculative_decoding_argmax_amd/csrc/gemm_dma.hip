@@ -291,11 +291,11 @@ hipError_t launch_dma(const DmaLaunch &L, int nb) {
   switch (nb) {
     case 1: return launch_dma_cfg<1, 1, 2, 4, 8, NT>(L);
     case 2: return launch_dma_cfg<2, 2, 2, 4, 8, NT>(L);
-    case 3: return launch_dma_cfg<3, 1, 2, 4, 8, NT>(L);
-    case 4: return launch_dma_cfg<4, 1, 2, 4, 8, NT>(L);
-    case 6: return launch_dma_cfg<6, 2, 2, 3, 8, NT>(L);
-    case 8: return launch_dma_cfg<8, 2, 2, 3, 8, NT>(L);
-    case 10: return launch_dma_cfg<10, 2, 2, 3, 8, NT>(L);
+    case 3: return launch_dma_cfg<3, 2, 2, 3, 8, NT>(L);
+    case 4: return launch_dma_cfg<4, 2, 2, 3, 8, NT>(L);
+    case 6: return launch_dma_cfg<6, 4, 1, 3, 8, NT>(L);
+    case 8: return launch_dma_cfg<8, 4, 1, 3, 8, NT>(L);
+    case 10: return launch_dma_cfg<10, 4, 1, 3, 8, NT>(L);
     default: return hipErrorInvalidValue;
   }
 }
