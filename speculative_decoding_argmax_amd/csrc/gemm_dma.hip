@@ -99,13 +99,19 @@ __global__ void __launch_bounds__(WV * 64)
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  // wave index as a scalar: copy addresses and LDS offsets are then
+  // computed on the scalar unit, not per lane
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int j = lane & 15;
   const int g = lane >> 4;
   const int m0 = blockIdx.y * NB * 16;
+  // grid size and position held in registers: the barrier's compiler fence
+  // would otherwise make every chunk reload gridDim from the dispatch packet
+  const int gdx = gridDim.x;
+  const int bx = blockIdx.x;
   const int nchunks = S / KS;                  // S is a multiple of 4
   const int ntiles = (N + TV - 1) / TV;
-  const int my_tiles = blockIdx.x < ntiles ? (ntiles - 1 - blockIdx.x) / gridDim.x + 1 : 0;
+  const int my_tiles = bx < ntiles ? (ntiles - 1 - bx) / gdx + 1 : 0;
   const int total = my_tiles * nchunks;
   const int nrb = ((N + 63) / 64) * 4;         // 16-row blocks stored (padded)
 
@@ -117,14 +123,20 @@ __global__ void __launch_bounds__(WV * 64)
     else return slot3;
   };
 
-  // Copy chunk `it` into a slot. Fragment f < AF: weights, step f / RBT of the
-  // chunk, 16-row block f % RBT of the tile; f >= AF: hidden fragment for step
+  // Copy the next chunk (tile iss_t, K chunk iss_c) into a slot, then step
+  // the position. Fragment f < AF: weights, step f / RBT of the chunk,
+  // 16-row block f % RBT of the tile; f >= AF: hidden fragment for step
   // (f - AF) / NB, hidden block (f - AF) % NB. Every wave issues PER_WAVE
   // copies; surplus ones repeat the last fragment (same bytes, same place).
-  auto issue = [&](auto tag, int it) {
+  int iss_t = bx, iss_c = 0;
+  auto issue = [&](auto tag) {
     uint4 *base = slot(tag);
-    const int tile = blockIdx.x + (it / nchunks) * gridDim.x;
-    const int c = it % nchunks;
+    const int tile = iss_t;
+    const int c = iss_c;
+    if (++iss_c == nchunks) {
+      iss_c = 0;
+      iss_t += gdx;
+    }
 #pragma unroll
     for (int q = 0; q < PER_WAVE; ++q) {
       int f = wave + WV * q;
@@ -163,11 +175,12 @@ __global__ void __launch_bounds__(WV * 64)
     bi[nb] = -1;
   }
 
-  if (0 < total) issue(std::integral_constant<int, 0>{}, 0);
-  if (1 < total) issue(std::integral_constant<int, 1>{}, 1);
+  if (0 < total) issue(std::integral_constant<int, 0>{});
+  if (1 < total) issue(std::integral_constant<int, 1>{});
   if constexpr (NBUF > 3) {
-    if (2 < total) issue(std::integral_constant<int, 2>{}, 2);
+    if (2 < total) issue(std::integral_constant<int, 2>{});
   }
+  int cur_t = bx, cur_c = 0;  // position of the chunk being multiplied
 
   auto body = [&](auto tag, int it) {
     constexpr int SL = decltype(tag)::value;
@@ -177,7 +190,7 @@ __global__ void __launch_bounds__(WV * 64)
     else
       wait_vmcnt<0>();
     barrier_no_fence();
-    if (it + NBUF - 1 < total) issue(std::integral_constant<int, (SL + NBUF - 1) % NBUF>{}, it + NBUF - 1);
+    if (it + NBUF - 1 < total) issue(std::integral_constant<int, (SL + NBUF - 1) % NBUF>{});
     const uint4 *A = slot(tag);
     const uint4 *Bf = A + AF * kWave;
 #pragma unroll
@@ -192,8 +205,10 @@ __global__ void __launch_bounds__(WV * 64)
         for (int rw = 0; rw < RW; ++rw) acc[rw][nb] = mfma16_dma(a[rw], b, acc[rw][nb]);
       }
     }
-    if (it % nchunks == nchunks - 1) {
-      const int tile = blockIdx.x + (it / nchunks) * gridDim.x;
+    if (++cur_c == nchunks) {
+      const int tile = cur_t;
+      cur_c = 0;
+      cur_t += gdx;
       const int vbase = tile * TV + wave * RW * 16 + 4 * g;
 #pragma unroll
       for (int rw = 0; rw < RW; ++rw) {
