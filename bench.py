@@ -54,6 +54,9 @@ def parse_args():
     ap.add_argument("--layout", choices=("auto", "rows", "tiled"), default="auto",
                     help="table layout: row-major, or the 64-row tiled layout of include/mtp.h "
                          "(auto: rows when every call has at most 8 hidden rows)")
+    ap.add_argument("--graph", action="store_true",
+                    help="time the steps as replays of a captured HIP graph (mtp_graph_*); "
+                         "per-call durations still come from event-bracketed eager launches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall-clock budget of the CPU oracle sample")
@@ -102,6 +105,10 @@ def main() -> int:
     wk = wl.workload(args.workload)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.graph:
+        # graph capture needs a created stream (the null stream cannot be
+        # captured); everything below runs on it
+        torch.cuda.set_stream(torch.cuda.Stream(dev))
     stream = torch.cuda.current_stream()
 
     t0 = time.time()
@@ -190,27 +197,53 @@ def main() -> int:
     torch.cuda.synchronize()
 
     K = args.steps
-    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(K)]
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for i in range(K):
-        step(i, evs[i])
-    torch.cuda.synchronize()
-    t_total = time.perf_counter() - t_start
+    graphs = []
+    if args.graph:
+        # step i reads table copies (i * draft_calls + c) % n_tab: one graph
+        # per phase i % n_tab
+        for ph in range(n_tab):
+            g = mtp.Graph()
+            g.begin()
+            step(ph)
+            g.end()
+            graphs.append(g)
+        for i in range(args.warmup):
+            graphs[i % n_tab].launch()
+        torch.cuda.synchronize()
+
+    def timed_steps(with_events: bool, use_graph: bool):
+        evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(K)] \
+            if with_events else None
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(K):
+            if use_graph:
+                if evs:
+                    evs[i][0].record(stream)
+                graphs[i % n_tab].launch()
+                if evs:
+                    evs[i][2].record(stream)
+            else:
+                step(i, evs[i] if evs else None)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0, evs
+
+    t_total, evs = timed_steps(True, bool(graphs))
+    graph_step_ms = None
+    if graphs:
+        graph_step_ms = [e[0].elapsed_time(e[2]) for e in evs]
+        # per-call durations: the same kernels launched eagerly, each block
+        # bracketed by events
+        _, evs = timed_steps(True, False)
 
     # per-call durations: the draft block's span over its calls (inter-kernel
     # gaps included), the verify launch's own span
     draft_ms = [evs[i][0].elapsed_time(evs[i][1]) / wk.draft_calls for i in range(K)]
     verify_ms = [evs[i][1].elapsed_time(evs[i][2]) for i in range(K)]
 
-    # Untimed context: the same calls without per-launch events, and the
+    # Untimed context: the same steps without per-launch events, and the
     # draft call re-reading one table (Infinity Cache may serve part of it).
-    torch.cuda.synchronize()
-    tq = time.perf_counter()
-    for i in range(K):
-        step(i)
-    torch.cuda.synchronize()
-    t_noev = time.perf_counter() - tq
+    t_noev, _ = timed_steps(False, bool(graphs))
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for i in range(K):
@@ -275,10 +308,14 @@ def main() -> int:
                         f"verify call (M={Mv}, {V}-row head), H={H}",
             "H": H, "V": V, "C": C, "B": wk.B, "k": wk.k, "draft_calls": wk.draft_calls,
             "accumulate": "f32", "table_copies": n_tab, "seed": wk.seed, "layout": layout,
+            "step": "hip_graph" if graphs else "eager",
         },
         "calls": {"draft": draft_stats, "verify": verify_stats},
         "context": {
             "ms_per_step_without_kernel_events": round(t_noev * 1000.0 / K, 4),
+            "step_mode": "hip_graph" if graphs else "eager",
+            "graph_step_us_mean": round(statistics.mean(graph_step_ms) * 1000.0, 2)
+            if graph_step_ms else None,
             "draft_same_table_us": round(warm_draft_us, 2),
             "setup_s": round(setup_s, 1),
         },

@@ -236,6 +236,48 @@ mtp_status mtp_verify_accept_tiled_cfg(const mtp_bf16 *hidden, int B, int k, int
                                        size_t ws_bytes, hipStream_t stream,
                                        const mtp_config *cfg);
 
+/*
+ * Graph-captured MTP step.
+ *
+ * Records the library calls a caller makes on `stream` between
+ * mtp_graph_begin and mtp_graph_end into one HIP graph, so that a whole MTP
+ * round (k draft calls, then verify with acceptance) is submitted with one
+ * launch and replayed without per-kernel launch cost. Every call of this
+ * library only enqueues kernels (no allocation, no host synchronisation, no
+ * memset; the workspaces reset themselves), which is what capture requires.
+ * [edge-inference runtime blog, section 3 (CUDA Graph), subsections 3.2 and
+ * 3.3: capture once, replay every decode step; nothing inside the capture
+ * may allocate or branch on device data. Production-inference page on vLLM,
+ * section 5: decode repeats many small launches, so the replayed graph
+ * removes their submission cost.]
+ *
+ * Usage: mtp_graph_begin(s); <calls on s>; mtp_graph_end(s, &g); then
+ * mtp_graph_launch(g, s) any number of times. A replay reads the device
+ * buffers whose pointers were passed during capture: write new inputs into
+ * those buffers (stream-ordered before the launch) and read outputs from the
+ * captured output buffers after it. The buffers must stay allocated until
+ * mtp_graph_destroy. Replays of one graph, and any other use of the
+ * workspaces it captured, must be stream-ordered.
+ *
+ * stream must be a created stream (the null stream cannot be captured).
+ * Capture mode is thread-local: other threads may keep using HIP. An error
+ * inside the capture (an argument error of a captured call) leaves the stream
+ * capturing; mtp_graph_end then ends the capture and returns the error of
+ * ending it, and the caller discards the graph.
+ * mtp_graph_end and mtp_graph_destroy create and free HIP graph objects
+ * (host-side set-up work); mtp_graph_launch allocates nothing.
+ */
+typedef struct mtp_graph mtp_graph;
+
+mtp_status mtp_graph_begin(hipStream_t stream);
+/* Ends the capture on `stream` and instantiates it; *graph receives the
+ * handle (NULL on error). */
+mtp_status mtp_graph_end(hipStream_t stream, mtp_graph **graph);
+/* Enqueues one replay of the captured step on `stream`. */
+mtp_status mtp_graph_launch(const mtp_graph *graph, hipStream_t stream);
+/* Frees the graph (NULL is ignored). Call after its last replay finished. */
+void mtp_graph_destroy(mtp_graph *graph);
+
 #ifdef __cplusplus
 }
 #endif

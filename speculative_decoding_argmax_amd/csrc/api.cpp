@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <new>
 #include <cstdint>
 #include <cstring>
 
@@ -372,6 +373,58 @@ mtp_status mtp_verify_accept_tiled(const mtp_bf16 *hidden, int B, int k, int H,
   return mtp_verify_accept_tiled_cfg(hidden, B, k, H, head_tiled, V, draft, out_argmax,
                                      out_logit, out_accept, out_tokens, ws, ws_bytes, stream,
                                      nullptr);
+}
+
+struct mtp_graph {
+  hipGraph_t graph;
+  hipGraphExec_t exec;
+};
+
+mtp_status mtp_graph_begin(hipStream_t stream) {
+  if (!stream) return MTP_ERR_INVALID_ARG;
+  const hipError_t e = hipStreamBeginCapture(stream, hipStreamCaptureModeThreadLocal);
+  if (e != hipSuccess) return hip_fail(e);
+  return MTP_OK;
+}
+
+mtp_status mtp_graph_end(hipStream_t stream, mtp_graph **out) {
+  if (!out) return MTP_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (!stream) return MTP_ERR_INVALID_ARG;
+  hipGraph_t graph = nullptr;
+  hipError_t e = hipStreamEndCapture(stream, &graph);
+  if (e != hipSuccess) {
+    if (graph) (void)hipGraphDestroy(graph);
+    return hip_fail(e);
+  }
+  hipGraphExec_t exec = nullptr;
+  e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+  if (e != hipSuccess) {
+    (void)hipGraphDestroy(graph);
+    return hip_fail(e);
+  }
+  mtp_graph *g = new (std::nothrow) mtp_graph{graph, exec};
+  if (!g) {
+    (void)hipGraphExecDestroy(exec);
+    (void)hipGraphDestroy(graph);
+    return hip_fail(hipErrorOutOfMemory);
+  }
+  *out = g;
+  return MTP_OK;
+}
+
+mtp_status mtp_graph_launch(const mtp_graph *g, hipStream_t stream) {
+  if (!g) return MTP_ERR_INVALID_ARG;
+  const hipError_t e = hipGraphLaunch(g->exec, stream);
+  if (e != hipSuccess) return hip_fail(e);
+  return MTP_OK;
+}
+
+void mtp_graph_destroy(mtp_graph *g) {
+  if (!g) return;
+  (void)hipGraphExecDestroy(g->exec);
+  (void)hipGraphDestroy(g->graph);
+  delete g;
 }
 
 }  // extern "C"

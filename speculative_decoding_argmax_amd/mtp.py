@@ -85,6 +85,10 @@ def _load() -> ctypes.CDLL:
         "mtp_draft_argmax_tiled_cfg": ([P, I, I, P, P, I64, P, P, P, S, P, P], I),
         "mtp_verify_accept_tiled": ([P, I, I, I, P, I64, P, P, P, P, P, P, S, P], I),
         "mtp_verify_accept_tiled_cfg": ([P, I, I, I, P, I64, P, P, P, P, P, P, S, P, P], I),
+        "mtp_graph_begin": ([P], I),
+        "mtp_graph_end": ([P, ctypes.POINTER(P)], I),
+        "mtp_graph_launch": ([P, P], I),
+        "mtp_graph_destroy": ([P], None),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -186,6 +190,15 @@ def alloc_workspace(nbytes: int, device=None, stream=None):
     return ws
 
 
+_capturing = 0
+
+
+def _no_alloc_in_capture(what: str) -> None:
+    if _capturing:
+        raise ValueError(f"{what}: pass ws explicitly; a call captured into a graph "
+                         "must not allocate (the graph keeps the workspace pointer)")
+
+
 def mtp_workspace_init(ws, stream=None) -> None:
     torch = _torch()
     p = _ptr(ws, "ws", (torch.int64, torch.uint8, torch.int32))
@@ -218,6 +231,7 @@ def mtp_draft_argmax(hidden, table, ids, out_ids, out_logit=None, ws=None, strea
     if out_ids.numel() != M or (out_logit is not None and out_logit.numel() != M):
         raise ValueError("outputs must have M entries")
     if ws is None:
+        _no_alloc_in_capture("mtp_draft_argmax")
         ws = alloc_workspace(mtp_draft_workspace_bytes(M, C, H), hidden.device, stream)
     cfg = _cfg(path, blocks_per_cu)
     _check(lib.mtp_draft_argmax_cfg(
@@ -243,6 +257,7 @@ def mtp_verify_accept(hidden, head, draft, B: int, k: int, out_argmax, out_accep
     if draft is not None and draft.numel() != B * k:
         raise ValueError("draft must be [B][k]")
     if ws is None:
+        _no_alloc_in_capture("mtp_verify_accept")
         ws = alloc_workspace(mtp_verify_workspace_bytes(B, k, V, H), hidden.device, stream)
     cfg = _cfg(path, blocks_per_cu)
     _check(lib.mtp_verify_accept_cfg(
@@ -338,3 +353,59 @@ def mtp_verify_accept_tiled(hidden, head_tiled, V: int, draft, B: int, k: int, o
         _ptr(out_tokens, "out_tokens", (torch.int32,)),
         _ptr(ws, "ws", (torch.int64, torch.uint8, torch.int32)), ws.numel() * ws.element_size(),
         _stream(stream), ctypes.byref(cfg)), "mtp_verify_accept_tiled")
+
+
+# ---- graph-captured MTP step ----------------------------------------------
+
+
+class Graph:
+    """One captured MTP step (``mtp_graph_begin`` / ``mtp_graph_end``).
+
+    Capture on a created (non-null) stream::
+
+        g = Graph()
+        with torch.cuda.stream(s):
+            g.begin()
+            mtp_draft_argmax(...); ...; mtp_verify_accept(...)
+            g.end()
+            g.launch()          # replays the step on the current stream
+
+    Every buffer passed during capture must stay allocated until ``destroy``;
+    allocate all of them before ``begin``.
+    """
+
+    def __init__(self):
+        self._h = _null_handle()
+
+    def begin(self, stream=None) -> None:
+        global _capturing
+        _check(lib.mtp_graph_begin(_stream(stream)), "mtp_graph_begin")
+        _capturing += 1
+
+    def end(self, stream=None) -> None:
+        global _capturing
+        _capturing = max(0, _capturing - 1)
+        h = _null_handle()
+        _check(lib.mtp_graph_end(_stream(stream), ctypes.byref(h)), "mtp_graph_end")
+        self.destroy()
+        self._h = h
+
+    def launch(self, stream=None) -> None:
+        if not self._h:
+            raise MTPError(MTP_ERR_INVALID_ARG, "mtp_graph_launch (no captured graph)")
+        _check(lib.mtp_graph_launch(self._h, _stream(stream)), "mtp_graph_launch")
+
+    def destroy(self) -> None:
+        if self._h:
+            lib.mtp_graph_destroy(self._h)
+            self._h = _null_handle()
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+
+def _null_handle():
+    return ctypes.c_void_p()
