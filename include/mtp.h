@@ -237,6 +237,36 @@ mtp_status mtp_verify_accept_tiled_cfg(const mtp_bf16 *hidden, int B, int k, int
                                        const mtp_config *cfg);
 
 /*
+ * Draft over gathered candidates (no packed table):
+ *   out_ids[m] = argmax over i < C of  hidden[m] . head[ids[i]]   (an id)
+ * The candidate list may change every call: a fixed set plus rows chosen for
+ * this step, in any order, repeats allowed. Ties go to the lowest id,
+ * whatever the order of the list; an id outside [0, V) is not a candidate
+ * (its row is never read); with no valid id, out_ids[m] = -1 and
+ * out_logit[m] = NaN. Reads C head rows of H bf16 each, in list order, so
+ * the cost per call is that of a packed table of C rows, without the packing.
+ * hidden device [M][H] bf16; head device [V][H] bf16; ids device int32 [C];
+ * out_ids / out_logit / ws as mtp_draft_argmax (workspace size
+ * mtp_draft_workspace_bytes(M, C, H)). Runs on the vector-ALU kernel (any M;
+ * more than its per-pass row count re-reads the rows); cfg->path must be
+ * MTP_PATH_AUTO or MTP_PATH_VALU (MTP_ERR_UNSUPPORTED otherwise), and H must
+ * be at most 16,384.
+ * [Qwen3.8 Flash dual-Spark tuning log, section "read one fewer big table":
+ * the upstream work on the same bottleneck drafts over a fixed candidate set
+ * plus rows picked per step; reading rows through the id list makes a
+ * per-step set cost no repacking.]
+ */
+mtp_status mtp_draft_argmax_gather(const mtp_bf16 *hidden, int M, int H, const mtp_bf16 *head,
+                                   int64_t V, const int32_t *ids, int64_t C, int32_t *out_ids,
+                                   float *out_logit, void *ws, size_t ws_bytes,
+                                   hipStream_t stream);
+mtp_status mtp_draft_argmax_gather_cfg(const mtp_bf16 *hidden, int M, int H,
+                                       const mtp_bf16 *head, int64_t V, const int32_t *ids,
+                                       int64_t C, int32_t *out_ids, float *out_logit, void *ws,
+                                       size_t ws_bytes, hipStream_t stream,
+                                       const mtp_config *cfg);
+
+/*
  * Graph-captured MTP step.
  *
  * Records the library calls a caller makes on `stream` between

@@ -11,6 +11,8 @@ the pages each one follows):
   logits(x, w)                [M][N] fp64 logits
   argmax(x, w, ids=None)      per-row first maximum of the fp32-rounded logits
   draft(h, table, ids)        argmax over the candidate table, mapped to ids
+  draft_gather(h, head, ids)  argmax over head rows named by an id list (any
+                              order, repeats; out-of-range ids are no candidates)
   verify(hv, head, B, k)      argmax over the full head, shaped [B][k+1]
   accept(draft, target)       greedy acceptance plus bonus token
 """
@@ -191,6 +193,25 @@ def pack(head: np.ndarray, ids: np.ndarray) -> np.ndarray:
 def draft(h: np.ndarray, table: np.ndarray, ids: np.ndarray) -> Dict[str, np.ndarray]:
     """Draft step: argmax of each hidden row over the candidate table, as global ids."""
     return argmax(h, table, ids)
+
+
+def draft_gather(h: np.ndarray, head: np.ndarray, ids: np.ndarray) -> Dict[str, np.ndarray]:
+    """Draft over a candidate set given as an id list (Qwen3.8 Flash dual-Spark
+    tuning log, section "read one fewer big table": a fixed candidate set plus
+    rows chosen per step). The candidates are the distinct ids of the list that
+    name a head row; the result is the draft over that set, i.e. the pinned
+    argmax over the sorted set's packed rows, so ties go to the lowest id
+    whatever the order of the list. With no valid id: id -1, logit NaN."""
+    head = _bf16(head)
+    V = head.shape[0]
+    ids = np.asarray(ids, dtype=np.int64).ravel()
+    valid = np.unique(ids[(ids >= 0) & (ids < V)]).astype(np.int32)
+    M = np.atleast_2d(h).shape[0]
+    if valid.size == 0:
+        return {"id": np.full(M, -1, np.int32), "logit": np.full(M, np.nan, np.float32),
+                "exact": np.full(M, np.nan), "runner_id": np.full(M, -1, np.int32),
+                "runner_exact": np.full(M, np.nan)}
+    return argmax(h, pack(head, valid), valid)
 
 
 def accept(draft_ids: np.ndarray, target: np.ndarray) -> Dict[str, np.ndarray]:

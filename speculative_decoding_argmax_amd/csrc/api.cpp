@@ -68,11 +68,18 @@ mtp_status check_cfg(const mtp_config *cfg) {
 // Score M hidden rows against N table rows and finish through `sink`.
 // Path: the vector-ALU kernel while one pass keeps every hidden row's slice in
 // registers (few rows), the matrix-core kernel beyond.
+// Gathered candidates (gather_ids != nullptr: candidate i is head row
+// gather_ids[i]) run on the vector-ALU kernel only.
 mtp_status run_rows(const mtp_bf16 *X, int M, int H, const mtp_bf16 *W, int64_t N,
-                    mtp::RowSink sink, hipStream_t stream, const mtp_config *cfg) {
+                    mtp::RowSink sink, hipStream_t stream, const mtp_config *cfg,
+                    const int32_t *gather_ids = nullptr, int64_t gather_V = 0) {
   const int nch = H / 8;
   const int ncl = mtp::valu_ncl_for(nch);
   int path = cfg ? cfg->path : MTP_PATH_AUTO;
+  if (gather_ids) {
+    if (path == MTP_PATH_MFMA) return MTP_ERR_UNSUPPORTED;
+    path = MTP_PATH_VALU;
+  }
   if (path == MTP_PATH_AUTO)
     path = (ncl != 0 && mtp::valu_rows_for(M, ncl) >= M) ? MTP_PATH_VALU : MTP_PATH_MFMA;
   int cus = 0;
@@ -94,6 +101,8 @@ mtp_status run_rows(const mtp_bf16 *X, int M, int H, const mtp_bf16 *W, int64_t 
     L.prefetch = true;
     L.sink = sink;
     L.stream = stream;
+    L.gather_ids = gather_ids;
+    L.gather_V = gather_V;
     e = mtp::launch_valu(L, mtp::valu_rows_for(M, ncl), ncl);
   } else {
     const int per_cu = (cfg && cfg->blocks_per_cu > 0) ? cfg->blocks_per_cu : 2;
@@ -373,6 +382,29 @@ mtp_status mtp_verify_accept_tiled(const mtp_bf16 *hidden, int B, int k, int H,
   return mtp_verify_accept_tiled_cfg(hidden, B, k, H, head_tiled, V, draft, out_argmax,
                                      out_logit, out_accept, out_tokens, ws, ws_bytes, stream,
                                      nullptr);
+}
+
+mtp_status mtp_draft_argmax_gather_cfg(const mtp_bf16 *hidden, int M, int H,
+                                       const mtp_bf16 *head, int64_t V, const int32_t *ids,
+                                       int64_t C, int32_t *out_ids, float *out_logit, void *ws,
+                                       size_t ws_bytes, hipStream_t stream,
+                                       const mtp_config *cfg) {
+  if (!ids) return MTP_ERR_INVALID_ARG;
+  if (V < 1 || V > INT32_MAX) return MTP_ERR_INVALID_ARG;
+  mtp_status st =
+      check_draft_args(hidden, M, H, head, ids, C, out_ids, out_logit, ws, ws_bytes, cfg);
+  if (st != MTP_OK) return st;
+  // the key of a gathered candidate is its id, so the finish needs no id map
+  return run_rows(hidden, M, H, head, C, draft_sink(ws, nullptr, out_ids, out_logit, M), stream,
+                  cfg, ids, V);
+}
+
+mtp_status mtp_draft_argmax_gather(const mtp_bf16 *hidden, int M, int H, const mtp_bf16 *head,
+                                   int64_t V, const int32_t *ids, int64_t C, int32_t *out_ids,
+                                   float *out_logit, void *ws, size_t ws_bytes,
+                                   hipStream_t stream) {
+  return mtp_draft_argmax_gather_cfg(hidden, M, H, head, V, ids, C, out_ids, out_logit, ws,
+                                     ws_bytes, stream, nullptr);
 }
 
 struct mtp_graph {

@@ -31,38 +31,74 @@ __device__ __forceinline__ uint4 load_stream(const uint4 *p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-// Loads RB rows x NCL chunks of this lane's slice. ROWS_OK / COLS_OK say the
-// whole block lies inside the table, so no predication is needed.
-template <int RB, int NCL, bool ROWS_OK, bool COLS_OK>
-__device__ __forceinline__ void load_block(uint4 (&w)[RB][NCL], const uint4 *__restrict__ W,
-                                           int64_t r0, int64_t N, int nch, int lane) {
+// Where the candidate rows live. Packed: row i of the table is candidate i.
+// Gathered: candidate i is head row ids[i] (any order, repeats allowed); an
+// id outside [0, V) is no candidate, and its row is never read.
+struct RowSource {
+  const int32_t *ids;  // gathered rows: ids[N]; nullptr for a packed table
+  int64_t V;           // rows of the head (gathered rows only)
+};
+
+// Table row of candidate i (< 0: not a candidate). Packed: i itself;
+// gathered: ids[i] if it names a head row.
+template <bool GATHER>
+__device__ __forceinline__ int32_t source_row(const RowSource &src, int64_t i) {
+  if (!GATHER) return (int32_t)i;
+  const int32_t id = src.ids[i];
+  return (id >= 0 && id < src.V) ? id : -1;
+}
+
+// Loads RB rows x NCL chunks of this lane's slice, row i at base + i * nch.
+// COLS_OK says every chunk is inside the row, so no column predication.
+template <int RB, int NCL, bool COLS_OK>
+__device__ __forceinline__ void load_consecutive(uint4 (&w)[RB][NCL],
+                                                 const uint4 *__restrict__ base, int nch,
+                                                 int lane) {
 #pragma unroll
   for (int i = 0; i < RB; ++i) {
-    const uint4 *row = W + (r0 + i) * nch + lane;
 #pragma unroll
     for (int c = 0; c < NCL; ++c) {
-      const bool ok = (ROWS_OK || r0 + i < N) && (COLS_OK || lane + kWave * c < nch);
+      const bool ok = COLS_OK || lane + kWave * c < nch;
+      w[i][c] = ok ? load_stream(base + (int64_t)i * nch + kWave * c)
+                   : make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+}
+
+// Loads the rows of candidates r0 .. r0 + RB - 1 and sets rows[i] to each
+// one's table row (-1: past N or not a candidate). A full block of a packed
+// table is consecutive rows addressed straight from r0. Otherwise every row
+// is looked up; a non-candidate loads table row 0 instead, so no load needs
+// a row predicate (the argmax skips it).
+template <int RB, int NCL, bool COLS_OK, bool GATHER>
+__device__ __forceinline__ void load_rows(uint4 (&w)[RB][NCL], int32_t (&rows)[RB],
+                                          const uint4 *__restrict__ W, const RowSource &src,
+                                          int64_t r0, int64_t N, int nch, int lane) {
+  if (!GATHER && r0 + RB <= N) {
+#pragma unroll
+    for (int i = 0; i < RB; ++i) rows[i] = (int32_t)(r0 + i);
+    load_consecutive<RB, NCL, COLS_OK>(w, W + r0 * nch + lane, nch, lane);
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < RB; ++i) {
+    rows[i] = r0 + i < N ? source_row<GATHER>(src, r0 + i) : -1;
+    const uint4 *row = W + (int64_t)(rows[i] >= 0 ? rows[i] : 0) * nch + lane;
+#pragma unroll
+    for (int c = 0; c < NCL; ++c) {
+      const bool ok = COLS_OK || lane + kWave * c < nch;
       w[i][c] = ok ? load_stream(row + kWave * c) : make_uint4(0u, 0u, 0u, 0u);
     }
   }
 }
 
-template <int RB, int NCL, bool EXACT>
-__device__ __forceinline__ void load_rows(uint4 (&w)[RB][NCL], const uint4 *__restrict__ W,
-                                          int64_t r0, int64_t N, int nch, int lane) {
-  if (r0 + RB <= N)
-    load_block<RB, NCL, true, EXACT>(w, W, r0, N, nch, lane);
-  else
-    load_block<RB, NCL, false, EXACT>(w, W, r0, N, nch, lane);
-}
-
 // MR hidden rows, NCL 16-byte chunks per lane and row, RB table rows per wave
 // iteration; PF: the next iteration's rows are loaded before this one's are
 // reduced; EXACT: H == NCL * 512 (no column predication).
-template <int MR, int NCL, int RB, bool PF, bool EXACT>
+template <int MR, int NCL, int RB, bool PF, bool EXACT, bool GATHER>
 __global__ void __launch_bounds__(kValuThreads)
     gemv_argmax_valu(const uint4 *__restrict__ X, const uint4 *__restrict__ W, int M, int64_t N,
-                     int nch, RowSink sink) {
+                     int nch, RowSource src, RowSink sink) {
   __shared__ float s_val[kValuWaves][MR];
   __shared__ int64_t s_row[kValuWaves][MR];
   __shared__ float f_val[MR];
@@ -95,17 +131,22 @@ __global__ void __launch_bounds__(kValuThreads)
   // wave-uniform row cursor, kept in scalar registers
   int64_t r0 = ((int64_t)blockIdx.x * kValuWaves + __builtin_amdgcn_readfirstlane(wave)) * RB;
   uint4 nxt[RB][NCL];
-  if (PF && r0 < N) load_rows<RB, NCL, EXACT>(nxt, W, r0, N, nch, lane);
+  int32_t rows_nxt[RB];
+  if (PF && r0 < N) load_rows<RB, NCL, EXACT, GATHER>(nxt, rows_nxt, W, src, r0, N, nch, lane);
   for (; r0 < N; r0 += stride) {
     uint4 w[RB][NCL];
+    int32_t rows[RB];
     if (PF) {
 #pragma unroll
-      for (int i = 0; i < RB; ++i)
+      for (int i = 0; i < RB; ++i) {
+        rows[i] = rows_nxt[i];
 #pragma unroll
         for (int c = 0; c < NCL; ++c) w[i][c] = nxt[i][c];
-      if (r0 + stride < N) load_rows<RB, NCL, EXACT>(nxt, W, r0 + stride, N, nch, lane);
+      }
+      if (r0 + stride < N)
+        load_rows<RB, NCL, EXACT, GATHER>(nxt, rows_nxt, W, src, r0 + stride, N, nch, lane);
     } else {
-      load_rows<RB, NCL, EXACT>(w, W, r0, N, nch, lane);
+      load_rows<RB, NCL, EXACT, GATHER>(w, rows, W, src, r0, N, nch, lane);
     }
     float acc[MR][RB];
 #pragma unroll
@@ -123,9 +164,15 @@ __global__ void __launch_bounds__(kValuThreads)
 #pragma unroll
       for (int r = 0; r < MR; ++r) {
         const float s = wave_sum(acc[r][i]);
-        if (r0 + i < N && better(s, r0 + i, bv[r], bi[r])) {
+        // argmax index: the position in a packed table, the id when gathered
+        // (for a packed table the test is written on r0 so that it stays a
+        // vector compare inside one basic block, as the scheduler needs to
+        // interleave the reductions with the next row's products)
+        const int64_t key = GATHER ? (int64_t)rows[i] : r0 + i;
+        const bool cand = GATHER ? rows[i] >= 0 : r0 + i < N;
+        if (cand && better(s, key, bv[r], bi[r])) {
           bv[r] = s;
-          bi[r] = r0 + i;
+          bi[r] = key;
         }
       }
     }
@@ -176,14 +223,26 @@ static hipError_t launch_variant(const ValuLaunch &L) {
   const int64_t want = (row_blocks + kValuWaves - 1) / kValuWaves;
   const int gx = (int)(want < L.max_blocks_x ? want : L.max_blocks_x);
   const int gy = (L.M + MR - 1) / MR;
-  if (L.nch == NCL * kWave)
-    hipLaunchKernelGGL((gemv_argmax_valu<MR, NCL, RB, PF, true>), dim3(gx, gy),
+  const RowSource src{L.gather_ids, L.gather_V};
+  const bool exact = L.nch == NCL * kWave;
+  if (L.gather_ids) {
+    if (exact)
+      hipLaunchKernelGGL((gemv_argmax_valu<MR, NCL, RB, PF, true, true>), dim3(gx, gy),
+                         dim3(kValuThreads), 0, L.stream, (const uint4 *)L.X, (const uint4 *)L.W,
+                         L.M, L.N, L.nch, src, L.sink);
+    else
+      hipLaunchKernelGGL((gemv_argmax_valu<MR, NCL, RB, PF, false, true>), dim3(gx, gy),
+                         dim3(kValuThreads), 0, L.stream, (const uint4 *)L.X, (const uint4 *)L.W,
+                         L.M, L.N, L.nch, src, L.sink);
+  } else if (exact) {
+    hipLaunchKernelGGL((gemv_argmax_valu<MR, NCL, RB, PF, true, false>), dim3(gx, gy),
                        dim3(kValuThreads), 0, L.stream, (const uint4 *)L.X, (const uint4 *)L.W,
-                       L.M, L.N, L.nch, L.sink);
-  else
-    hipLaunchKernelGGL((gemv_argmax_valu<MR, NCL, RB, PF, false>), dim3(gx, gy),
+                       L.M, L.N, L.nch, src, L.sink);
+  } else {
+    hipLaunchKernelGGL((gemv_argmax_valu<MR, NCL, RB, PF, false, false>), dim3(gx, gy),
                        dim3(kValuThreads), 0, L.stream, (const uint4 *)L.X, (const uint4 *)L.W,
-                       L.M, L.N, L.nch, L.sink);
+                       L.M, L.N, L.nch, src, L.sink);
+  }
   return hipGetLastError();
 }
 

@@ -18,6 +18,10 @@ struct ValuLaunch {
   bool prefetch;     // prefetching variant (fewer rows per iteration)
   RowSink sink;
   hipStream_t stream;
+  // gathered candidates: row i is head row gather_ids[i] of gather_V rows
+  // (W is then the head); nullptr for a packed table
+  const int32_t *gather_ids = nullptr;
+  int64_t gather_V = 0;
 };
 
 // Chunks-per-lane instantiation covering nch 16-byte chunks (0: too wide).

@@ -85,6 +85,8 @@ def _load() -> ctypes.CDLL:
         "mtp_draft_argmax_tiled_cfg": ([P, I, I, P, P, I64, P, P, P, S, P, P], I),
         "mtp_verify_accept_tiled": ([P, I, I, I, P, I64, P, P, P, P, P, P, S, P], I),
         "mtp_verify_accept_tiled_cfg": ([P, I, I, I, P, I64, P, P, P, P, P, P, S, P, P], I),
+        "mtp_draft_argmax_gather": ([P, I, I, P, I64, P, I64, P, P, P, S, P], I),
+        "mtp_draft_argmax_gather_cfg": ([P, I, I, P, I64, P, I64, P, P, P, S, P, P], I),
         "mtp_graph_begin": ([P], I),
         "mtp_graph_end": ([P, ctypes.POINTER(P)], I),
         "mtp_graph_launch": ([P, P], I),
@@ -353,6 +355,31 @@ def mtp_verify_accept_tiled(hidden, head_tiled, V: int, draft, B: int, k: int, o
         _ptr(out_tokens, "out_tokens", (torch.int32,)),
         _ptr(ws, "ws", (torch.int64, torch.uint8, torch.int32)), ws.numel() * ws.element_size(),
         _stream(stream), ctypes.byref(cfg)), "mtp_verify_accept_tiled")
+
+
+def mtp_draft_argmax_gather(hidden, head, ids, out_ids, out_logit=None, ws=None, stream=None,
+                            path: int = MTP_PATH_AUTO, blocks_per_cu: int = 0) -> None:
+    """Draft over gathered candidates: out_ids[m] = the id in ``ids`` (any
+    order; ids outside [0, V) skipped) maximising hidden[m] . head[id]."""
+    torch = _torch()
+    M, H = hidden.shape
+    V, H2 = head.shape
+    if H != H2:
+        raise ValueError("hidden and head widths differ")
+    C = ids.numel()
+    if out_ids.numel() != M or (out_logit is not None and out_logit.numel() != M):
+        raise ValueError("outputs must have M entries")
+    if ws is None:
+        _no_alloc_in_capture("mtp_draft_argmax_gather")
+        ws = alloc_workspace(mtp_draft_workspace_bytes(M, C, H), hidden.device, stream)
+    cfg = _cfg(path, blocks_per_cu)
+    _check(lib.mtp_draft_argmax_gather_cfg(
+        _ptr(hidden, "hidden", _bf16_types()), M, H, _ptr(head, "head", _bf16_types()), V,
+        _ptr(ids, "ids", (torch.int32,)), C,
+        _ptr(out_ids, "out_ids", (torch.int32,)),
+        _ptr(out_logit, "out_logit", (torch.float32,), allow_none=True),
+        _ptr(ws, "ws", (torch.int64, torch.uint8, torch.int32)), ws.numel() * ws.element_size(),
+        _stream(stream), ctypes.byref(cfg)), "mtp_draft_argmax_gather")
 
 
 # ---- graph-captured MTP step ----------------------------------------------

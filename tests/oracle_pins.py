@@ -182,6 +182,46 @@ def pin_candidate_vs_full(oracle, seed=5):
         assert full_r["id"][m] == _first_max([int(v) for v in full[m]])
 
 
+def pin_gathered_candidates(oracle, seed=29):
+    """Drafting over an id list (unsorted, repeated and out-of-range ids) picks
+    the lowest id among the maximal exact logits of the valid distinct ids,
+    computed here by brute force on the q/16 grid; a list of only invalid
+    ids gives id -1."""
+    V, H = 900, 40
+    W = wl.exact_grid_bf16((V, H), seed, 1)
+    h = wl.exact_grid_bf16((3, H), seed, 2)
+    r = wl.rng(seed, 3)
+    ids = r.integers(-50, V + 50, size=400).astype(np.int32)
+    ids = np.concatenate([ids, ids[:60]])          # repeats
+    r.shuffle(ids)
+    # force an exact tie between two valid ids, the larger one listed first
+    W[611] = W[87]
+    ids = np.concatenate([[611], ids, [87]]).astype(np.int32)
+    qh = np.rint(wl.bf16_bits_to_f32(h) * 16).astype(np.int64)
+    qW = np.rint(wl.bf16_bits_to_f32(W) * 16).astype(np.int64)
+    full = qh @ qW.T
+    d = oracle.draft_gather(h, W, ids)
+    valid = {int(i) for i in ids if 0 <= i < V}
+    for m in range(3):
+        best = max(full[m, i] for i in valid)
+        expect = min(i for i in valid if full[m, i] == best)
+        assert d["id"][m] == expect, (m, d["id"][m], expect)
+        assert d["logit"][m] == np.float32(best / 256.0)
+    # a row made to win by the duplicated pair: the lower id of the two
+    h2 = W[[87]].copy()
+    d2 = oracle.draft_gather(h2, W, ids)
+    s2 = np.rint(wl.bf16_bits_to_f32(h2) * 16).astype(np.int64) @ qW.T
+    best2 = max(s2[0, i] for i in valid)
+    assert d2["id"][0] == min(i for i in valid if s2[0, i] == best2)
+    if s2[0, 87] == best2:
+        assert d2["id"][0] == 87
+    # sorted distinct ids: the same as drafting over the packed table
+    srt = np.array(sorted(valid), np.int32)
+    assert np.array_equal(d["id"], oracle.draft(h, oracle.pack(W, srt), srt)["id"])
+    none = oracle.draft_gather(h, W, np.array([-1, V, V + 7], np.int32))
+    assert np.all(none["id"] == -1) and np.all(np.isnan(none["logit"]))
+
+
 def pin_pack(oracle):
     """Packing copies head rows ids[i]; invalid id lists are refused."""
     V, H = 50, 16
@@ -288,6 +328,7 @@ ALL_PINS = [
     pin_exact_grid,
     pin_tie_break,
     pin_candidate_vs_full,
+    pin_gathered_candidates,
     pin_pack,
     pin_worked_accept,
     pin_accept_invariants,

@@ -176,3 +176,20 @@ def test_one_hip_runtime_per_process():
     assert out.returncode == 0, out.stderr
     n = int(out.stdout.split()[0])
     assert n == 1, out.stdout
+
+
+def test_gather_rejects_bad_arguments():
+    f = mtp.lib.mtp_draft_argmax_gather
+    ok = (FAKE, 1, 64, FAKE, 100, FAKE, 50, FAKE, None, FAKE, 4096, None)
+    assert f(*ok[:5], None, *ok[6:]) == INVALID                 # no id list
+    assert f(*ok[:4], 0, *ok[5:]) == INVALID                    # V < 1
+    assert f(*ok[:4], 2 ** 31, *ok[5:]) == INVALID              # V too large
+    assert f(*ok[:6], 0, *ok[7:]) == INVALID                    # C < 1
+    assert f(None, *ok[1:]) == INVALID
+    assert f(*ok[:3], FAKE_ODD, *ok[4:]) == INVALID             # head alignment
+    assert f(*ok[:5], P(0x10002), *ok[6:]) == INVALID           # ids alignment
+    assert f(*ok[:9], None, *ok[10:]) == mtp.MTP_ERR_WORKSPACE
+    c = mtp.mtp_config()
+    c.path = mtp.MTP_PATH_MFMA
+    g = mtp.lib.mtp_draft_argmax_gather_cfg
+    assert g(*ok, ctypes.byref(c)) == mtp.MTP_ERR_UNSUPPORTED
