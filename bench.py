@@ -54,6 +54,9 @@ def parse_args():
     ap.add_argument("--layout", choices=("auto", "rows", "tiled"), default="auto",
                     help="table layout: row-major, or the 64-row tiled layout of include/mtp.h "
                          "(auto: rows when every call has at most 8 hidden rows)")
+    ap.add_argument("--draft-source", choices=("table", "gather"), default="table",
+                    help="draft calls read a packed candidate table (default), or head rows "
+                         "through a per-call id list (mtp_draft_argmax_gather; row-major only)")
     ap.add_argument("--graph", action="store_true",
                     help="time the steps as replays of a captured HIP graph (mtp_graph_*); "
                          "per-call durations still come from event-bracketed eager launches")
@@ -123,6 +126,11 @@ def main() -> int:
     layout = args.layout
     if layout == "auto":
         layout = "rows" if max(wk.Md, wk.Mv) <= 8 else "tiled"
+    gather = args.draft_source == "gather"
+    if gather and layout != "rows":
+        print("--draft-source gather runs on the row-major head (use --layout rows)",
+              file=sys.stderr)
+        return 2
     head_d = up(head)
     ids_d = up(ids, np.int32)
     tables = []
@@ -152,8 +160,16 @@ def main() -> int:
     v_tok = torch.empty((wk.B, wk.k + 1), dtype=torch.int32, device=dev)
     # drafts with the workload's agreement rate against the target's argmax
     # (taken from one untimed verify call; the timed calls only read them)
+    # gathered drafts: one sorted id list of C candidates per draft call, each
+    # from its own seed, so no call re-reads rows the previous one cached
+    gather_ids = [up(wl.candidate_ids(wk.V, wk.C, wk.seed + 1000 * (c + 1)), np.int32)
+                  for c in range(wk.draft_calls)] if gather else None
+
     def draft_call(c, table):
-        if layout == "rows":
+        if gather:
+            mtp.mtp_draft_argmax_gather(h_d[c], head_d, gather_ids[c], out_ids[c], out_logit[c],
+                                        ws=ws_d)
+        elif layout == "rows":
             mtp.mtp_draft_argmax(h_d[c], table, ids_d, out_ids[c], out_logit[c], ws=ws_d)
         else:
             mtp.mtp_draft_argmax_tiled(h_d[c], table, wk.C, ids_d, out_ids[c], out_logit[c],
@@ -255,7 +271,7 @@ def main() -> int:
     H, C, V, Md, Mv = wk.H, wk.C, wk.V, wk.Md, wk.Mv
     # algorithmic bytes: weight rows + hidden rows + small outputs (winner ids,
     # logits; verify also reads drafts and writes acceptance)
-    draft_bytes = C * H * 2 + Md * H * 2 + Md * (4 + 4 + 4)
+    draft_bytes = C * H * 2 + Md * H * 2 + Md * (4 + 4 + 4) + (C * 4 if gather else 0)
     verify_bytes = V * H * 2 + Mv * H * 2 + wk.B * wk.k * 4 + Mv * (4 + 4 + 4) + wk.B * 4
     d_us = statistics.mean(draft_ms) * 1000.0
     v_us = statistics.mean(verify_ms) * 1000.0
@@ -309,6 +325,7 @@ def main() -> int:
             "H": H, "V": V, "C": C, "B": wk.B, "k": wk.k, "draft_calls": wk.draft_calls,
             "accumulate": "f32", "table_copies": n_tab, "seed": wk.seed, "layout": layout,
             "step": "hip_graph" if graphs else "eager",
+            "draft_source": args.draft_source,
         },
         "calls": {"draft": draft_stats, "verify": verify_stats},
         "context": {
