@@ -13,6 +13,11 @@ the pages each one follows):
   draft(h, table, ids)        argmax over the candidate table, mapped to ids
   draft_gather(h, head, ids)  argmax over head rows named by an id list (any
                               order, repeats; out-of-range ids are no candidates)
+  e4m3_value(codes), e4m3_round(x)
+                              the OCP E4M3 format: exact values, nearest code
+  quantize_fp8(head, ids)     fp8 candidate table: E4M3 rows and per-row
+                              power-of-two scale exponents
+  draft_fp8(h, q, exps, ids)  argmax over the fp8 table, mapped to ids
   verify(hv, head, B, k)      argmax over the full head, shaped [B][k+1]
   accept(draft, target)       greedy acceptance plus bonus token
 """
@@ -59,8 +64,18 @@ class _Lib:
         lib.mtp_oracle_accept.argtypes = [P, P, I64, I64, P, P]
         lib.mtp_oracle_check_ids.argtypes = [P, I64, I64]
         lib.mtp_oracle_pack.argtypes = [P, I64, I64, P, I64, P]
+        lib.mtp_oracle_e4m3_value.argtypes = [ctypes.c_uint8]
+        lib.mtp_oracle_e4m3_value.restype = ctypes.c_double
+        lib.mtp_oracle_e4m3_round.argtypes = [ctypes.c_double]
+        lib.mtp_oracle_e4m3_round.restype = ctypes.c_uint8
+        lib.mtp_oracle_e4m3_round_array.argtypes = [P, I64, P]
+        lib.mtp_oracle_fp8_row_exponent.argtypes = [P, I64, P]
+        lib.mtp_oracle_quantize_fp8.argtypes = [P, I64, I64, P, I64, P, P]
+        lib.mtp_oracle_fp8_argmax.argtypes = [P, I64, P, P, P, I64, I64, P, P, P, P, P]
         for f in ("mtp_oracle_logits", "mtp_oracle_pair_logits", "mtp_oracle_argmax",
-                  "mtp_oracle_accept", "mtp_oracle_check_ids", "mtp_oracle_pack"):
+                  "mtp_oracle_accept", "mtp_oracle_check_ids", "mtp_oracle_pack",
+                  "mtp_oracle_e4m3_round_array", "mtp_oracle_fp8_row_exponent",
+                  "mtp_oracle_quantize_fp8", "mtp_oracle_fp8_argmax"):
             getattr(lib, f).restype = ctypes.c_int
         self.lib = lib
         self.path = path
@@ -233,4 +248,72 @@ def verify(hv: np.ndarray, head: np.ndarray, B: int, k: int,
     out = {key: v.reshape(B, k + 1) for key, v in r.items()}
     if draft_ids is not None:
         out.update(accept(draft_ids, out["id"]))
+    return out
+
+
+# ---- FP8 (E4M3) candidate table ---------------------------------------------
+
+
+def e4m3_value(codes) -> np.ndarray:
+    """Exact values of E4M3 codes (NaN for S.1111.111)."""
+    lib = _load()
+    codes = np.asarray(codes, dtype=np.uint8)
+    table = np.array([lib.mtp_oracle_e4m3_value(c) for c in range(256)], dtype=np.float64)
+    return table[codes]
+
+
+def e4m3_round(x) -> np.ndarray:
+    """Nearest E4M3 code of each value (ties to even, saturating at 448)."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(x.shape, dtype=np.uint8)
+    _check(_load().mtp_oracle_e4m3_round_array(_p(x), x.size, _p(out)), "e4m3_round")
+    return out
+
+
+def fp8_row_exponent(w_row: np.ndarray) -> int:
+    w = _bf16(np.atleast_1d(w_row))
+    e = np.zeros(1, np.int32)
+    _check(_load().mtp_oracle_fp8_row_exponent(_p(w), w.size, _p(e)), "fp8_row_exponent")
+    return int(e[0])
+
+
+def quantize_fp8(head: np.ndarray, ids: Optional[np.ndarray] = None):
+    """The fp8 candidate table of head rows ids (None: every row): E4M3 codes
+    [C][H] and the per-row scale exponents [C] (scale 2^e)."""
+    head = _bf16(head)
+    V, H = head.shape
+    if ids is not None:
+        ids = np.ascontiguousarray(ids, dtype=np.int32)
+    C = V if ids is None else len(ids)
+    q = np.empty((C, H), dtype=np.uint8)
+    exps = np.empty(C, dtype=np.int32)
+    _check(_load().mtp_oracle_quantize_fp8(_p(head), V, H, _p(ids), C, _p(q), _p(exps)),
+           "quantize_fp8")
+    return q, exps
+
+
+def draft_fp8(h: np.ndarray, q: np.ndarray, exps: np.ndarray,
+              ids: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+    """Draft over an fp8 candidate table: first maximum of the fp32-rounded
+    logits 2^e[n] * sum_j h[j] * value(q[n][j]), reported as ids."""
+    x = _bf16(np.atleast_2d(h))
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    exps = np.ascontiguousarray(exps, dtype=np.int32)
+    M, H = x.shape
+    N = q.shape[0]
+    if q.shape[1] != H or exps.shape != (N,):
+        raise ValueError("shapes differ")
+    if ids is not None:
+        ids = np.ascontiguousarray(ids, dtype=np.int32)
+    out = {
+        "id": np.empty(M, np.int32),
+        "logit": np.empty(M, np.float32),
+        "exact": np.empty(M, np.float64),
+        "runner_id": np.empty(M, np.int32),
+        "runner_exact": np.empty(M, np.float64),
+    }
+    _check(_load().mtp_oracle_fp8_argmax(_p(x), M, _p(q), _p(exps), _p(ids), N, H,
+                                         _p(out["id"]), _p(out["logit"]), _p(out["exact"]),
+                                         _p(out["runner_id"]), _p(out["runner_exact"])),
+           "fp8_argmax")
     return out

@@ -32,6 +32,19 @@
  * Threads split the list of table rows only; each logit's arithmetic does
  * not depend on the thread count.
  *
+ * FP8 candidate table (quantised rows; the functions at the end of this
+ * file). The draft may read its candidate rows in an 8-bit format instead of
+ * bfloat16, halving the bytes that dominate the call. (Same section of the
+ * tuning log: the upstream work on this bottleneck stores the candidate rows
+ * in a low-precision float format and reports a further gain over bf16
+ * rows.) Format: OCP 8-bit float E4M3 ("E4M3FN"): sign, 4 exponent bits with
+ * bias 7, 3 mantissa bits; exponent field 0 holds the subnormals m * 2^-9; no
+ * infinities; S.1111.111 is NaN; the largest finite magnitude is 448. Each
+ * row carries one scale 2^e, the smallest power of two with
+ * max_j |w[j]| <= 448 * 2^e (e = 0 for an all-zero row), and stores element
+ * j as the E4M3 value nearest to w[j] * 2^-e (ties to the even code). A
+ * row's logit is 2^e * sum_j x[j] * value(q[j]), summed as above in double.
+ *
  * Build: gcc -O2 -fopenmp -ffp-contract=off -shared -fPIC (no fast-math).
  */
 #include <float.h>
@@ -107,6 +120,33 @@ int mtp_oracle_pair_logits(const uint16_t *x, const uint16_t *w, int64_t H, cons
  *                            (first such row), used to find near-ties; -1 and
  *                            -inf if N == 1.
  */
+/* The argmax decision over one query row's N double logits z: the first
+ * maximum of the fp32-rounded logits, and the double runner-up among the
+ * other rows (see mtp_oracle_argmax). */
+static int decide_row(const double *z, int64_t N, const int32_t *ids, int32_t *top_id,
+                      float *top_logit, double *top_exact, int32_t *runner_id,
+                      double *runner_exact) {
+  int64_t best = -1;
+  float best_f = 0.0f;
+  for (int64_t n = 0; n < N; ++n) {
+    if (!isfinite(z[n])) return ORC_NOT_FINITE;
+    float f = (float)z[n];
+    if (best < 0 || f > best_f) { best = n; best_f = f; }
+  }
+  int64_t second = -1;
+  double second_z = -INFINITY;
+  for (int64_t n = 0; n < N; ++n) {
+    if (n == best) continue;
+    if (second < 0 || z[n] > second_z) { second = n; second_z = z[n]; }
+  }
+  *top_id = ids ? ids[best] : (int32_t)best;
+  *top_logit = best_f;
+  *top_exact = z[best];
+  *runner_id = second < 0 ? -1 : (ids ? ids[second] : (int32_t)second);
+  *runner_exact = second_z;
+  return ORC_OK;
+}
+
 int mtp_oracle_argmax(const uint16_t *x, int64_t M, const uint16_t *w, const int32_t *ids,
                       int64_t N, int64_t H, int32_t *top_id, float *top_logit,
                       double *top_exact, int32_t *runner_id, double *runner_exact) {
@@ -118,27 +158,8 @@ int mtp_oracle_argmax(const uint16_t *x, int64_t M, const uint16_t *w, const int
   int rc = ORC_OK;
   for (int64_t m = 0; m < M && rc == ORC_OK; ++m) {
     mtp_oracle_logits(x + m * H, 1, w, N, H, z);
-    /* fp32 decision: first maximum of the rounded logits. */
-    int64_t best = -1;
-    float best_f = 0.0f;
-    for (int64_t n = 0; n < N; ++n) {
-      if (!isfinite(z[n])) { rc = ORC_NOT_FINITE; break; }
-      float f = (float)z[n];
-      if (best < 0 || f > best_f) { best = n; best_f = f; }
-    }
-    if (rc != ORC_OK) break;
-    /* runner-up in double over the other rows */
-    int64_t second = -1;
-    double second_z = -INFINITY;
-    for (int64_t n = 0; n < N; ++n) {
-      if (n == best) continue;
-      if (second < 0 || z[n] > second_z) { second = n; second_z = z[n]; }
-    }
-    top_id[m] = ids ? ids[best] : (int32_t)best;
-    top_logit[m] = best_f;
-    top_exact[m] = z[best];
-    runner_id[m] = second < 0 ? -1 : (ids ? ids[second] : (int32_t)second);
-    runner_exact[m] = second_z;
+    rc = decide_row(z, N, ids, top_id + m, top_logit + m, top_exact + m, runner_id + m,
+                    runner_exact + m);
   }
   free(z);
   return rc;
@@ -184,4 +205,111 @@ int mtp_oracle_pack(const uint16_t *head, int64_t V, int64_t H, const int32_t *i
   for (int64_t i = 0; i < C; ++i)
     memcpy(table + i * H, head + (int64_t)ids[i] * H, (size_t)H * sizeof(uint16_t));
   return ORC_OK;
+}
+
+/* ---- FP8 (E4M3) candidate table ---------------------------------------- */
+
+/* The value of an E4M3 code (NaN for S.1111.111). */
+double mtp_oracle_e4m3_value(uint8_t code) {
+  const int e = (code >> 3) & 15;
+  const int m = code & 7;
+  if (e == 15 && m == 7) return NAN;
+  /* subnormal: m * 2^-9; normal: (1 + m/8) * 2^(e-7) = (8 + m) * 2^(e-10) */
+  const double v = e == 0 ? ldexp((double)m, -9) : ldexp((double)(8 + m), e - 10);
+  return (code & 0x80) ? -v : v;
+}
+
+/* The E4M3 code nearest to x (ties to the even code, i.e. mantissa bit 0
+ * clear); magnitudes beyond 448 saturate to +-448; NaN gives 0x7F. */
+uint8_t mtp_oracle_e4m3_round(double x) {
+  if (isnan(x)) return 0x7F;
+  const uint8_t s = signbit(x) ? 0x80 : 0x00;
+  const double a = fabs(x);
+  if (a >= 448.0) return s | 0x7E;
+  if (a < ldexp(1.0, -6)) {
+    /* subnormal spacing 2^-9: round a / 2^-9 to an integer, ties to even;
+       8 is the smallest normal, whose code is also 8 */
+    const double r = nearbyint(ldexp(a, 9));
+    return s | (uint8_t)r;
+  }
+  int E;
+  frexp(a, &E);                    /* a = f * 2^E, f in [0.5, 1) */
+  int ue = E - 1;                  /* a in [2^ue, 2^(ue+1)) */
+  double r = nearbyint(ldexp(a, 3 - ue));  /* 8..16: 1.mmm in eighths */
+  if (r == 16.0) { r = 8.0; ue += 1; }
+  if (ue > 8 || (ue == 8 && r > 14.0)) return s | 0x7E;
+  return s | (uint8_t)(((ue + 7) << 3) | ((int)r - 8));
+}
+
+int mtp_oracle_e4m3_round_array(const double *x, int64_t n, uint8_t *out) {
+  if (!x || !out || n < 0) return ORC_BAD_ARG;
+  for (int64_t i = 0; i < n; ++i) out[i] = mtp_oracle_e4m3_round(x[i]);
+  return ORC_OK;
+}
+
+/* The row's scale exponent: the smallest e with max|w| <= 448 * 2^e (0 for
+ * an all-zero row). */
+int mtp_oracle_fp8_row_exponent(const uint16_t *w, int64_t H, int32_t *e_out) {
+  if (!w || !e_out || H <= 0) return ORC_BAD_ARG;
+  double amax = 0.0;
+  for (int64_t j = 0; j < H; ++j) {
+    const double v = fabs(bf16_to_double(w[j]));
+    if (!isfinite(v)) return ORC_NOT_FINITE;
+    if (v > amax) amax = v;
+  }
+  if (amax == 0.0) { *e_out = 0; return ORC_OK; }
+  int e = ilogb(amax) - 8;
+  while (ldexp(448.0, e) < amax) ++e;
+  while (ldexp(448.0, e - 1) >= amax) --e;
+  *e_out = e;
+  return ORC_OK;
+}
+
+/* Quantise the candidate rows head[ids[i]] (ids NULL: rows 0..C-1):
+ * q[i][j] = E4M3(head[ids[i]][j] * 2^-e[i]), exps[i] = e[i]. */
+int mtp_oracle_quantize_fp8(const uint16_t *head, int64_t V, int64_t H, const int32_t *ids,
+                            int64_t C, uint8_t *q, int32_t *exps) {
+  if (!head || !q || !exps || V <= 0 || H <= 0 || C <= 0) return ORC_BAD_ARG;
+  if (ids && mtp_oracle_check_ids(ids, C, V) != ORC_OK) return ORC_BAD_IDS;
+  if (!ids && C > V) return ORC_BAD_ARG;
+  int rc = ORC_OK;
+  for (int64_t i = 0; i < C; ++i) {
+    const uint16_t *w = head + (int64_t)(ids ? ids[i] : i) * H;
+    int32_t e = 0;
+    const int r = mtp_oracle_fp8_row_exponent(w, H, &e);
+    if (r != ORC_OK) { rc = r; break; }
+    exps[i] = e;
+    for (int64_t j = 0; j < H; ++j) q[i * H + j] = mtp_oracle_e4m3_round(ldexp(bf16_to_double(w[j]), -e));
+  }
+  return rc;
+}
+
+/* One fp8 row's logit: 2^e * sum over j of x[j] * value(q[j]), in order,
+ * in double (each product is exact). */
+static double dot_fp8(const uint16_t *x, const uint8_t *q, int32_t e, int64_t H) {
+  double s = 0.0;
+  for (int64_t j = 0; j < H; ++j) s += bf16_to_double(x[j]) * mtp_oracle_e4m3_value(q[j]);
+  return ldexp(s, e);
+}
+
+/* Argmax of every query row over an fp8 table of N rows (as
+ * mtp_oracle_argmax, with each row's logit from dot_fp8). */
+int mtp_oracle_fp8_argmax(const uint16_t *x, int64_t M, const uint8_t *q, const int32_t *exps,
+                          const int32_t *ids, int64_t N, int64_t H, int32_t *top_id,
+                          float *top_logit, double *top_exact, int32_t *runner_id,
+                          double *runner_exact) {
+  if (!x || !q || !exps || !top_id || !top_logit || !top_exact || !runner_id || !runner_exact ||
+      M < 0 || N <= 0 || H <= 0)
+    return ORC_BAD_ARG;
+  double *z = (double *)malloc((size_t)N * sizeof(double));
+  if (!z) return ORC_NO_MEMORY;
+  int rc = ORC_OK;
+  for (int64_t m = 0; m < M && rc == ORC_OK; ++m) {
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) z[n] = dot_fp8(x + m * H, q + n * H, exps[n], H);
+    rc = decide_row(z, N, ids, top_id + m, top_logit + m, top_exact + m, runner_id + m,
+                    runner_exact + m);
+  }
+  free(z);
+  return rc;
 }

@@ -222,6 +222,119 @@ def pin_gathered_candidates(oracle, seed=29):
     assert np.all(none["id"] == -1) and np.all(np.isnan(none["logit"]))
 
 
+def _e4m3_table():
+    """Values of the 256 E4M3 codes as torch's float8_e4m3fn decodes them."""
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    return torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def _nearest_code_brute(x: float, table: np.ndarray) -> int:
+    """Nearest finite E4M3 code by exhaustive search; ties to the code with
+    mantissa bit 0 clear; beyond the largest magnitude, saturate."""
+    finite = [c for c in range(256) if np.isfinite(table[c])]
+    if abs(x) >= 448.0:
+        return 0xFE if x < 0 else 0x7E
+    best = None
+    for c in finite:
+        if (table[c] == 0.0) and (np.signbit(table[c]) != np.signbit(x)):
+            continue                                   # keep the sign of zero
+        d = abs(table[c] - x)
+        key = (d, c & 1)
+        if best is None or key < best[0]:
+            best = (key, c)
+    return best[1]
+
+
+def pin_e4m3_format(oracle, seed=41):
+    """The E4M3 decode equals torch's float8_e4m3fn for all 256 codes; the
+    rounding equals torch's cast for in-range values and an exhaustive
+    nearest-even search everywhere (including saturation at 448)."""
+    import torch
+    table = _e4m3_table()
+    ours = oracle.e4m3_value(np.arange(256, dtype=np.uint8))
+    assert np.array_equal(np.isnan(ours), np.isnan(table))
+    fin = ~np.isnan(table)
+    assert np.array_equal(ours[fin], table[fin])
+    assert np.array_equal(np.signbit(ours[fin]), np.signbit(table[fin]))
+    r = wl.rng(seed, 1)
+    mags = np.concatenate([
+        r.uniform(0, 448, 3000), np.exp2(r.uniform(-12, 8.8, 3000)), r.uniform(0, 2 ** -6, 500)])
+    # exact midpoints between neighbouring finite codes, and the codes themselves
+    pos = np.sort(table[(table >= 0) & np.isfinite(table)])
+    mids = (pos[1:] + pos[:-1]) / 2
+    x = np.concatenate([mags, pos, mids])
+    x = np.concatenate([x, -x]).astype(np.float32).astype(np.float64)
+    got = oracle.e4m3_round(x)
+    want_t = torch.from_numpy(x.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8)
+    assert np.array_equal(got, want_t.numpy()), "rounding differs from torch's cast"
+    extra = np.array([448.0, 460.0, 464.0, 1e6, -500.0, 2 ** -10, -2 ** -10, 3 * 2 ** -10])
+    for v in np.concatenate([x[::37], extra]):
+        assert int(oracle.e4m3_round([v])[0]) == _nearest_code_brute(float(v), table), v
+
+
+def pin_fp8_quantize(oracle, seed=43):
+    """Per-row scale 2^e is the smallest power of two with max|w| <= 448 * 2^e;
+    every element is the nearest E4M3 code of w * 2^-e (error at most half a
+    step of its binade); values already on the scaled grid round-trip; an
+    all-zero row has e = 0 and zero codes."""
+    V, H = 40, 96
+    W = wl.normal_bf16_rows(V, H, 0.02, seed, 1)
+    W[3] = 0
+    W[5] = wl.f32_to_bf16_bits(np.full(H, 448.0, np.float32))
+    q, e = oracle.quantize_fp8(W)
+    wf = wl.bf16_bits_to_f32(W).astype(np.float64)
+    table = _e4m3_table()
+    for i in range(V):
+        amax = np.abs(wf[i]).max()
+        if amax == 0:
+            assert e[i] == 0 and not q[i].any()
+            continue
+        assert amax <= 448.0 * 2.0 ** int(e[i]) and amax > 448.0 * 2.0 ** (int(e[i]) - 1)
+        deq = table[q[i]] * 2.0 ** int(e[i])
+        y = wf[i] * 2.0 ** -int(e[i])
+        step = np.where(np.abs(y) < 2 ** -6, 2.0 ** -9, 2.0 ** (np.floor(np.log2(np.maximum(np.abs(y), 2 ** -6))) - 3))
+        assert np.all(np.abs(deq - wf[i]) <= 0.5 * step * 2.0 ** int(e[i]) * (1 + 1e-12))
+    assert e[5] == 0 and np.all(table[q[5]] == 448.0)
+    # rows already on the scaled E4M3 grid come back exactly
+    codes = wl.rng(seed, 2).integers(0, 126, size=(4, H)).astype(np.uint8)
+    codes[:, 0] = 0x7E                                  # pins the scale to 2^-3
+    vals = (table[codes] * 2.0 ** -3).astype(np.float32)
+    Wg = wl.f32_to_bf16_bits(vals)
+    assert np.array_equal(wl.bf16_bits_to_f32(Wg), vals)
+    qg, eg = oracle.quantize_fp8(Wg)
+    assert np.all(eg == -3) and np.array_equal(qg, codes)
+    # with ids: the rows of the listed head rows
+    ids = np.array([1, 3, 7, 30], np.int32)
+    qi, ei = oracle.quantize_fp8(W, ids)
+    assert np.array_equal(qi, q[ids]) and np.array_equal(ei, e[ids])
+
+
+def pin_fp8_draft(oracle, seed=47):
+    """Head rows of multiples of 1/8 up to 2 quantise exactly (scale 2^-7),
+    so with hidden rows on the q/16 grid every fp8 logit is an exact integer
+    sum over 128; the pick is the first maximum of those integers and equals
+    the bf16 draft over the same rows."""
+    V, H, C = 700, 64, 300
+    r = wl.rng(seed, 1)
+    kq = r.integers(-16, 17, size=(V, H))
+    kq[:, 0] = 16                                       # max|w| = 2 in every row
+    W = wl.f32_to_bf16_bits((kq / 8.0).astype(np.float32))
+    h = wl.exact_grid_bf16((3, H), seed, 2)
+    ids = wl.candidate_ids(V, C, seed)
+    q, e = oracle.quantize_fp8(W, ids)
+    assert np.all(e == -7)
+    d8 = oracle.draft_fp8(h, q, e, ids)
+    qh = np.rint(wl.bf16_bits_to_f32(h) * 16).astype(np.int64)
+    num = qh @ kq[ids].T                                 # logits * 128
+    for m in range(3):
+        row = [int(v) for v in num[m]]
+        best = _first_max(row)
+        assert d8["id"][m] == ids[best]
+        assert d8["logit"][m] == np.float32(row[best] / 128.0)
+    assert np.array_equal(d8["id"], oracle.draft(h, oracle.pack(W, ids), ids)["id"])
+
+
 def pin_pack(oracle):
     """Packing copies head rows ids[i]; invalid id lists are refused."""
     V, H = 50, 16
@@ -329,6 +442,9 @@ ALL_PINS = [
     pin_tie_break,
     pin_candidate_vs_full,
     pin_gathered_candidates,
+    pin_e4m3_format,
+    pin_fp8_quantize,
+    pin_fp8_draft,
     pin_pack,
     pin_worked_accept,
     pin_accept_invariants,

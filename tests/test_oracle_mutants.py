@@ -10,9 +10,9 @@ from tests import oracle_pins
 
 # (name, text in mtp_oracle.c, replacement)
 MUTATIONS = [
-    ("dropped_last_term", "for (int64_t j = 0; j < H; ++j) s +=", "for (int64_t j = 0; j + 1 < H; ++j) s +="),
+    ("dropped_last_term", "for (int64_t j = 0; j < H; ++j) s += bf16_to_double(x[j]) * bf16_to_double(w[j]);", "for (int64_t j = 0; j + 1 < H; ++j) s += bf16_to_double(x[j]) * bf16_to_double(w[j]);"),
     ("wrong_bf16_shift", "(uint32_t)b << 16", "(uint32_t)b << 15"),
-    ("reversed_operand_index", "bf16_to_double(w[j])", "bf16_to_double(w[H - 1 - j])"),
+    ("reversed_operand_index", "bf16_to_double(x[j]) * bf16_to_double(w[j])", "bf16_to_double(x[j]) * bf16_to_double(w[H - 1 - j])"),
     ("highest_index_wins_ties", "if (best < 0 || f > best_f)", "if (best < 0 || f >= best_f)"),
     ("argmin_instead_of_argmax", "if (best < 0 || f > best_f)", "if (best < 0 || f < best_f)"),
     ("bonus_token_dropped", "p <= n ? target", "p < n ? target"),
@@ -20,9 +20,16 @@ MUTATIONS = [
     ("pack_ignores_ids", "head + (int64_t)ids[i] * H", "head + i * H"),
     ("runner_up_may_be_top", "if (n == best) continue;", ""),
     ("ids_may_repeat", "ids[i] <= ids[i - 1]", "ids[i] < ids[i - 1]"),
-    ("id_map_dropped", "top_id[m] = ids ? ids[best] : (int32_t)best;", "top_id[m] = (int32_t)best;"),
+    ("id_map_dropped", "*top_id = ids ? ids[best] : (int32_t)best;", "*top_id = (int32_t)best;"),
     ("pair_rows_swapped", "x + rows[i] * H, w + cols[i] * H", "x + cols[i] * H, w + rows[i] * H"),
-    ("logit_not_rounded_from_pick", "top_logit[m] = best_f;", "top_logit[m] = (float)z[0];"),
+    ("logit_not_rounded_from_pick", "*top_logit = best_f;", "*top_logit = (float)z[0];"),
+    ("e4m3_bias_8", "ldexp((double)(8 + m), e - 10)", "ldexp((double)(8 + m), e - 11)"),
+    ("e4m3_ties_away_from_zero", "nearbyint(ldexp(a, 3 - ue))", "round(ldexp(a, 3 - ue))"),
+    ("e4m3_subnormal_spacing", "nearbyint(ldexp(a, 9))", "nearbyint(ldexp(a, 8))"),
+    ("e4m3_sign_lost", "const uint8_t s = signbit(x) ? 0x80 : 0x00;", "const uint8_t s = 0x00;"),
+    ("fp8_scale_search_dropped", "while (ldexp(448.0, e) < amax) ++e;\n  while (ldexp(448.0, e - 1) >= amax) --e;", ""),
+    ("fp8_scale_ignored", "return ldexp(s, e);", "return s;"),
+    ("fp8_code_ignores_scale", "mtp_oracle_e4m3_round(ldexp(bf16_to_double(w[j]), -e))", "mtp_oracle_e4m3_round(bf16_to_double(w[j]))"),
 ]
 
 
