@@ -267,6 +267,58 @@ mtp_status mtp_draft_argmax_gather_cfg(const mtp_bf16 *hidden, int M, int H,
                                        const mtp_config *cfg);
 
 /*
+ * FP8 candidate table.
+ *
+ * The draft reads its candidate rows as 8-bit floats instead of bf16: half
+ * the bytes of the call that dominates the draft path.
+ * [Qwen3.8 Flash dual-Spark tuning log, section "read one fewer big table":
+ * the upstream work on this bottleneck stores the candidate rows in a
+ * low-precision float format and reports a further gain over bf16 rows.]
+ *
+ * Format: OCP 8-bit float E4M3 (sign, 4 exponent bits with bias 7, 3 mantissa
+ * bits; subnormals m * 2^-9; no infinities; S.1111.111 is NaN; largest
+ * magnitude 448). Row i has one scale s_i = 2^e_i, the smallest power of two
+ * with max_j |w_i[j]| <= 448 * s_i (s_i = 1 for an all-zero row), and stores
+ * q_i[j] = the E4M3 code nearest to w_i[j] / s_i, ties to the even code.
+ * The draft's logit of row i is s_i * sum_j hidden[j] * value(q_i[j]),
+ * accumulated in fp32; its argmax follows mtp_draft_argmax (lowest id on
+ * ties). This is an approximation of the bf16 draft: each weight carries a
+ * relative error up to 2^-4 (the verify still scores the full bf16 head).
+ *
+ * mtp_fp8_table_bytes(C, H) = C * H (the codes; the scales are C floats);
+ * 0 when out of range. H must be a multiple of 16 (16-byte code chunks).
+ */
+size_t mtp_fp8_table_bytes(int64_t C, int H);
+
+/* Quantise the candidate rows (one-time set-up): table_q[i][:] and
+ * scales[i] from head[ids[i]][:] as above (ids NULL: head rows 0..C-1,
+ * C <= V). head device [V][H] bf16, 16-byte aligned; ids device int32 [C]
+ * (check with mtp_validate_ids; an out-of-range id gives a zero row with
+ * scale 1); table_q device [C][H] bytes, 16-byte aligned, written; scales
+ * device float [C], written. The codes are exactly the format's rounding of
+ * the bf16 values (bit-identical to any correct implementation). */
+mtp_status mtp_pack_candidates_fp8(const mtp_bf16 *head, int64_t V, int H, const int32_t *ids,
+                                   int64_t C, uint8_t *table_q, float *scales,
+                                   hipStream_t stream);
+
+/* Draft over an fp8 candidate table: out_ids[m] = ids[argmax_i logit_i]
+ * (ids NULL: i). hidden device [M][H] bf16; table_q, scales as written by
+ * mtp_pack_candidates_fp8; out_ids / out_logit / ws as mtp_draft_argmax
+ * (workspace size mtp_draft_workspace_bytes(M, C, H)). Runs on the
+ * vector-ALU kernel: 1, 2, 4 or 8 hidden rows per pass (at most 16 / NCL,
+ * NCL = ceil(H / 1024)); more rows take further passes over the table.
+ * cfg->path MTP_PATH_MFMA gives MTP_ERR_UNSUPPORTED. */
+mtp_status mtp_draft_argmax_fp8(const mtp_bf16 *hidden, int M, int H, const uint8_t *table_q,
+                                const float *scales, const int32_t *ids, int64_t C,
+                                int32_t *out_ids, float *out_logit, void *ws, size_t ws_bytes,
+                                hipStream_t stream);
+mtp_status mtp_draft_argmax_fp8_cfg(const mtp_bf16 *hidden, int M, int H, const uint8_t *table_q,
+                                    const float *scales, const int32_t *ids, int64_t C,
+                                    int32_t *out_ids, float *out_logit, void *ws,
+                                    size_t ws_bytes, hipStream_t stream,
+                                    const mtp_config *cfg);
+
+/*
  * Graph-captured MTP step.
  *
  * Records the library calls a caller makes on `stream` between

@@ -1,0 +1,345 @@
+// FP8 (E4M3) candidate table: quantising pack and the draft GEMV + argmax
+// over it (mtp.h, "FP8 candidate table").
+//
+// Format: OCP 8-bit float E4M3 (sign, 4 exponent bits with bias 7, 3
+// mantissa bits, subnormals m * 2^-9, no infinities, S.1111.111 NaN, largest
+// magnitude 448). Each row has one scale 2^e, the smallest power of two with
+// max|w| <= 448 * 2^e (e = 0 for an all-zero row); element j is the E4M3
+// code nearest to w[j] * 2^-e, ties to the even code. The pack does this in
+// double precision, where every step is exact except the one rounding, so the
+// codes are the format's definition applied to the bf16 values.
+//
+// The draft kernel streams 16 codes (16 bytes) per lane and load, converts
+// them to bf16 pairs with v_cvt_scalef32_pk_bf16_fp8 (exact: every E4M3
+// value is a bf16 value) and accumulates with v_dot2c_f32_bf16 against the
+// hidden row, in column order; the wave sum is multiplied by the row's scale
+// (a power of two: exact). Rows per wave, prefetch, argmax and the
+// cross-workgroup finish follow the bf16 vector-ALU kernel.
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace mtp {
+
+typedef __bf16 bf16x2_fp8_t __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4_fp8_t __attribute__((ext_vector_type(4)));
+
+// ---- quantising pack ------------------------------------------------------
+
+// Nearest E4M3 code of x (ties to even, magnitudes >= 448 saturate to 448,
+// NaN gives 0x7F).
+__device__ uint8_t e4m3_code(double x) {
+  if (isnan(x)) return 0x7F;
+  const uint8_t sign = signbit(x) ? 0x80 : 0x00;
+  const double a = fabs(x);
+  if (a >= 448.0) return sign | 0x7E;
+  if (a < 0.015625) {  // below 2^-6: subnormal steps of 2^-9
+    return sign | (uint8_t)rint(ldexp(a, 9));
+  }
+  int E;
+  frexp(a, &E);  // a = f * 2^E, f in [0.5, 1)
+  int ue = E - 1;
+  double r = rint(ldexp(a, 3 - ue));  // 8 .. 16 eighths
+  if (r == 16.0) {
+    r = 8.0;
+    ue += 1;
+  }
+  if (ue > 8 || (ue == 8 && r > 14.0)) return sign | 0x7E;
+  return sign | (uint8_t)(((ue + 7) << 3) | ((int)r - 8));
+}
+
+__device__ __forceinline__ double bf16_value(uint32_t bits16) {
+  return (double)__uint_as_float(bits16 << 16);
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const uint32_t o = (uint32_t)__shfl_xor((int)v, off, kWave);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+// One wave per candidate row (grid-strided). ids NULL: row i is head row i.
+// A row whose id is outside [0, V) is written as zero codes with scale 1.
+__global__ void __launch_bounds__(256)
+    pack_fp8(const uint4 *__restrict__ head, int64_t V, int H, const int32_t *__restrict__ ids,
+             int64_t C, uint2 *__restrict__ q, float *__restrict__ scales) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t waves = (int64_t)gridDim.x * (blockDim.x / kWave);
+  const int nch = H / 8;  // 16-byte chunks of 8 bf16
+  for (int64_t row = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave; row < C;
+       row += waves) {
+    const int64_t id = ids ? (int64_t)ids[row] : row;
+    const bool valid = id >= 0 && id < V;
+    const uint4 *src = head + (valid ? id : 0) * nch;
+    uint32_t mx = 0;
+    for (int c = lane; c < nch; c += kWave) {
+      const uint4 v = src[c];
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t lo = w[k] & 0x7FFFu, hi = (w[k] >> 16) & 0x7FFFu;
+        mx = lo > mx ? lo : mx;
+        mx = hi > mx ? hi : mx;
+      }
+    }
+    mx = valid ? wave_max_u32(mx) : 0u;
+    int e = 0;
+    // (a row holding Inf or NaN is outside the contract: it keeps e = 0, so
+    // the search below always ends)
+    if (mx != 0 && mx < 0x7F80u) {
+      const double amax = bf16_value(mx);
+      e = ilogb(amax) - 8;
+      while (ldexp(448.0, e) < amax) ++e;
+      while (ldexp(448.0, e - 1) >= amax) --e;
+    }
+    uint2 *dst = q + row * (int64_t)(H / 8);
+    for (int c = lane; c < nch; c += kWave) {
+      uint32_t b[2] = {0u, 0u};
+      if (valid) {
+        const uint4 v = src[c];
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const uint32_t bits = (k & 1) ? (w[k >> 1] >> 16) : (w[k >> 1] & 0xFFFFu);
+          const uint32_t code = e4m3_code(ldexp(bf16_value(bits), -e));
+          b[k >> 2] |= code << (8 * (k & 3));
+        }
+      }
+      dst[c] = make_uint2(b[0], b[1]);
+    }
+    if (lane == 0) scales[row] = valid ? (float)ldexp(1.0, e) : 1.0f;
+  }
+}
+
+hipError_t launch_pack_fp8(const void *head, int64_t V, int H, const int32_t *ids, int64_t C,
+                           void *q, float *scales, int num_cus, hipStream_t stream) {
+  const int64_t waves_per_block = 4;
+  int64_t blocks = (C + waves_per_block - 1) / waves_per_block;
+  const int64_t cap = (int64_t)num_cus * 8;
+  if (blocks > cap) blocks = cap;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(pack_fp8, dim3((unsigned)blocks), dim3(256), 0, stream, (const uint4 *)head,
+                     V, H, ids, C, (uint2 *)q, scales);
+  return hipGetLastError();
+}
+
+// ---- draft GEMV + argmax ---------------------------------------------------
+
+constexpr int kFp8Threads = 256;
+constexpr int kFp8Waves = kFp8Threads / kWave;
+
+__device__ __forceinline__ uint4 load_stream_fp8(const uint4 *p) {
+  const u32x4_fp8_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_fp8_t *>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// acc + sum over 16 columns of value(code) * hidden: codes c (16 bytes),
+// hidden h0 (columns 0..7), h1 (columns 8..15), in column order.
+__device__ __forceinline__ float dot16_fp8(const uint4 &c, const uint4 &h0, const uint4 &h1,
+                                           float acc) {
+  const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
+  const uint32_t hw[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const bf16x2_fp8_t lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)cw[k], 1.0f, false);
+    const bf16x2_fp8_t hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)cw[k], 1.0f, true);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(lo, __builtin_bit_cast(bf16x2_fp8_t, hw[2 * k]), acc,
+                                          false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(hi, __builtin_bit_cast(bf16x2_fp8_t, hw[2 * k + 1]),
+                                          acc, false);
+  }
+  return acc;
+}
+
+// MR hidden rows, NCL code chunks (16 columns) per lane and row, RB table
+// rows per wave iteration, next iteration's rows in flight; EXACT: H is
+// NCL * 1024 (no column predication).
+template <int MR, int NCL, int RB, bool EXACT>
+__global__ void __launch_bounds__(kFp8Threads)
+    gemv_argmax_fp8(const uint4 *__restrict__ X, const uint4 *__restrict__ Q,
+                    const float *__restrict__ scales, int M, int64_t N, int ncq,
+                    RowSink sink) {
+  __shared__ float s_val[kFp8Waves][MR];
+  __shared__ int64_t s_row[kFp8Waves][MR];
+  __shared__ float f_val[MR];
+  __shared__ int64_t f_row[MR];
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int m0 = blockIdx.y * MR;
+  const int nch = 2 * ncq;  // hidden row: 16-byte chunks of 8 bf16
+
+  uint4 h[MR][NCL][2];
+#pragma unroll
+  for (int r = 0; r < MR; ++r) {
+#pragma unroll
+    for (int c = 0; c < NCL; ++c) {
+      const int col = lane + kWave * c;
+      const bool ok = m0 + r < M && (EXACT || col < ncq);
+      const uint4 *xr = X + (int64_t)(m0 + r) * nch + 2 * col;
+      h[r][c][0] = ok ? xr[0] : make_uint4(0u, 0u, 0u, 0u);
+      h[r][c][1] = ok ? xr[1] : make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+
+  float bv[MR];
+  int64_t bi[MR];
+#pragma unroll
+  for (int r = 0; r < MR; ++r) {
+    bv[r] = 0.0f;
+    bi[r] = -1;
+  }
+
+  auto load = [&](uint4(&w)[RB][NCL], int64_t r0) {
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+      // rows past N read row 0 (never reported)
+      const int64_t row = r0 + i < N ? r0 + i : 0;
+      const uint4 *p = Q + row * ncq + lane;
+#pragma unroll
+      for (int c = 0; c < NCL; ++c)
+        w[i][c] = (EXACT || lane + kWave * c < ncq) ? load_stream_fp8(p + kWave * c)
+                                                    : make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+
+  const int64_t stride = (int64_t)gridDim.x * kFp8Waves * RB;
+  int64_t r0 = ((int64_t)blockIdx.x * kFp8Waves + __builtin_amdgcn_readfirstlane(wave)) * RB;
+  uint4 nxt[RB][NCL];
+  if (r0 < N) load(nxt, r0);
+  for (; r0 < N; r0 += stride) {
+    uint4 w[RB][NCL];
+#pragma unroll
+    for (int i = 0; i < RB; ++i)
+#pragma unroll
+      for (int c = 0; c < NCL; ++c) w[i][c] = nxt[i][c];
+    if (r0 + stride < N) load(nxt, r0 + stride);
+    float acc[MR][RB];
+#pragma unroll
+    for (int r = 0; r < MR; ++r)
+#pragma unroll
+      for (int i = 0; i < RB; ++i) acc[r][i] = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NCL; ++c)
+#pragma unroll
+      for (int i = 0; i < RB; ++i)
+#pragma unroll
+        for (int r = 0; r < MR; ++r)
+          acc[r][i] = dot16_fp8(w[i][c], h[r][c][0], h[r][c][1], acc[r][i]);
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+      const float scale = r0 + i < N ? scales[r0 + i] : 0.0f;
+#pragma unroll
+      for (int r = 0; r < MR; ++r) {
+        const float s = wave_sum(acc[r][i]) * scale;
+        if (r0 + i < N && better(s, r0 + i, bv[r], bi[r])) {
+          bv[r] = s;
+          bi[r] = r0 + i;
+        }
+      }
+    }
+  }
+
+  if (lane == 0) {
+#pragma unroll
+    for (int r = 0; r < MR; ++r) {
+      s_val[wave][r] = bv[r];
+      s_row[wave][r] = bi[r];
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < MR) {
+    const int r = threadIdx.x;
+    float v = s_val[0][r];
+    int64_t ix = s_row[0][r];
+    for (int q = 1; q < kFp8Waves; ++q) {
+      if (s_row[q][r] >= 0 && better(s_val[q][r], s_row[q][r], v, ix)) {
+        v = s_val[q][r];
+        ix = s_row[q][r];
+      }
+    }
+    f_val[r] = v;
+    f_row[r] = ix;
+  }
+  __syncthreads();
+  finish_rows(sink, f_val, f_row, m0, min(MR, M - m0));
+}
+
+// Rows per iteration: about 8 KiB of codes in flight per wave.
+template <int NCL>
+constexpr int fp8_rb() {
+  return NCL >= 8 ? 1 : (8 / NCL > 4 ? 4 : 8 / NCL);
+}
+
+template <int MR, int NCL>
+static hipError_t launch_fp8_cfg(const Fp8Launch &L) {
+  // the hidden slices take 8 registers per (row, chunk): MR * NCL <= 16
+  if constexpr (MR * NCL > 16) {
+    return hipErrorInvalidValue;
+  } else {
+  constexpr int RB = fp8_rb<NCL>();
+  const int64_t row_blocks = (L.N + RB - 1) / RB;
+  const int64_t want = (row_blocks + kFp8Waves - 1) / kFp8Waves;
+  const int gx = (int)(want < L.max_blocks_x ? want : L.max_blocks_x);
+  const int gy = (L.M + MR - 1) / MR;
+  if (L.ncq == NCL * kWave)
+    hipLaunchKernelGGL((gemv_argmax_fp8<MR, NCL, RB, true>), dim3(gx, gy), dim3(kFp8Threads), 0,
+                       L.stream, (const uint4 *)L.X, (const uint4 *)L.Q, L.scales, L.M, L.N,
+                       L.ncq, L.sink);
+  else
+    hipLaunchKernelGGL((gemv_argmax_fp8<MR, NCL, RB, false>), dim3(gx, gy), dim3(kFp8Threads),
+                       0, L.stream, (const uint4 *)L.X, (const uint4 *)L.Q, L.scales, L.M, L.N,
+                       L.ncq, L.sink);
+  return hipGetLastError();
+  }
+}
+
+template <int MR>
+static hipError_t launch_fp8_mr(const Fp8Launch &L, int ncl) {
+  switch (ncl) {
+    case 1: return launch_fp8_cfg<MR, 1>(L);
+    case 2: return launch_fp8_cfg<MR, 2>(L);
+    case 3: return launch_fp8_cfg<MR, 3>(L);
+    case 4: return launch_fp8_cfg<MR, 4>(L);
+    case 5: return launch_fp8_cfg<MR, 5>(L);
+    case 6: return launch_fp8_cfg<MR, 6>(L);
+    case 8: return launch_fp8_cfg<MR, 8>(L);
+    case 10: return launch_fp8_cfg<MR, 10>(L);
+    case 12: return launch_fp8_cfg<MR, 12>(L);
+    case 16: return launch_fp8_cfg<MR, 16>(L);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// Code chunks per lane that have an instantiation (a request rounds up).
+static const int kFp8NclSteps[] = {1, 2, 3, 4, 5, 6, 8, 10, 12, 16};
+
+int fp8_ncl_for(int ncq) {
+  const int need = (ncq + kWave - 1) / kWave;
+  for (int n : kFp8NclSteps)
+    if (n >= need) return n;
+  return 0;
+}
+
+// Hidden rows per pass: the smallest power of two >= M, at most 8 and with
+// MR * NCL <= 16 (more rows take several passes over the table).
+int fp8_rows_for(int M, int ncl) {
+  int mr = 1;
+  while (mr < M && mr < 8 && 2 * mr * ncl <= 16) mr *= 2;
+  return mr;
+}
+
+hipError_t launch_fp8(const Fp8Launch &L, int mr, int ncl) {
+  switch (mr) {
+    case 1: return launch_fp8_mr<1>(L, ncl);
+    case 2: return launch_fp8_mr<2>(L, ncl);
+    case 4: return launch_fp8_mr<4>(L, ncl);
+    case 8: return launch_fp8_mr<8>(L, ncl);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace mtp

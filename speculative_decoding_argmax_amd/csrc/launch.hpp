@@ -68,6 +68,25 @@ hipError_t launch_pack_tiled(const void *head, int64_t V, int nch, const int32_t
 
 hipError_t launch_pack(const void *head, int64_t V, int nch, const int32_t *ids, int64_t C,
                        void *table, int num_cus, hipStream_t stream);
+
+struct Fp8Launch {
+  const void *X;        // hidden [M][H] bf16
+  const void *Q;        // E4M3 codes [N][H]
+  const float *scales;  // [N] row scales (powers of two)
+  int M;
+  int64_t N;
+  int ncq;              // H / 16 (16-byte code chunks per row)
+  int max_blocks_x;
+  RowSink sink;
+  hipStream_t stream;
+};
+
+// Code chunks per lane that have an instantiation (0: too wide).
+int fp8_ncl_for(int ncq);
+int fp8_rows_for(int M, int ncl);
+hipError_t launch_fp8(const Fp8Launch &L, int mr, int ncl);
+hipError_t launch_pack_fp8(const void *head, int64_t V, int H, const int32_t *ids, int64_t C,
+                           void *q, float *scales, int num_cus, hipStream_t stream);
 hipError_t launch_fill_zero(void *ws, size_t bytes, hipStream_t stream);
 
 }  // namespace mtp

@@ -193,3 +193,24 @@ def test_gather_rejects_bad_arguments():
     c.path = mtp.MTP_PATH_MFMA
     g = mtp.lib.mtp_draft_argmax_gather_cfg
     assert g(*ok, ctypes.byref(c)) == mtp.MTP_ERR_UNSUPPORTED
+
+
+def test_fp8_entry_points_reject_bad_arguments():
+    assert mtp.mtp_fp8_table_bytes(100, 2048) == 100 * 2048
+    assert mtp.mtp_fp8_table_bytes(100, 24) == 0          # H % 16 != 0
+    assert mtp.mtp_fp8_table_bytes(0, 32) == 0
+    p = mtp.lib.mtp_pack_candidates_fp8
+    ok = (FAKE, 100, 64, FAKE, 50, FAKE, FAKE, None)
+    assert p(None, *ok[1:]) == INVALID
+    assert p(*ok[:2], 24, *ok[3:]) == INVALID            # H % 16
+    assert p(*ok[:3], None, 101, *ok[5:]) == INVALID     # C > V without ids
+    assert p(*ok[:5], P(0x10008), *ok[6:]) == INVALID    # codes not 16-byte aligned
+    assert p(*ok[:6], P(0x10002), None) == INVALID       # scales not 4-byte aligned
+    d = mtp.lib.mtp_draft_argmax_fp8
+    dk = (FAKE, 1, 64, FAKE, FAKE, None, 100, FAKE, None, FAKE, 4096, None)
+    assert d(*dk[:2], 24, *dk[3:]) == INVALID
+    assert d(*dk[:4], None, *dk[5:]) == INVALID          # no scales
+    assert d(*dk[:9], None, *dk[10:]) == mtp.MTP_ERR_WORKSPACE
+    c = mtp.mtp_config()
+    c.path = mtp.MTP_PATH_MFMA
+    assert mtp.lib.mtp_draft_argmax_fp8_cfg(*dk, ctypes.byref(c)) == mtp.MTP_ERR_UNSUPPORTED
