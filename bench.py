@@ -54,6 +54,10 @@ def parse_args():
     ap.add_argument("--layout", choices=("auto", "rows", "tiled"), default="auto",
                     help="table layout: row-major, or the 64-row tiled layout of include/mtp.h "
                          "(auto: rows when every call has at most 8 hidden rows)")
+    ap.add_argument("--table", choices=("bf16", "fp8"), default="bf16",
+                    help="precision of the draft's candidate table: bf16 rows, or E4M3 rows "
+                         "with power-of-two row scales (mtp_pack_candidates_fp8; row-major "
+                         "layout); the verify always reads the bf16 head")
     ap.add_argument("--draft-source", choices=("table", "gather"), default="table",
                     help="draft calls read a packed candidate table (default), or head rows "
                          "through a per-call id list (mtp_draft_argmax_gather; row-major only)")
@@ -127,6 +131,11 @@ def main() -> int:
     if layout == "auto":
         layout = "rows" if max(wk.Md, wk.Mv) <= 8 else "tiled"
     gather = args.draft_source == "gather"
+    fp8 = args.table == "fp8"
+    if fp8 and (layout != "rows" or gather):
+        print("--table fp8 runs on the row-major packed table (use --layout rows, "
+              "--draft-source table)", file=sys.stderr)
+        return 2
     if gather and layout != "rows":
         print("--draft-source gather runs on the row-major head (use --layout rows)",
               file=sys.stderr)
@@ -135,6 +144,12 @@ def main() -> int:
     ids_d = up(ids, np.int32)
     tables = []
     for _ in range(max(1, args.table_copies)):
+        if fp8:
+            tq = torch.empty((wk.C, wk.H), dtype=torch.uint8, device=dev)
+            ts = torch.empty(wk.C, dtype=torch.float32, device=dev)
+            mtp.mtp_pack_candidates_fp8(head_d, ids_d, tq, ts)
+            tables.append((tq, ts))
+            continue
         if layout == "rows":
             t = torch.empty((wk.C, wk.H), dtype=torch.int16, device=dev)
             mtp.mtp_pack_candidates(head_d, ids_d, t)
@@ -142,6 +157,14 @@ def main() -> int:
             t = mtp.alloc_tiled(wk.C, wk.H, dev)
             mtp.mtp_pack_tiled(head_d, ids_d, t)
         tables.append(t)
+    if layout == "tiled" or fp8:
+        # counter calibration for rocprofv3 runs (untimed): one plain
+        # gather-copy of known size, the row-major candidate pack, which
+        # these layouts do not otherwise run
+        calib = torch.empty((wk.C, wk.H), dtype=torch.int16, device=dev)
+        mtp.mtp_pack_candidates(head_d, ids_d, calib)
+        torch.cuda.synchronize()
+        del calib
     if layout == "tiled":
         head_v = mtp.alloc_tiled(wk.V, wk.H, dev)
         mtp.mtp_pack_tiled(head_d, None, head_v, C=wk.V)
@@ -166,7 +189,10 @@ def main() -> int:
                   for c in range(wk.draft_calls)] if gather else None
 
     def draft_call(c, table):
-        if gather:
+        if fp8:
+            mtp.mtp_draft_argmax_fp8(h_d[c], table[0], table[1], ids_d, out_ids[c], out_logit[c],
+                                     ws=ws_d)
+        elif gather:
             mtp.mtp_draft_argmax_gather(h_d[c], head_d, gather_ids[c], out_ids[c], out_logit[c],
                                         ws=ws_d)
         elif layout == "rows":
@@ -268,10 +294,29 @@ def main() -> int:
     torch.cuda.synchronize()
     warm_draft_us = e0.elapsed_time(e1) * 1000.0 / K
 
+    agreement = None
+    if fp8:
+        # how often the fp8 draft picks the bf16 draft's token (512 hidden rows
+        # of the workload's distribution; untimed)
+        n_rows = 512
+        hx = up(wl.hidden_states(n_rows, wk.H, wk.seed, block=900))
+        t16 = torch.empty((wk.C, wk.H), dtype=torch.int16, device=dev)
+        mtp.mtp_pack_candidates(head_d, ids_d, t16)
+        a8 = torch.empty(n_rows, dtype=torch.int32, device=dev)
+        a16 = torch.empty(n_rows, dtype=torch.int32, device=dev)
+        mtp.mtp_draft_argmax_fp8(hx, tables[0][0], tables[0][1], ids_d, a8)
+        mtp.mtp_draft_argmax(hx, t16, ids_d, a16)
+        agreement = round(float((a8 == a16).float().mean().item()), 4)
+        del t16
+
     H, C, V, Md, Mv = wk.H, wk.C, wk.V, wk.Md, wk.Mv
     # algorithmic bytes: weight rows + hidden rows + small outputs (winner ids,
     # logits; verify also reads drafts and writes acceptance)
-    draft_bytes = C * H * 2 + Md * H * 2 + Md * (4 + 4 + 4) + (C * 4 if gather else 0)
+    if fp8:
+        # codes + one scale per row
+        draft_bytes = C * H + C * 4 + Md * H * 2 + Md * (4 + 4 + 4)
+    else:
+        draft_bytes = C * H * 2 + Md * H * 2 + Md * (4 + 4 + 4) + (C * 4 if gather else 0)
     verify_bytes = V * H * 2 + Mv * H * 2 + wk.B * wk.k * 4 + Mv * (4 + 4 + 4) + wk.B * 4
     d_us = statistics.mean(draft_ms) * 1000.0
     v_us = statistics.mean(verify_ms) * 1000.0
@@ -317,7 +362,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8-e4m3 draft rows, bf16 hidden and head" if fp8 else "bf16",
         "data": "synthetic",
         "config": {
             "workload": f"{wk.name}: {wk.draft_calls} draft calls (M={Md}, {C}-row table) + 1 "
@@ -326,6 +371,7 @@ def main() -> int:
             "accumulate": "f32", "table_copies": n_tab, "seed": wk.seed, "layout": layout,
             "step": "hip_graph" if graphs else "eager",
             "draft_source": args.draft_source,
+            "draft_table": args.table,
         },
         "calls": {"draft": draft_stats, "verify": verify_stats},
         "context": {
@@ -334,6 +380,7 @@ def main() -> int:
             "graph_step_us_mean": round(statistics.mean(graph_step_ms) * 1000.0, 2)
             if graph_step_ms else None,
             "draft_same_table_us": round(warm_draft_us, 2),
+            "fp8_draft_agrees_with_bf16": agreement,
             "setup_s": round(setup_s, 1),
         },
         "roofline": roofline,

@@ -446,7 +446,12 @@ mtp_status mtp_draft_argmax_fp8_cfg(const mtp_bf16 *hidden, int M, int H, const 
   int cus = 0;
   hipError_t e = current_cus(&cus);
   if (e != hipSuccess) return hip_fail(e);
-  const int per_cu = (cfg && cfg->blocks_per_cu > 0) ? cfg->blocks_per_cu : 1;
+  const int mr = mtp::fp8_rows_for(M, ncl);
+  // two workgroups per CU when one pass covers every hidden row with enough
+  // arithmetic per byte (MR * NCL >= 8) to be ALU-limited; one otherwise
+  // (measured on MI355X at H = 2,048 .. 5,120, M = 1 .. 8)
+  const int per_cu = (cfg && cfg->blocks_per_cu > 0) ? cfg->blocks_per_cu
+                                                      : ((mr >= M && mr * ncl >= 8) ? 2 : 1);
   mtp::Fp8Launch L;
   L.X = hidden;
   L.Q = table_q;
@@ -457,7 +462,7 @@ mtp_status mtp_draft_argmax_fp8_cfg(const mtp_bf16 *hidden, int M, int H, const 
   L.max_blocks_x = per_cu * cus;
   L.sink = draft_sink(ws, ids, out_ids, out_logit, M);
   L.stream = stream;
-  e = mtp::launch_fp8(L, mtp::fp8_rows_for(M, ncl), ncl);
+  e = mtp::launch_fp8(L, mr, ncl);
   if (e != hipSuccess) return hip_fail(e);
   return MTP_OK;
 }
