@@ -99,7 +99,7 @@ def main() -> int:
     args = parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this path has no "
-              "multi-GPU mode; the sharded design is described in DESIGN.md.", file=sys.stderr)
+              "multi-GPU mode.", file=sys.stderr)
         return 2
     import torch
 
