@@ -319,6 +319,37 @@ mtp_status mtp_draft_argmax_fp8_cfg(const mtp_bf16 *hidden, int M, int H, const 
                                     const mtp_config *cfg);
 
 /*
+ * FP8 candidate table in the tiled layout (batched draft rows: the
+ * matrix-core kernel). Same codes and scales as mtp_pack_candidates_fp8,
+ * stored as the fp8 form of the 64-row tiled layout: rows in tiles of 64
+ * (zero rows pad the last), columns padded with zeros to a multiple of 128
+ * and grouped in pairs of 32-column steps; fragment (t, p, rb), 1 KiB,
+ * ordered (t, p, rb), lane j + 16g holding the 8 codes of row
+ * 64t + 16rb + j at columns 64p + 8g .. 64p + 8g + 7 followed by those at
+ * columns 64p + 32 + 8g .. 64p + 32 + 8g + 7. The kernel converts each half to
+ * the bf16 operand of one v_mfma_f32_16x16x32_bf16 step (exact) and
+ * multiplies each finished logit by its row's scale.
+ * mtp_tiled_fp8_bytes(R, H) = ceil64(R) * ceil128(H) (0 if out of range; H a
+ * multiple of 16). scales: float [C], written by the pack.
+ */
+size_t mtp_tiled_fp8_bytes(int64_t rows, int H);
+mtp_status mtp_pack_tiled_fp8(const mtp_bf16 *head, int64_t V, int H, const int32_t *ids,
+                              int64_t C, void *tiled_q, size_t tiled_bytes, float *scales,
+                              hipStream_t stream);
+/* mtp_draft_argmax_fp8 on the tiled fp8 table: up to 64 hidden rows per
+ * pass (more take further passes); cfg->path MTP_PATH_VALU gives
+ * MTP_ERR_UNSUPPORTED. */
+mtp_status mtp_draft_argmax_tiled_fp8(const mtp_bf16 *hidden, int M, int H, const void *table_q,
+                                      const float *scales, const int32_t *ids, int64_t C,
+                                      int32_t *out_ids, float *out_logit, void *ws,
+                                      size_t ws_bytes, hipStream_t stream);
+mtp_status mtp_draft_argmax_tiled_fp8_cfg(const mtp_bf16 *hidden, int M, int H,
+                                          const void *table_q, const float *scales,
+                                          const int32_t *ids, int64_t C, int32_t *out_ids,
+                                          float *out_logit, void *ws, size_t ws_bytes,
+                                          hipStream_t stream, const mtp_config *cfg);
+
+/*
  * Graph-captured MTP step.
  *
  * Records the library calls a caller makes on `stream` between

@@ -475,6 +475,67 @@ mtp_status mtp_draft_argmax_fp8(const mtp_bf16 *hidden, int M, int H, const uint
                                   ws_bytes, stream, nullptr);
 }
 
+size_t mtp_tiled_fp8_bytes(int64_t rows, int H) {
+  if (rows < 1 || rows > INT32_MAX || H < 16 || H > MTP_MAX_HIDDEN || H % 16 != 0) return 0;
+  return (size_t)mtp::tiled_rows(rows) * (size_t)mtp::tiled_cols(H);
+}
+
+mtp_status mtp_pack_tiled_fp8(const mtp_bf16 *head, int64_t V, int H, const int32_t *ids,
+                              int64_t C, void *tiled_q, size_t tiled_bytes, float *scales,
+                              hipStream_t stream) {
+  if (!head || !tiled_q || !scales) return MTP_ERR_INVALID_ARG;
+  if (V < 1 || V > INT32_MAX || (!ids && C > V)) return MTP_ERR_INVALID_ARG;
+  const size_t need = mtp_tiled_fp8_bytes(C, H);
+  if (need == 0 || tiled_bytes < need) return MTP_ERR_INVALID_ARG;
+  if (!aligned(head, 16) || !aligned(tiled_q, 16) || !aligned(scales, 4) ||
+      (ids && !aligned(ids, 4)))
+    return MTP_ERR_INVALID_ARG;
+  int cus = 0;
+  hipError_t e = current_cus(&cus);
+  if (e != hipSuccess) return hip_fail(e);
+  e = mtp::launch_pack_tiled_fp8(head, V, H, ids, C, tiled_q, scales, cus, stream);
+  if (e != hipSuccess) return hip_fail(e);
+  return MTP_OK;
+}
+
+mtp_status mtp_draft_argmax_tiled_fp8_cfg(const mtp_bf16 *hidden, int M, int H,
+                                          const void *table_q, const float *scales,
+                                          const int32_t *ids, int64_t C, int32_t *out_ids,
+                                          float *out_logit, void *ws, size_t ws_bytes,
+                                          hipStream_t stream, const mtp_config *cfg) {
+  if (!scales || !aligned(scales, 4) || H % 16 != 0) return MTP_ERR_INVALID_ARG;
+  mtp_status st =
+      check_draft_args(hidden, M, H, table_q, ids, C, out_ids, out_logit, ws, ws_bytes, cfg);
+  if (st != MTP_OK) return st;
+  if (cfg && cfg->path == MTP_PATH_VALU) return MTP_ERR_UNSUPPORTED;
+  int cus = 0;
+  hipError_t e = current_cus(&cus);
+  if (e != hipSuccess) return hip_fail(e);
+  const int per_cu = (cfg && cfg->blocks_per_cu > 0) ? cfg->blocks_per_cu : 1;
+  mtp::DmaLaunch L;
+  L.X = hidden;
+  L.WT = table_q;
+  L.M = M;
+  L.N = C;
+  L.nch = H / 8;
+  L.S = mtp::tiled_cols(H) / 32;
+  L.max_blocks_x = per_cu * cus;
+  L.sink = draft_sink(ws, ids, out_ids, out_logit, M);
+  L.stream = stream;
+  L.scales = scales;
+  e = mtp::launch_dma_fp8(L, mtp::dma_nb_for_fp8(M));
+  if (e != hipSuccess) return hip_fail(e);
+  return MTP_OK;
+}
+
+mtp_status mtp_draft_argmax_tiled_fp8(const mtp_bf16 *hidden, int M, int H, const void *table_q,
+                                      const float *scales, const int32_t *ids, int64_t C,
+                                      int32_t *out_ids, float *out_logit, void *ws,
+                                      size_t ws_bytes, hipStream_t stream) {
+  return mtp_draft_argmax_tiled_fp8_cfg(hidden, M, H, table_q, scales, ids, C, out_ids, out_logit,
+                                        ws, ws_bytes, stream, nullptr);
+}
+
 struct mtp_graph {
   hipGraph_t graph;
   hipGraphExec_t exec;

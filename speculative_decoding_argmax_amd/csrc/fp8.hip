@@ -126,6 +126,84 @@ hipError_t launch_pack_fp8(const void *head, int64_t V, int H, const int32_t *id
   return hipGetLastError();
 }
 
+// FP8 tiled layout (the fp8 form of the 64-row tiled layout): rows in tiles
+// of 64, columns padded to a multiple of 128 and grouped in pairs of 32-column
+// steps. Fragment (t, p, rb), 1 KiB, ordered (t, p, rb): lane j + 16g holds
+// the 8 codes of row 64t + 16rb + j, columns 64p + 8g .. 64p + 8g + 7, then
+// the 8 codes of columns 64p + 32 + 8g .. 64p + 32 + 8g + 7. One wave per
+// row (padding rows included, written as zeros); rows quantised as pack_fp8.
+__global__ void __launch_bounds__(256)
+    pack_tiled_fp8(const uint4 *__restrict__ head, int64_t V, int H, const int32_t *__restrict__ ids,
+                   int64_t C, int64_t Cp, int Hp, uint8_t *__restrict__ tiled,
+                   float *__restrict__ scales) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t waves = (int64_t)gridDim.x * (blockDim.x / kWave);
+  const int nch = H / 8;
+  const int SP = Hp / 64;
+  for (int64_t row = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave; row < Cp;
+       row += waves) {
+    const int64_t id = row < C ? (ids ? (int64_t)ids[row] : row) : -1;
+    const bool valid = id >= 0 && id < V;
+    const uint4 *src = head + (valid ? id : 0) * nch;
+    uint32_t mx = 0;
+    if (valid) {
+      for (int c = lane; c < nch; c += kWave) {
+        const uint4 v = src[c];
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t lo = w[k] & 0x7FFFu, hi = (w[k] >> 16) & 0x7FFFu;
+          mx = lo > mx ? lo : mx;
+          mx = hi > mx ? hi : mx;
+        }
+      }
+    }
+    mx = wave_max_u32(mx);
+    int e = 0;
+    if (mx != 0 && mx < 0x7F80u) {
+      const double amax = bf16_value(mx);
+      e = ilogb(amax) - 8;
+      while (ldexp(448.0, e) < amax) ++e;
+      while (ldexp(448.0, e - 1) >= amax) --e;
+    }
+    const int64_t t = row / 64;
+    const int rb = (int)(row % 64) / 16;
+    const int jj = (int)(row % 16);
+    for (int c8 = lane; c8 < Hp / 8; c8 += kWave) {
+      uint32_t b[2] = {0u, 0u};
+      if (valid && c8 < nch) {
+        const uint4 v = src[c8];
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const uint32_t bits = (k & 1) ? (w[k >> 1] >> 16) : (w[k >> 1] & 0xFFFFu);
+          const uint32_t code = e4m3_code(ldexp(bf16_value(bits), -e));
+          b[k >> 2] |= code << (8 * (k & 3));
+        }
+      }
+      const int s = c8 / 4, g = c8 % 4;
+      const int64_t off = ((((t * SP + s / 2) * 4 + rb) * kWave + jj + 16 * g) * 16) + (s & 1) * 8;
+      *reinterpret_cast<uint2 *>(tiled + off) = make_uint2(b[0], b[1]);
+    }
+    if (lane == 0 && row < C) scales[row] = valid ? (float)ldexp(1.0, e) : 1.0f;
+  }
+}
+
+hipError_t launch_pack_tiled_fp8(const void *head, int64_t V, int H, const int32_t *ids,
+                                 int64_t C, void *tiled, float *scales, int num_cus,
+                                 hipStream_t stream) {
+  const int64_t Cp = tiled_rows(C);
+  const int Hp = tiled_cols(H);
+  const int64_t waves_per_block = 4;
+  int64_t blocks = (Cp + waves_per_block - 1) / waves_per_block;
+  const int64_t cap = (int64_t)num_cus * 8;
+  if (blocks > cap) blocks = cap;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(pack_tiled_fp8, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     (const uint4 *)head, V, H, ids, C, Cp, Hp, (uint8_t *)tiled, scales);
+  return hipGetLastError();
+}
+
 // ---- draft GEMV + argmax ---------------------------------------------------
 
 constexpr int kFp8Threads = 256;

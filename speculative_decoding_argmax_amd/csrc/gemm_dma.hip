@@ -78,13 +78,18 @@ __device__ __forceinline__ void wait_vmcnt() {
 // 32-column steps per chunk; NBUF: LDS slots (3 or 4); WV: waves per group;
 // CP: cache-policy bits of the weight copies (2 = nt: the table is streamed
 // once per call, so its lines should not displace the hidden rows in L2).
-template <int NB, int RW, int KS, int NBUF, int WV, int CP>
+// FP8: the table holds E4M3 codes in the fp8 tiled layout (one 1 KiB
+// fragment carries two 32-column steps of a 16-row block: lane j + 16g holds
+// the 8 codes of step 2p, columns 8g..8g+7, then those of step 2p + 1), and
+// scales[row] multiplies each finished logit.
+template <int NB, int RW, int KS, int NBUF, int WV, int CP, bool FP8 = false>
 __global__ void __launch_bounds__(WV * 64)
     gemm_argmax_dma(const uint4 *__restrict__ X, const uint4 *__restrict__ WT, int M, int N,
-                    int nch, int S, RowSink sink) {
+                    int nch, int S, RowSink sink, const float *__restrict__ scales) {
   constexpr int RBT = WV * RW;                 // 16-row blocks per workgroup tile
   constexpr int TV = RBT * 16;                 // table rows per workgroup tile
-  constexpr int AF = RBT * KS;                 // weight fragments per chunk
+  static_assert(!FP8 || KS % 2 == 0, "fp8 chunks hold whole step pairs");
+  constexpr int AF = FP8 ? RBT * KS / 2 : RBT * KS;  // weight fragments per chunk
   constexpr int FR = AF + KS * NB;             // fragments per chunk
   constexpr int PER_WAVE = (FR + WV - 1) / WV; // copies per wave per chunk
   static_assert(NBUF >= 3 && NBUF <= 4, "three or four slots");
@@ -96,6 +101,13 @@ __global__ void __launch_bounds__(WV * 64)
   __shared__ uint4 slot3[NBUF > 3 ? FR * 64 : 1];
   __shared__ float f_val[NB * 16];
   __shared__ int64_t f_row[NB * 16];
+  // fp8: the row scales of a tile, copied with the tile's last chunk into
+  // the slot's scale array (one array per slot, like the fragments)
+  constexpr int SCN = FP8 ? TV : 1;
+  __shared__ float scale0[SCN];
+  __shared__ float scale1[SCN];
+  __shared__ float scale2[SCN];
+  __shared__ float scale3[NBUF > 3 ? SCN : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -122,6 +134,13 @@ __global__ void __launch_bounds__(WV * 64)
     else if constexpr (SL == 2) return slot2;
     else return slot3;
   };
+  auto scl = [&](auto tag) -> float * {
+    constexpr int SL = decltype(tag)::value;
+    if constexpr (SL == 0) return scale0;
+    else if constexpr (SL == 1) return scale1;
+    else if constexpr (SL == 2) return scale2;
+    else return scale3;
+  };
 
   // Copy the next chunk (tile iss_t, K chunk iss_c) into a slot, then step
   // the position. Fragment f < AF: weights, step f / RBT of the chunk,
@@ -142,10 +161,12 @@ __global__ void __launch_bounds__(WV * 64)
       int f = wave + WV * q;
       f = f < FR ? f : FR - 1;
       if (f < AF) {
-        const int s = f / RBT;
+        const int s = f / RBT;                 // step (bf16) or step pair (fp8) of the chunk
         int rb = tile * RBT + f % RBT;
         rb = rb < nrb ? rb : nrb - 1;          // past the table: valid, never reported
-        const uint4 *src = WT + (((int64_t)(rb >> 2) * S + c * KS + s) * 4 + (rb & 3)) * kWave + lane;
+        const uint4 *src =
+            FP8 ? WT + (((int64_t)(rb >> 2) * (S / 2) + c * (KS / 2) + s) * 4 + (rb & 3)) * kWave + lane
+                : WT + (((int64_t)(rb >> 2) * S + c * KS + s) * 4 + (rb & 3)) * kWave + lane;
         __builtin_amdgcn_global_load_lds((const void *)src, MTP_LDS(base + f * kWave), 16, 0, CP);
       } else {
         const int fb = f - AF;
@@ -158,6 +179,16 @@ __global__ void __launch_bounds__(WV * 64)
         const int col = min((c * KS + s) * 4 + g, nch - 1);
         const uint4 *src = X + (int64_t)m * nch + col;
         __builtin_amdgcn_global_load_lds((const void *)src, MTP_LDS(base + f * kWave), 16, 0, 0);
+      }
+    }
+    if constexpr (FP8) {
+      // the tile's last chunk also brings its row scales: wave w copies those
+      // of 64-row block w (issued after the chunk's fragments, so the waits
+      // for the chunk cover it; rows past N read row N - 1, never reported)
+      if (c == nchunks - 1 && wave < RBT / 4) {
+        const int row = min(tile * TV + wave * 64 + lane, N - 1);
+        __builtin_amdgcn_global_load_lds((const void *)(scales + row),
+                                         MTP_LDS(scl(tag) + wave * 64), 4, 0, 0);
       }
     }
   };
@@ -193,11 +224,27 @@ __global__ void __launch_bounds__(WV * 64)
     if (it + NBUF - 1 < total) issue(std::integral_constant<int, (SL + NBUF - 1) % NBUF>{});
     const uint4 *A = slot(tag);
     const uint4 *Bf = A + AF * kWave;
+    uint4 raw[RW];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       uint4 a[RW];
 #pragma unroll
-      for (int rw = 0; rw < RW; ++rw) a[rw] = A[(s * RBT + wave * RW + rw) * kWave + lane];
+      for (int rw = 0; rw < RW; ++rw) {
+        if constexpr (FP8) {
+          // one read per step pair; each half converts to that step's
+          // bf16 operand (E4M3 -> bf16 is exact)
+          if (s % 2 == 0) raw[rw] = A[((s / 2) * RBT + wave * RW + rw) * kWave + lane];
+          const uint32_t w0 = s % 2 ? raw[rw].z : raw[rw].x;
+          const uint32_t w1 = s % 2 ? raw[rw].w : raw[rw].y;
+          a[rw] = make_uint4(
+              __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w0, 1.0f, false)),
+              __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w0, 1.0f, true)),
+              __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w1, 1.0f, false)),
+              __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w1, 1.0f, true)));
+        } else {
+          a[rw] = A[(s * RBT + wave * RW + rw) * kWave + lane];
+        }
+      }
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         const uint4 b = Bf[(s * NB + nb) * kWave + lane];
@@ -217,7 +264,8 @@ __global__ void __launch_bounds__(WV * 64)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int v = vbase + rw * 16 + r;
-            const float z = acc[rw][nb][r];
+            float z = acc[rw][nb][r];
+            if constexpr (FP8) z *= scl(tag)[(wave * RW + rw) * 16 + 4 * g + r];
             if (v < N && better_row(z, v, bv[nb], bi[nb])) {
               bv[nb] = z;
               bi[nb] = v;
@@ -275,15 +323,15 @@ __global__ void __launch_bounds__(WV * 64)
 int64_t tiled_rows(int64_t rows) { return (rows + 63) / 64 * 64; }
 int tiled_cols(int H) { return (H + 127) / 128 * 128; }
 
-template <int NB, int RW, int KS, int NBUF, int WV, int CP>
+template <int NB, int RW, int KS, int NBUF, int WV, int CP, bool FP8 = false>
 static hipError_t launch_dma_cfg(const DmaLaunch &L) {
   constexpr int TV = WV * RW * 16;
   const int64_t ntiles = (L.N + TV - 1) / TV;
   const int gx = (int)(ntiles < L.max_blocks_x ? ntiles : L.max_blocks_x);
   const int gy = (L.M + NB * 16 - 1) / (NB * 16);
-  hipLaunchKernelGGL((gemm_argmax_dma<NB, RW, KS, NBUF, WV, CP>), dim3(gx, gy), dim3(WV * 64), 0,
-                     L.stream, (const uint4 *)L.X, (const uint4 *)L.WT, L.M, (int)L.N, L.nch,
-                     L.S, L.sink);
+  hipLaunchKernelGGL((gemm_argmax_dma<NB, RW, KS, NBUF, WV, CP, FP8>), dim3(gx, gy),
+                     dim3(WV * 64), 0, L.stream, (const uint4 *)L.X, (const uint4 *)L.WT, L.M,
+                     (int)L.N, L.nch, L.S, L.sink, L.scales);
   return hipGetLastError();
 }
 
@@ -311,6 +359,24 @@ hipError_t launch_dma(const DmaLaunch &L, int nb) {
     case 6: return launch_dma_cfg<6, 4, 1, 3, 8, NT>(L);
     case 8: return launch_dma_cfg<8, 4, 1, 3, 8, NT>(L);
     case 10: return launch_dma_cfg<10, 4, 1, 3, 8, NT>(L);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// FP8 tables: hidden-row blocks per pass 1..4 (up to 64 rows; more rows take
+// further passes). Chunks hold one step pair (KS = 2).
+int dma_nb_for_fp8(int M) {
+  const int need = (M + 15) / 16;
+  return need < 4 ? need : 4;
+}
+
+hipError_t launch_dma_fp8(const DmaLaunch &L, int nb) {
+  constexpr int NT = 2;
+  switch (nb) {
+    case 1: return launch_dma_cfg<1, 1, 2, 4, 8, NT, true>(L);
+    case 2: return launch_dma_cfg<2, 2, 2, 4, 8, NT, true>(L);
+    case 3: return launch_dma_cfg<3, 2, 2, 4, 8, NT, true>(L);
+    case 4: return launch_dma_cfg<4, 2, 2, 4, 8, NT, true>(L);
     default: return hipErrorInvalidValue;
   }
 }

@@ -57,12 +57,18 @@ struct DmaLaunch {
   int max_blocks_x;
   RowSink sink;
   hipStream_t stream;
+  const float *scales = nullptr;  // fp8 tables: row scales [N]
 };
 
 int64_t tiled_rows(int64_t rows);
 int tiled_cols(int H);
 int dma_nb_for(int M);
 hipError_t launch_dma(const DmaLaunch &L, int nb);
+int dma_nb_for_fp8(int M);
+hipError_t launch_dma_fp8(const DmaLaunch &L, int nb);
+hipError_t launch_pack_tiled_fp8(const void *head, int64_t V, int H, const int32_t *ids,
+                                 int64_t C, void *tiled, float *scales, int num_cus,
+                                 hipStream_t stream);
 hipError_t launch_pack_tiled(const void *head, int64_t V, int nch, const int32_t *ids,
                              int64_t C, int S, void *tiled, int num_cus, hipStream_t stream);
 

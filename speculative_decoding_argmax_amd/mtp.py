@@ -91,6 +91,10 @@ def _load() -> ctypes.CDLL:
         "mtp_pack_candidates_fp8": ([P, I64, I, P, I64, P, P, P], I),
         "mtp_draft_argmax_fp8": ([P, I, I, P, P, P, I64, P, P, P, S, P], I),
         "mtp_draft_argmax_fp8_cfg": ([P, I, I, P, P, P, I64, P, P, P, S, P, P], I),
+        "mtp_tiled_fp8_bytes": ([I64, I], S),
+        "mtp_pack_tiled_fp8": ([P, I64, I, P, I64, P, S, P, P], I),
+        "mtp_draft_argmax_tiled_fp8": ([P, I, I, P, P, P, I64, P, P, P, S, P], I),
+        "mtp_draft_argmax_tiled_fp8_cfg": ([P, I, I, P, P, P, I64, P, P, P, S, P, P], I),
         "mtp_graph_begin": ([P], I),
         "mtp_graph_end": ([P, ctypes.POINTER(P)], I),
         "mtp_graph_launch": ([P, P], I),
@@ -432,6 +436,56 @@ def mtp_draft_argmax_fp8(hidden, table_q, scales, ids, out_ids, out_logit=None, 
         _ptr(out_logit, "out_logit", (torch.float32,), allow_none=True),
         _ptr(ws, "ws", (torch.int64, torch.uint8, torch.int32)), ws.numel() * ws.element_size(),
         _stream(stream), ctypes.byref(cfg)), "mtp_draft_argmax_fp8")
+
+
+def mtp_tiled_fp8_bytes(rows: int, H: int) -> int:
+    return int(lib.mtp_tiled_fp8_bytes(rows, H))
+
+
+def alloc_tiled_fp8(rows: int, H: int, device=None):
+    """A uint8 buffer for an fp8 tiled table of `rows` rows, and its scales."""
+    torch = _torch()
+    n = mtp_tiled_fp8_bytes(rows, H)
+    if n == 0:
+        raise ValueError("unsupported fp8 tiled shape")
+    return (torch.empty(n, dtype=torch.uint8, device=device or "cuda"),
+            torch.empty(rows, dtype=torch.float32, device=device or "cuda"))
+
+
+def mtp_pack_tiled_fp8(head, ids, tiled_q, scales, C: Optional[int] = None, stream=None) -> None:
+    torch = _torch()
+    V, H = head.shape
+    C = ids.numel() if ids is not None else (V if C is None else C)
+    if scales.numel() != C:
+        raise ValueError("scales must have C entries")
+    _check(lib.mtp_pack_tiled_fp8(
+        _ptr(head, "head", _bf16_types()), V, H, _ptr(ids, "ids", (torch.int32,), allow_none=True),
+        C, _ptr(tiled_q, "tiled_q", (torch.uint8,)), tiled_q.numel(),
+        _ptr(scales, "scales", (torch.float32,)), _stream(stream)), "mtp_pack_tiled_fp8")
+
+
+def mtp_draft_argmax_tiled_fp8(hidden, table_q, scales, C: int, ids, out_ids, out_logit=None,
+                               ws=None, stream=None, path: int = MTP_PATH_AUTO,
+                               blocks_per_cu: int = 0) -> None:
+    """Draft over an fp8 tiled candidate table of C rows (matrix cores)."""
+    torch = _torch()
+    M, H = hidden.shape
+    if scales.numel() != C or (ids is not None and ids.numel() != C):
+        raise ValueError("scales and ids must have C entries")
+    if out_ids.numel() != M or (out_logit is not None and out_logit.numel() != M):
+        raise ValueError("outputs must have M entries")
+    if ws is None:
+        _no_alloc_in_capture("mtp_draft_argmax_tiled_fp8")
+        ws = alloc_workspace(mtp_draft_workspace_bytes(M, C, H), hidden.device, stream)
+    cfg = _cfg(path, blocks_per_cu)
+    _check(lib.mtp_draft_argmax_tiled_fp8_cfg(
+        _ptr(hidden, "hidden", _bf16_types()), M, H, _ptr(table_q, "table_q", (torch.uint8,)),
+        _ptr(scales, "scales", (torch.float32,)),
+        _ptr(ids, "ids", (torch.int32,), allow_none=True), C,
+        _ptr(out_ids, "out_ids", (torch.int32,)),
+        _ptr(out_logit, "out_logit", (torch.float32,), allow_none=True),
+        _ptr(ws, "ws", (torch.int64, torch.uint8, torch.int32)), ws.numel() * ws.element_size(),
+        _stream(stream), ctypes.byref(cfg)), "mtp_draft_argmax_tiled_fp8")
 
 
 # ---- graph-captured MTP step ----------------------------------------------

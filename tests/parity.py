@@ -148,3 +148,20 @@ def make_drafts(t_oracle: np.ndarray, wk: wl.Workload, ids: np.ndarray) -> np.nd
     if wk.p is None:
         return wl.uniform_drafts(wk.B, wk.k, ids, wk.seed)
     return wl.select_drafts(t_oracle, wl.agreement_draws(wk.B, wk.k, wk.p, len(ids), wk.seed), ids)
+
+
+def check_fp8_rows(g_ids, g_logit, ref, x, q, e, ids):
+    """Near-tie rule of the bf16 path, with logits recomputed as fp8 logits."""
+    pos = {int(v): i for i, v in enumerate(ids)} if ids is not None else None
+    for m in range(len(g_ids)):
+        top, runner = float(ref["exact"][m]), float(ref["runner_exact"][m])
+        tol = NEAR_TIE_REL * abs(top)
+        g = int(g_ids[m])
+        row = pos[g] if pos is not None else g
+        if g == ref["id"][m]:
+            zg = top
+        else:
+            assert runner >= top - tol, f"row {m}: {g} vs {ref['id'][m]} outside a near tie"
+            zg = float(oracle.draft_fp8(x[m:m + 1], q[row:row + 1], e[row:row + 1])["exact"][0])
+            assert zg >= top - tol
+        assert abs(float(g_logit[m]) - zg) <= LOGIT_REL * abs(zg)

@@ -214,3 +214,30 @@ def test_fp8_entry_points_reject_bad_arguments():
     c = mtp.mtp_config()
     c.path = mtp.MTP_PATH_MFMA
     assert mtp.lib.mtp_draft_argmax_fp8_cfg(*dk, ctypes.byref(c)) == mtp.MTP_ERR_UNSUPPORTED
+
+
+def test_tiled_fp8_entry_points_reject_bad_arguments():
+    assert mtp.mtp_tiled_fp8_bytes(100, 2048) == 128 * 2048
+    assert mtp.mtp_tiled_fp8_bytes(65, 16) == 128 * 128
+    assert mtp.mtp_tiled_fp8_bytes(100, 24) == 0         # H % 16 != 0
+    assert mtp.mtp_tiled_fp8_bytes(0, 32) == 0
+    p = mtp.lib.mtp_pack_tiled_fp8
+    need = mtp.mtp_tiled_fp8_bytes(50, 64)
+    ok = (FAKE, 100, 64, FAKE, 50, FAKE, need, FAKE, None)
+    assert p(None, *ok[1:]) == INVALID
+    assert p(*ok[:2], 24, *ok[3:]) == INVALID            # H % 16
+    assert p(*ok[:3], None, 101, *ok[5:]) == INVALID     # C > V without ids
+    assert p(*ok[:6], need - 1, *ok[7:]) == INVALID      # buffer too small
+    assert p(*ok[:5], P(0x10008), *ok[6:]) == INVALID    # codes not 16-byte aligned
+    assert p(*ok[:7], P(0x10002), None) == INVALID       # scales not 4-byte aligned
+    assert p(*ok[:7], None, None) == INVALID             # no scales
+    d = mtp.lib.mtp_draft_argmax_tiled_fp8
+    dk = (FAKE, 1, 64, FAKE, FAKE, None, 100, FAKE, None, FAKE, 4096, None)
+    assert d(*dk[:2], 24, *dk[3:]) == INVALID
+    assert d(*dk[:4], None, *dk[5:]) == INVALID          # no scales
+    assert d(*dk[:4], P(0x10002), *dk[5:]) == INVALID    # scales alignment
+    assert d(*dk[:9], None, *dk[10:]) == mtp.MTP_ERR_WORKSPACE
+    c = mtp.mtp_config()
+    c.path = mtp.MTP_PATH_VALU
+    assert mtp.lib.mtp_draft_argmax_tiled_fp8_cfg(*dk, ctypes.byref(c)) == \
+        mtp.MTP_ERR_UNSUPPORTED

@@ -8,7 +8,7 @@ import pytest
 
 import oracle
 from speculative_decoding_argmax_amd import workloads as wl
-from tests.parity import NEAR_TIE_REL, LOGIT_REL, dev_bf16, dev_i32
+from tests.parity import check_fp8_rows, dev_bf16, dev_i32
 
 pytestmark = pytest.mark.gpu
 
@@ -111,23 +111,6 @@ def test_draft_fp8_exact_grid(torch, mtp, M, C, H, with_ids):
     ref = oracle.draft_fp8(x, q_ref, e_ref, ids)
     assert np.array_equal(g_ids, ref["id"]), (g_ids, ref["id"])
     assert np.array_equal(g_logit, ref["logit"])
-
-
-def check_fp8_rows(g_ids, g_logit, ref, x, q, e, ids):
-    """Near-tie rule of the bf16 path, with logits recomputed as fp8 logits."""
-    pos = {int(v): i for i, v in enumerate(ids)} if ids is not None else None
-    for m in range(len(g_ids)):
-        top, runner = float(ref["exact"][m]), float(ref["runner_exact"][m])
-        tol = NEAR_TIE_REL * abs(top)
-        g = int(g_ids[m])
-        row = pos[g] if pos is not None else g
-        if g == ref["id"][m]:
-            zg = top
-        else:
-            assert runner >= top - tol, f"row {m}: {g} vs {ref['id'][m]} outside a near tie"
-            zg = float(oracle.draft_fp8(x[m:m + 1], q[row:row + 1], e[row:row + 1])["exact"][0])
-            assert zg >= top - tol
-        assert abs(float(g_logit[m]) - zg) <= LOGIT_REL * abs(zg)
 
 
 def test_draft_fp8_workload_data(torch, mtp):
