@@ -56,8 +56,9 @@ def parse_args():
                          "(auto: rows when every call has at most 8 hidden rows)")
     ap.add_argument("--table", choices=("bf16", "fp8"), default="bf16",
                     help="precision of the draft's candidate table: bf16 rows, or E4M3 rows "
-                         "with power-of-two row scales (mtp_pack_candidates_fp8; row-major "
-                         "layout); the verify always reads the bf16 head")
+                         "with power-of-two row scales (mtp_pack_candidates_fp8, or "
+                         "mtp_pack_tiled_fp8 with --layout tiled); the verify always reads the "
+                         "bf16 head")
     ap.add_argument("--draft-source", choices=("table", "gather"), default="table",
                     help="draft calls read a packed candidate table (default), or head rows "
                          "through a per-call id list (mtp_draft_argmax_gather; row-major only)")
@@ -132,9 +133,9 @@ def main() -> int:
         layout = "rows" if max(wk.Md, wk.Mv) <= 8 else "tiled"
     gather = args.draft_source == "gather"
     fp8 = args.table == "fp8"
-    if fp8 and (layout != "rows" or gather):
-        print("--table fp8 runs on the row-major packed table (use --layout rows, "
-              "--draft-source table)", file=sys.stderr)
+    if fp8 and gather:
+        print("--table fp8 runs on a packed candidate table (use --draft-source table)",
+              file=sys.stderr)
         return 2
     if gather and layout != "rows":
         print("--draft-source gather runs on the row-major head (use --layout rows)",
@@ -144,10 +145,15 @@ def main() -> int:
     ids_d = up(ids, np.int32)
     tables = []
     for _ in range(max(1, args.table_copies)):
-        if fp8:
+        if fp8 and layout == "rows":
             tq = torch.empty((wk.C, wk.H), dtype=torch.uint8, device=dev)
             ts = torch.empty(wk.C, dtype=torch.float32, device=dev)
             mtp.mtp_pack_candidates_fp8(head_d, ids_d, tq, ts)
+            tables.append((tq, ts))
+            continue
+        if fp8:
+            tq, ts = mtp.alloc_tiled_fp8(wk.C, wk.H, dev)
+            mtp.mtp_pack_tiled_fp8(head_d, ids_d, tq, ts)
             tables.append((tq, ts))
             continue
         if layout == "rows":
@@ -189,9 +195,12 @@ def main() -> int:
                   for c in range(wk.draft_calls)] if gather else None
 
     def draft_call(c, table):
-        if fp8:
+        if fp8 and layout == "rows":
             mtp.mtp_draft_argmax_fp8(h_d[c], table[0], table[1], ids_d, out_ids[c], out_logit[c],
                                      ws=ws_d)
+        elif fp8:
+            mtp.mtp_draft_argmax_tiled_fp8(h_d[c], table[0], table[1], wk.C, ids_d, out_ids[c],
+                                           out_logit[c], ws=ws_d)
         elif gather:
             mtp.mtp_draft_argmax_gather(h_d[c], head_d, gather_ids[c], out_ids[c], out_logit[c],
                                         ws=ws_d)
@@ -304,7 +313,12 @@ def main() -> int:
         mtp.mtp_pack_candidates(head_d, ids_d, t16)
         a8 = torch.empty(n_rows, dtype=torch.int32, device=dev)
         a16 = torch.empty(n_rows, dtype=torch.int32, device=dev)
-        mtp.mtp_draft_argmax_fp8(hx, tables[0][0], tables[0][1], ids_d, a8)
+        ws_x = mtp.alloc_workspace(mtp.mtp_draft_workspace_bytes(n_rows, wk.C, wk.H), dev)
+        if layout == "rows":
+            mtp.mtp_draft_argmax_fp8(hx, tables[0][0], tables[0][1], ids_d, a8, ws=ws_x)
+        else:
+            mtp.mtp_draft_argmax_tiled_fp8(hx, tables[0][0], tables[0][1], wk.C, ids_d, a8,
+                                           ws=ws_x)
         mtp.mtp_draft_argmax(hx, t16, ids_d, a16)
         agreement = round(float((a8 == a16).float().mean().item()), 4)
         del t16
