@@ -303,6 +303,43 @@ def main() -> int:
     torch.cuda.synchronize()
     warm_draft_us = e0.elapsed_time(e1) * 1000.0 / K
 
+    # Untimed context: isolated single calls (the device idle before each),
+    # and the read rate a plain streaming read reaches over buffers of each
+    # call's weight size (the practical ceiling of these HBM-bound calls).
+    def one_call_us(fn, reps=15):
+        out = []
+        for _ in range(reps):
+            torch.cuda.synchronize()
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            out.append(e0.elapsed_time(e1) * 1000.0)
+        return round(statistics.median(out), 2)
+
+    single_draft_us = one_call_us(lambda: draft_call(0, tables[0]))
+    single_verify_us = one_call_us(lambda: verify_call(drafts_d))
+    sink = torch.empty(mtp.MTP_STREAM_SINK_WORDS, dtype=torch.int32, device=dev)
+
+    def stream_gbps(bufs, nbytes, reps):
+        # untimed reads first: the single calls above left the device idle
+        for i in range(reps):
+            mtp.mtp_stream_read(bufs[i % len(bufs)], sink, nbytes)
+        e0.record(stream)
+        for i in range(reps):
+            mtp.mtp_stream_read(bufs[i % len(bufs)], sink, nbytes)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return round(nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+
+    tab_bufs = [t[0] if isinstance(t, tuple) else t for t in tables]
+    tab_bytes = min(b.numel() * b.element_size() for b in tab_bufs)
+    head_bytes = head_v.numel() * head_v.element_size()
+    stream_read = {"draft_table_bytes": int(tab_bytes),
+                   "draft_table_GBps": stream_gbps(tab_bufs, tab_bytes, 60),
+                   "head_bytes": int(head_bytes),
+                   "head_GBps": stream_gbps([head_v], head_bytes, 20)}
+
     agreement = None
     if fp8:
         # how often the fp8 draft picks the bf16 draft's token (512 hidden rows
@@ -365,6 +402,10 @@ def main() -> int:
                 "traffic": traffic, "kernel": dom_name,
                 "algorithmic_bytes_per_launch": int(dom_bytes)}
 
+    dom_stream = stream_read["head_GBps"] if dom_name == "verify" else \
+        stream_read["draft_table_GBps"]
+    stream_read["dominant_kernel_frac_of_stream_read"] = round(achieved / dom_stream, 4)
+
     result = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -394,6 +435,8 @@ def main() -> int:
             "graph_step_us_mean": round(statistics.mean(graph_step_ms) * 1000.0, 2)
             if graph_step_ms else None,
             "draft_same_table_us": round(warm_draft_us, 2),
+            "single_call_us": {"draft": single_draft_us, "verify": single_verify_us},
+            "stream_read": stream_read,
             "fp8_draft_agrees_with_bf16": agreement,
             "setup_s": round(setup_s, 1),
         },

@@ -391,6 +391,26 @@ mtp_status mtp_graph_launch(const mtp_graph *graph, hipStream_t stream);
 /* Frees the graph (NULL is ignored). Call after its last replay finished. */
 void mtp_graph_destroy(mtp_graph *graph);
 
+/*
+ * Streaming-read reference (a measurement aid, not a step of the method).
+ *
+ * Reads `bytes` bytes at `buf` once, as a plain stream of non-temporal 16-byte
+ * loads, and writes one XOR word per wave into `sink` (at most
+ * MTP_STREAM_SINK_WORDS words; their values carry no meaning). Timing it
+ * over a buffer of a call's size gives the read rate this device actually
+ * reaches, against which the draft and verify calls, whose cost is the bytes
+ * of the rows they read, are judged. [Qwen3.8 Flash dual-Spark tuning log,
+ * section "read one fewer big table": the draft's time follows the size of
+ * the table it reads.]
+ *
+ * buf: device, 16-byte aligned; bytes: > 0, a multiple of 16. sink: device
+ * uint32 [MTP_STREAM_SINK_WORDS], 4-byte aligned. Errors: MTP_ERR_INVALID_ARG
+ * for a null pointer, misalignment or a bad size; MTP_ERR_HIP for a launch
+ * failure. Asynchronous on `stream`; allocates nothing.
+ */
+#define MTP_STREAM_SINK_WORDS 8192
+mtp_status mtp_stream_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -536,6 +536,19 @@ mtp_status mtp_draft_argmax_tiled_fp8(const mtp_bf16 *hidden, int M, int H, cons
                                         ws, ws_bytes, stream, nullptr);
 }
 
+static_assert(MTP_STREAM_SINK_WORDS == mtp::kStreamSinkWords, "sink size");
+
+mtp_status mtp_stream_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t stream) {
+  if (!buf || !sink || bytes == 0 || bytes % 16 != 0) return MTP_ERR_INVALID_ARG;
+  if (!aligned(buf, 16) || !aligned(sink, 4)) return MTP_ERR_INVALID_ARG;
+  int cus = 0;
+  hipError_t e = current_cus(&cus);
+  if (e != hipSuccess) return hip_fail(e);
+  e = mtp::launch_stream_read(buf, bytes, sink, cus, stream);
+  if (e != hipSuccess) return hip_fail(e);
+  return MTP_OK;
+}
+
 struct mtp_graph {
   hipGraph_t graph;
   hipGraphExec_t exec;

@@ -95,4 +95,9 @@ hipError_t launch_pack_fp8(const void *head, int64_t V, int H, const int32_t *id
                            void *q, float *scales, int num_cus, hipStream_t stream);
 hipError_t launch_fill_zero(void *ws, size_t bytes, hipStream_t stream);
 
+// Streaming-read reference (probe.hip): sink words written per call, at most.
+constexpr int kStreamSinkWords = 8192;
+hipError_t launch_stream_read(const void *buf, size_t bytes, uint32_t *sink, int cus,
+                              hipStream_t stream);
+
 }  // namespace mtp

@@ -95,6 +95,7 @@ def _load() -> ctypes.CDLL:
         "mtp_pack_tiled_fp8": ([P, I64, I, P, I64, P, S, P, P], I),
         "mtp_draft_argmax_tiled_fp8": ([P, I, I, P, P, P, I64, P, P, P, S, P], I),
         "mtp_draft_argmax_tiled_fp8_cfg": ([P, I, I, P, P, P, I64, P, P, P, S, P, P], I),
+        "mtp_stream_read": ([P, S, P, P], I),
         "mtp_graph_begin": ([P], I),
         "mtp_graph_end": ([P, ctypes.POINTER(P)], I),
         "mtp_graph_launch": ([P, P], I),
@@ -486,6 +487,25 @@ def mtp_draft_argmax_tiled_fp8(hidden, table_q, scales, C: int, ids, out_ids, ou
         _ptr(out_logit, "out_logit", (torch.float32,), allow_none=True),
         _ptr(ws, "ws", (torch.int64, torch.uint8, torch.int32)), ws.numel() * ws.element_size(),
         _stream(stream), ctypes.byref(cfg)), "mtp_draft_argmax_tiled_fp8")
+
+
+# ---- streaming-read reference ----------------------------------------------
+
+MTP_STREAM_SINK_WORDS = 8192
+
+
+def mtp_stream_read(buf, sink, nbytes: Optional[int] = None, stream=None) -> None:
+    """One plain streaming read of buf's first nbytes bytes (all of it by
+    default); sink: int32/uint8 device tensor of MTP_STREAM_SINK_WORDS words."""
+    torch = _torch()
+    n = buf.numel() * buf.element_size() if nbytes is None else int(nbytes)
+    if n > buf.numel() * buf.element_size():
+        raise ValueError("nbytes exceeds the buffer")
+    if sink.numel() * sink.element_size() < 4 * MTP_STREAM_SINK_WORDS:
+        raise ValueError("sink too small")
+    _check(lib.mtp_stream_read(_ptr(buf, "buf", (buf.dtype,)), n,
+                               _ptr(sink, "sink", (torch.int32, torch.uint8)), _stream(stream)),
+           "mtp_stream_read")
 
 
 # ---- graph-captured MTP step ----------------------------------------------

@@ -241,3 +241,13 @@ def test_tiled_fp8_entry_points_reject_bad_arguments():
     c.path = mtp.MTP_PATH_VALU
     assert mtp.lib.mtp_draft_argmax_tiled_fp8_cfg(*dk, ctypes.byref(c)) == \
         mtp.MTP_ERR_UNSUPPORTED
+
+
+def test_stream_read_rejects_bad_arguments():
+    f = mtp.lib.mtp_stream_read
+    assert f(None, 1024, FAKE, None) == INVALID
+    assert f(FAKE, 1024, None, None) == INVALID
+    assert f(FAKE, 0, FAKE, None) == INVALID
+    assert f(FAKE, 1000, FAKE, None) == INVALID          # not a multiple of 16
+    assert f(P(0x10008), 1024, FAKE, None) == INVALID    # buffer not 16-byte aligned
+    assert f(FAKE, 1024, P(0x10002), None) == INVALID    # sink not 4-byte aligned
