@@ -37,9 +37,13 @@
  *     be any int32.
  *   - Workspace: a caller-owned device buffer of at least the queried size,
  *     8-byte aligned, zeroed once with mtp_workspace_init(). Every call
- *     leaves it zeroed again, so it needs no per-call clearing. Calls that
- *     share a workspace must be ordered on one stream; calls with distinct
- *     workspaces may run concurrently from any threads.
+ *     leaves its counters zeroed again, so it needs no per-call clearing.
+ *     With more than 128 hidden rows the query also covers a staging area
+ *     past the counters of the largest call (MTP_MAX_ROWS rows), where the
+ *     tiled calls pack the hidden block in fragment order: each such call
+ *     writes it before reading it and leaves it as scratch, and no call
+ *     keeps counters there. Calls that share a workspace must be ordered on one stream;
+ *     calls with distinct workspaces may run concurrently from any threads.
  *   - Outputs are bit-identical for identical inputs, whatever the launch
  *     configuration.
  */
@@ -97,8 +101,11 @@ int mtp_version(void);
 mtp_status mtp_validate_ids(const int32_t *ids_host, int64_t C, int64_t V);
 
 /* Bytes of workspace needed by mtp_draft_argmax for M hidden rows, and by
- * mtp_verify_accept for B sequences with k drafts each. 0 for arguments out
- * of range. */
+ * mtp_verify_accept for B sequences with k drafts each (the same sizes serve
+ * every variant of these calls; with M or B*(k+1) above 128 they include the
+ * tiled calls' staging area of about M*H*2 bytes, placed past 33 KiB of
+ * counters). 0 for arguments out of range. A tiled call with more than 128 hidden rows returns
+ * MTP_ERR_WORKSPACE when given less. */
 size_t mtp_draft_workspace_bytes(int M, int64_t C, int H);
 size_t mtp_verify_workspace_bytes(int B, int k, int64_t V, int H);
 

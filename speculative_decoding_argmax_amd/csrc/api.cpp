@@ -51,6 +51,24 @@ size_t rows_workspace_bytes(int64_t M) {
   return mtp::kWsHeader + ((keys + 255) / 256) * 256;
 }
 
+// Tiled calls with more than 128 hidden rows also stage the packed hidden
+// block in the workspace. It starts past the largest counter region any call
+// can use (MTP_MAX_ROWS keys), so the scratch it leaves behind never lies
+// where another call on the same workspace expects zeroed keys; the start is
+// rounded up to 256 bytes (the workspace itself is only 8-byte aligned,
+// hence the slack).
+size_t stage_offset() { return rows_workspace_bytes(MTP_MAX_ROWS); }
+
+size_t call_workspace_bytes(int64_t M, int H) {
+  const size_t b = mtp::ring_stage_bytes((int)M, H);
+  return b ? stage_offset() + b + 256 : rows_workspace_bytes(M);
+}
+
+void *stage_ptr(void *ws) {
+  const uintptr_t p = (uintptr_t)ws + stage_offset();
+  return (void *)((p + 255) & ~(uintptr_t)255);
+}
+
 bool shape_ok(int64_t M, int64_t N, int64_t H) {
   return M >= 1 && M <= MTP_MAX_ROWS && N >= 1 && N <= INT32_MAX && H >= 8 &&
          H <= MTP_MAX_HIDDEN && H % 8 == 0;
@@ -123,8 +141,11 @@ mtp_status run_rows(const mtp_bf16 *X, int M, int H, const mtp_bf16 *W, int64_t 
 
 // Score M hidden rows against N rows of a tiled table.
 mtp_status run_rows_tiled(const mtp_bf16 *X, int M, int H, const void *WT, int64_t N,
-                          mtp::RowSink sink, hipStream_t stream, const mtp_config *cfg) {
+                          mtp::RowSink sink, void *ws, size_t ws_bytes, hipStream_t stream,
+                          const mtp_config *cfg) {
   if (cfg && cfg->path == MTP_PATH_VALU) return MTP_ERR_UNSUPPORTED;
+  const bool stage = mtp::ring_stage_bytes(M, H) != 0;
+  if (ws_bytes < call_workspace_bytes(M, H)) return MTP_ERR_WORKSPACE;
   int cus = 0;
   hipError_t e = current_cus(&cus);
   if (e != hipSuccess) return hip_fail(e);
@@ -139,6 +160,7 @@ mtp_status run_rows_tiled(const mtp_bf16 *X, int M, int H, const void *WT, int64
   L.max_blocks_x = per_cu * cus;
   L.sink = sink;
   L.stream = stream;
+  L.stage = stage ? stage_ptr(ws) : nullptr;
   e = mtp::launch_dma(L, mtp::dma_nb_for(M));
   if (e != hipSuccess) return hip_fail(e);
   return MTP_OK;
@@ -249,14 +271,14 @@ mtp_status mtp_validate_ids(const int32_t *ids_host, int64_t C, int64_t V) {
 
 size_t mtp_draft_workspace_bytes(int M, int64_t C, int H) {
   if (!shape_ok(M, C, H)) return 0;
-  return rows_workspace_bytes(M);
+  return call_workspace_bytes(M, H);
 }
 
 size_t mtp_verify_workspace_bytes(int B, int k, int64_t V, int H) {
   if (B < 1 || k < 0 || k > MTP_MAX_K) return 0;
   const int64_t M = (int64_t)B * (k + 1);
   if (!shape_ok(M, V, H)) return 0;
-  return rows_workspace_bytes(M);
+  return call_workspace_bytes(M, H);
 }
 
 mtp_status mtp_workspace_init(void *ws, size_t ws_bytes, hipStream_t stream) {
@@ -349,7 +371,7 @@ mtp_status mtp_draft_argmax_tiled_cfg(const mtp_bf16 *hidden, int M, int H,
                                    ws_bytes, cfg);
   if (st != MTP_OK) return st;
   return run_rows_tiled(hidden, M, H, table_tiled, C, draft_sink(ws, ids, out_ids, out_logit, M),
-                        stream, cfg);
+                        ws, ws_bytes, stream, cfg);
 }
 
 mtp_status mtp_draft_argmax_tiled(const mtp_bf16 *hidden, int M, int H, const void *table_tiled,
@@ -371,7 +393,8 @@ mtp_status mtp_verify_accept_tiled_cfg(const mtp_bf16 *hidden, int B, int k, int
   if (st != MTP_OK) return st;
   return run_rows_tiled(
       hidden, B * (k + 1), H, head_tiled, V,
-      verify_sink(ws, B, k, draft, out_argmax, out_logit, out_accept, out_tokens), stream, cfg);
+      verify_sink(ws, B, k, draft, out_argmax, out_logit, out_accept, out_tokens), ws, ws_bytes,
+      stream, cfg);
 }
 
 mtp_status mtp_verify_accept_tiled(const mtp_bf16 *hidden, int B, int k, int H,

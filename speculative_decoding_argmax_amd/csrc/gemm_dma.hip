@@ -44,6 +44,7 @@ namespace mtp {
 
 typedef __bf16 bf16x8_dma_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_dma_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_ring_t __attribute__((ext_vector_type(4)));
 
 #define MTP_LDS(p) ((__attribute__((address_space(3))) void *)(p))
 
@@ -319,6 +320,249 @@ __global__ void __launch_bounds__(WV * 64)
   finish_rows(sink, f_val, f_row, m0, mcount);
 }
 
+
+// ---------------------------------------------------------------------------
+// Wide verify blocks (more than 128 hidden rows per call): weights through a
+// per-wave register ring, hidden fragments through LDS.
+//
+// With 160 hidden rows the kernel above spends its LDS on three slots of
+// 42 KiB (32 KiB of weights, 10 KiB of hidden fragments), so only two chunks
+// of weights are in flight per CU, too few to cover the memory latency at
+// this chunk rate. But each wave multiplies only its own 16-row blocks: the
+// weight fragments need no sharing, so each wave streams them straight into
+// registers (one coalesced 1 KiB non-temporal load per fragment), D - 1
+// chunks ahead, and the LDS holds only the hidden fragments that all waves
+// read. The hidden block is first packed into fragment order by
+// pack_hidden_frags (zero rows past M, zero columns past H), so that each
+// hidden copy is one contiguous 1 KiB buffer load with a loop-invariant lane
+// offset. Per chunk each wave issues RW * KS weight loads, then waits until
+// chunk it's hidden fragments have landed (a fixed count of younger loads),
+// meets the other waves at the barrier, and issues the hidden copies of
+// chunk it + D - 1 into the slot freed by chunk it - 1.
+//
+// The hand-counted wait assumes the issue order A(it + D - 1), barrier,
+// B(it + D - 1) in every body: the compiler fences after each group keep
+// it, and the weight pointer is not __restrict__, because loads through a
+// restrict pointer count as invariant and may move across the fences. The
+// loop always runs whole trips of D bodies (a body skipped on some path would
+// make the compiler's own register waits as strict as that path's count):
+// the up to D - 1 chunks past the end are multiplied into a tile that is
+// never evaluated. Summation order per logit is that of the kernel above
+// (steps ascending, MFMA in-step order), so results are bit-identical to it.
+
+// hidden [M][nch] (16-byte chunks) -> fragments (st, b), 1 KiB each, ordered
+// st * nbt + b: lane j + 16 g holds hidden row 16 b + j, chunk 4 st + g.
+__global__ void __launch_bounds__(256)
+    pack_hidden_frags(const uint4 *__restrict__ X, int M, int nch, int S, int nbt,
+                      uint4 *__restrict__ out) {
+  const int64_t total = (int64_t)S * nbt * kWave;
+  const int64_t step = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += step) {
+    const int lane = (int)(e & (kWave - 1));
+    const int64_t fr = e / kWave;
+    const int b = (int)(fr % nbt);
+    const int st = (int)(fr / nbt);
+    const int row = b * 16 + (lane & 15);
+    const int col = st * 4 + (lane >> 4);
+    out[e] = (row < M && col < nch) ? X[(int64_t)row * nch + col] : make_uint4(0u, 0u, 0u, 0u);
+  }
+}
+
+template <int NB, int RW, int KS, int D, int WV, int CP>
+__global__ void __launch_bounds__(WV * 64)
+    gemm_argmax_ring(const uint4 *__restrict__ XP, const uint4 *WT, int M, int N, int S,
+                     int nbt, RowSink sink) {
+  constexpr int RBT = WV * RW;
+  constexpr int TV = RBT * 16;
+  constexpr int BF = KS * NB;                   // hidden fragments per chunk
+  constexpr int PWB = (BF + WV - 1) / WV;       // hidden copies per wave per chunk
+  constexpr int AL = RW * KS;                   // weight loads per wave per chunk
+  static_assert(D >= 3 && D <= 4, "ring depth");
+  static_assert(RBT % 4 == 0, "whole 64-row tiles");
+  __shared__ uint4 bs0[BF * 64];
+  __shared__ uint4 bs1[BF * 64];
+  __shared__ uint4 bs2[BF * 64];
+  __shared__ uint4 bs3[D > 3 ? BF * 64 : 1];
+  __shared__ float red_v[WV * NB * 64];
+  __shared__ int red_i[WV * NB * 64];
+  __shared__ float f_val[NB * 16];
+  __shared__ int64_t f_row[NB * 16];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int g = lane >> 4;
+  const int m0 = blockIdx.y * NB * 16;
+  const int gdx = gridDim.x;
+  const int bx = blockIdx.x;
+  const int by = blockIdx.y;
+  const int nchunks = S / KS;
+  const int ntiles = (N + TV - 1) / TV;
+  const int my_tiles = bx < ntiles ? (ntiles - 1 - bx) / gdx + 1 : 0;
+  const int total = my_tiles * nchunks;
+  const int nrb = ((N + 63) / 64) * 4;
+
+  auto bslot = [&](auto tag) __attribute__((always_inline)) -> uint4 * {
+    constexpr int SL = decltype(tag)::value;
+    if constexpr (SL == 0) return bs0;
+    else if constexpr (SL == 1) return bs1;
+    else if constexpr (SL == 2) return bs2;
+    else return bs3;
+  };
+
+  uint4 ar[D][KS][RW];
+  int a_t = bx, a_c = 0;
+  auto issue_a = [&](auto tag) __attribute__((always_inline)) {
+    constexpr int SL = decltype(tag)::value;
+    const int tile = a_t;
+    const int c = a_c;
+    if (++a_c == nchunks) {
+      a_c = 0;
+      a_t += gdx;
+    }
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+#pragma unroll
+      for (int rw = 0; rw < RW; ++rw) {
+        int rb = tile * RBT + wave * RW + rw;
+        rb = rb < nrb ? rb : nrb - 1;            // past the table: valid, never reported
+        const uint4 *src =
+            WT + (((int64_t)(rb >> 2) * S + c * KS + s) * 4 + (rb & 3)) * kWave + lane;
+        const u32x4_ring_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_ring_t *>(src));
+        ar[SL][s][rw] = make_uint4(v.x, v.y, v.z, v.w);
+      }
+    }
+  };
+  int b_c = 0;
+  auto issue_b = [&](auto tag) __attribute__((always_inline)) {
+    uint4 *base = bslot(tag);
+    const int c = b_c;
+    if (++b_c == nchunks) b_c = 0;
+#pragma unroll
+    for (int q = 0; q < PWB; ++q) {
+      int f = wave + WV * q;
+      f = f < BF ? f : BF - 1;                   // surplus copies repeat the last fragment
+      const int s = f / NB;
+      const int nb = f - s * NB;
+      const uint4 *fr = XP + ((int64_t)(c * KS + s) * nbt + by * NB + nb) * kWave;
+      __amdgpu_buffer_rsrc_t r =
+          __builtin_amdgcn_make_buffer_rsrc((void *)fr, (short)0, 1024, 0x00020000);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, MTP_LDS(base + f * kWave), 16, lane * 16, 0, 0,
+                                               0);
+    }
+  };
+
+  f32x4_dma_t acc[RW][NB];
+#pragma unroll
+  for (int rw = 0; rw < RW; ++rw)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[rw][nb] = f32x4_dma_t{0.f, 0.f, 0.f, 0.f};
+  float bv[NB];
+  int bi[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    bv[nb] = 0.f;
+    bi[nb] = -1;
+  }
+
+  // prologue: chunks 0 .. D - 2, in the order A B A B ...
+  issue_a(std::integral_constant<int, 0>{});
+  asm volatile("" ::: "memory");
+  issue_b(std::integral_constant<int, 0>{});
+  asm volatile("" ::: "memory");
+  issue_a(std::integral_constant<int, 1>{});
+  asm volatile("" ::: "memory");
+  issue_b(std::integral_constant<int, 1>{});
+  asm volatile("" ::: "memory");
+  if constexpr (D > 3) {
+    issue_a(std::integral_constant<int, 2>{});
+    asm volatile("" ::: "memory");
+    issue_b(std::integral_constant<int, 2>{});
+    asm volatile("" ::: "memory");
+  }
+  int cur_t = bx, cur_c = 0;
+
+  auto body = [&](auto tag) __attribute__((always_inline)) {
+    constexpr int SL = decltype(tag)::value;
+    constexpr int NX = (SL + D - 1) % D;
+    issue_a(std::integral_constant<int, NX>{});
+    // younger than chunk it's hidden copies: D - 2 whole chunks, then this
+    // body's weight loads (the weights of chunk it are older still)
+    wait_vmcnt<(D - 2) * (AL + PWB) + AL>();
+    barrier_no_fence();
+    issue_b(std::integral_constant<int, NX>{});
+    asm volatile("" ::: "memory");
+    const uint4 *Bf = bslot(tag);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const uint4 b = Bf[(s * NB + nb) * kWave + lane];
+#pragma unroll
+        for (int rw = 0; rw < RW; ++rw) acc[rw][nb] = mfma16_dma(ar[SL][s][rw], b, acc[rw][nb]);
+      }
+    }
+    if (++cur_c == nchunks) {
+      const int tile = cur_t;
+      cur_c = 0;
+      cur_t += gdx;
+      const int vbase = tile * TV + wave * RW * 16 + 4 * g;
+#pragma unroll
+      for (int rw = 0; rw < RW; ++rw) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int v = vbase + rw * 16 + r;
+            const float z = acc[rw][nb][r];
+            if (v < N && better_row(z, v, bv[nb], bi[nb])) {
+              bv[nb] = z;
+              bi[nb] = v;
+            }
+          }
+          acc[rw][nb] = f32x4_dma_t{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+    }
+  };
+
+  for (int it = 0; it < total; it += D) {
+    body(std::integral_constant<int, 0>{});
+    body(std::integral_constant<int, 1>{});
+    body(std::integral_constant<int, 2>{});
+    if constexpr (D > 3) body(std::integral_constant<int, 3>{});
+  }
+  wait_vmcnt<0>();
+  __syncthreads();
+
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    red_v[(wave * NB + nb) * kWave + lane] = bv[nb];
+    red_i[(wave * NB + nb) * kWave + lane] = bi[nb];
+  }
+  __syncthreads();
+  if (tid < NB * 16) {
+    const int nb = tid >> 4;
+    const int jj = tid & 15;
+    float v = 0.f;
+    int ix = -1;
+    for (int w = 0; w < WV; ++w) {
+      for (int gg = 0; gg < 4; ++gg) {
+        const int o = (w * NB + nb) * kWave + jj + 16 * gg;
+        if (red_i[o] >= 0 && better_row(red_v[o], red_i[o], v, ix)) {
+          v = red_v[o];
+          ix = red_i[o];
+        }
+      }
+    }
+    f_val[tid] = v;
+    f_row[tid] = ix;
+  }
+  __syncthreads();
+  const int mcount = M - m0 < NB * 16 ? M - m0 : NB * 16;
+  finish_rows(sink, f_val, f_row, m0, mcount);
+}
+
 // Padded sizes of the tiled layout.
 int64_t tiled_rows(int64_t rows) { return (rows + 63) / 64 * 64; }
 int tiled_cols(int H) { return (H + 127) / 128 * 128; }
@@ -349,8 +593,37 @@ int dma_nb_for(int M) {
 // Instantiated shapes (measured on MI355X at the workload shapes; none spills
 // registers, every one fits the 160 KiB LDS). Non-temporal weight copies
 // (CP = 2) stream 6.7 TB/s where default-policy copies reach 6.0 TB/s.
+template <int NB, int RW, int KS, int D, int WV, int CP>
+static hipError_t launch_ring_cfg(const DmaLaunch &L) {
+  constexpr int TV = WV * RW * 16;
+  const int64_t ntiles = (L.N + TV - 1) / TV;
+  const int gx = (int)(ntiles < L.max_blocks_x ? ntiles : L.max_blocks_x);
+  const int gy = (L.M + NB * 16 - 1) / (NB * 16);
+  const int nbt = gy * NB;
+  const int64_t elems = (int64_t)L.S * nbt * kWave;
+  const int pblocks = (int)(elems / 256 + 1 < 1024 ? elems / 256 + 1 : 1024);
+  hipLaunchKernelGGL(pack_hidden_frags, dim3(pblocks), dim3(256), 0, L.stream,
+                     (const uint4 *)L.X, L.M, L.nch, L.S, nbt, (uint4 *)L.stage);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((gemm_argmax_ring<NB, RW, KS, D, WV, CP>), dim3(gx, gy), dim3(WV * 64), 0,
+                     L.stream, (const uint4 *)L.stage, (const uint4 *)L.WT, L.M, (int)L.N, L.S,
+                     nbt, L.sink);
+  return hipGetLastError();
+}
+
+// Staging bytes of the wide passes (the packed hidden block), 0 for M <= 128.
+size_t ring_stage_bytes(int M, int H) {
+  if (dma_nb_for(M) != 10) return 0;
+  const size_t nbt = (size_t)10 * ((M + 159) / 160);
+  return (size_t)(tiled_cols(H) / 32) * nbt * 1024;
+}
+
 hipError_t launch_dma(const DmaLaunch &L, int nb) {
   constexpr int NT = 2;
+  // wide passes: the register-ring kernel (M = 160 at H = 5,120 on MI355X:
+  // 415 us against 489 us, bit-identical results) when staging is given
+  if (nb == 10 && L.stage) return launch_ring_cfg<10, 4, 1, 3, 8, NT>(L);
   switch (nb) {
     case 1: return launch_dma_cfg<1, 1, 2, 4, 8, NT>(L);
     case 2: return launch_dma_cfg<2, 2, 2, 4, 8, NT>(L);

@@ -58,12 +58,14 @@ struct DmaLaunch {
   RowSink sink;
   hipStream_t stream;
   const float *scales = nullptr;  // fp8 tables: row scales [N]
+  void *stage = nullptr;          // wide passes: packed hidden block (ring_stage_bytes)
 };
 
 int64_t tiled_rows(int64_t rows);
 int tiled_cols(int H);
 int dma_nb_for(int M);
 hipError_t launch_dma(const DmaLaunch &L, int nb);
+size_t ring_stage_bytes(int M, int H);
 int dma_nb_for_fp8(int M);
 hipError_t launch_dma_fp8(const DmaLaunch &L, int nb);
 hipError_t launch_pack_tiled_fp8(const void *head, int64_t V, int H, const int32_t *ids,

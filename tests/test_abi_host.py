@@ -41,7 +41,10 @@ def test_workspace_sizes():
     assert mtp.mtp_draft_workspace_bytes(1, 65536, 2048) == 512
     assert mtp.mtp_draft_workspace_bytes(32, 65536, 5120) == 512
     assert mtp.mtp_draft_workspace_bytes(33, 65536, 5120) == 768
-    assert mtp.mtp_verify_workspace_bytes(32, 4, 248320, 5120) == 256 + 1280
+    # 160 rows: the counters of the largest call, then the tiled calls'
+    # staging area (see below)
+    assert mtp.mtp_verify_workspace_bytes(32, 4, 248320, 5120) == \
+        256 + 4096 * 8 + 160 * 10 * 1024 + 256
     assert mtp.mtp_verify_workspace_bytes(1, 0, 10, 8) == 512
     for bad in ((0, 10, 8), (1, 0, 8), (1, 10, 12), (1, 10, 4), (4097, 10, 8), (1, 10, 16392)):
         assert mtp.mtp_draft_workspace_bytes(*bad) == 0, bad
@@ -251,3 +254,26 @@ def test_stream_read_rejects_bad_arguments():
     assert f(FAKE, 1000, FAKE, None) == INVALID          # not a multiple of 16
     assert f(P(0x10008), 1024, FAKE, None) == INVALID    # buffer not 16-byte aligned
     assert f(FAKE, 1024, P(0x10002), None) == INVALID    # sink not 4-byte aligned
+
+
+def test_wide_tiled_calls_need_the_staging_area():
+    """Above 128 hidden rows the workspace query adds the packed-hidden
+    staging area (S steps x 10 row blocks x 1 KiB per 160-row pass, plus
+    256 bytes of alignment slack) past the counters of the largest possible
+    call, and a tiled call given only the counters' size is refused before
+    anything is enqueued."""
+    counters = lambda M: 256 + -(-M * 8 // 256) * 256
+    assert mtp.mtp_draft_workspace_bytes(128, 1000, 5120) == counters(128)
+    base = counters(4096)
+    stage160 = (5120 // 32) * 10 * 1024 + 256
+    assert mtp.mtp_draft_workspace_bytes(160, 1000, 5120) == base + stage160
+    assert mtp.mtp_verify_workspace_bytes(32, 4, 248320, 5120) == base + stage160
+    # 161 rows: two 160-row passes; H = 1000 pads to 1024 columns (32 steps)
+    assert mtp.mtp_draft_workspace_bytes(161, 1000, 1000) == base + 32 * 20 * 1024 + 256
+    assert mtp.mtp_draft_workspace_bytes(4096, 1000, 64) == base + 4 * 260 * 1024 + 256
+    d = mtp.lib.mtp_draft_argmax_tiled
+    assert d(FAKE, 160, 5120, FAKE, None, 1000, FAKE, None, FAKE, counters(160), None) == \
+        mtp.MTP_ERR_WORKSPACE
+    v = mtp.lib.mtp_verify_accept_tiled
+    assert v(FAKE, 32, 4, 5120, FAKE, 248320, FAKE, FAKE, None, FAKE, FAKE, FAKE, counters(160),
+             None) == mtp.MTP_ERR_WORKSPACE

@@ -71,6 +71,8 @@ TILED_SHAPES = [  # (M, N, H)
     (1, 1, 8), (1, 1000, 8), (3, 4097, 256), (8, 3001, 4096), (2, 999, 5120), (16, 1025, 640),
     (17, 333, 1032), (32, 5000, 1024), (48, 2049, 4096), (64, 4000, 2048), (100, 700, 512),
     (160, 1111, 5120), (161, 300, 256), (1, 257, 16384), (90, 1500, 1024), (130, 2100, 768),
+    # more than 128 rows: the register-ring kernel over the packed hidden block
+    (129, 64, 8), (144, 70, 1000), (200, 513, 2056), (320, 257, 136), (4096, 65, 64),
 ]
 
 
@@ -88,7 +90,7 @@ def test_tiled_draft_exact_grid(torch, mtp, M, N, H, with_ids):
 
 
 @pytest.mark.parametrize("B,k,H,V", [(1, 3, 256, 4096), (8, 3, 4096, 20000), (32, 4, 5120, 3000),
-                                     (1, 0, 2048, 777), (40, 3, 1024, 999)])
+                                     (1, 0, 2048, 777), (40, 3, 1024, 999), (64, 3, 1000, 1234)])
 def test_tiled_verify_exact_grid(torch, mtp, B, k, H, V):
     seed = 91 + B + k + H + V
     hv = wl.exact_grid_bf16((B * (k + 1), H), seed, 1)
@@ -133,7 +135,7 @@ def test_tiled_duplicate_rows_tie_to_lowest_id(torch, mtp, M):
     check_rows(g_ids, g_logit, orc, h, W, None, strict=strict)
 
 
-@pytest.mark.parametrize("M", [4, 33])
+@pytest.mark.parametrize("M", [4, 33, 150])
 def test_tiled_determinism_across_grids(torch, mtp, M):
     V, H = 50000, 2048
     W = wl.head_weights(V, H, 9)
@@ -160,3 +162,23 @@ def test_tiled_workspace_left_zeroed(torch, mtp):
         mtp.mtp_draft_argmax_tiled(dev_bf16(wl.hidden_states(M, H, 3)), t, V, None, out, ws=ws)
         torch.cuda.synchronize()
         assert int(ws.abs().sum()) == 0
+
+
+def test_tiled_wide_calls_share_one_workspace(torch, mtp):
+    """The staging area of the wide calls is scratch that never overlaps any
+    call's counters: one workspace, sized for the widest call, serves calls
+    of 320, 140, 200 and 40 rows in turn (a narrower call's staging data
+    must not sit where a wider call's keys go); each matches the oracle bit
+    for bit and leaves its counters zeroed."""
+    N, H = 900, 1032
+    w = wl.exact_grid_bf16((N, H), 77, 2)
+    t = tile_on_gpu(torch, mtp, w)
+    ws = mtp.alloc_workspace(mtp.mtp_draft_workspace_bytes(320, N, H))
+    for M in (320, 140, 200, 40):
+        x = wl.exact_grid_bf16((M, H), 77 + M, 1)
+        g_ids, g_logit = tiled_draft(torch, mtp, x, t, N, None, ws=ws)
+        exact_logit_match(g_ids, g_logit, x, w, None)
+        # every counter a call of up to 4,096 rows could use (256-byte
+        # header, one 8-byte key per row) is left zeroed; the staging area
+        # past them is scratch
+        assert int(ws[:(256 + 4096 * 8) // 8].abs().sum()) == 0
