@@ -83,14 +83,16 @@ def kernel_source_hash(path: str) -> str:
 
 
 def measured_traffic(kernel: str, workload: str, path: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary of
-    this kernel and workload, if it was taken from the current sources."""
-    p = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_pmc.txt")
+    """HBM bytes per launch of the verify or draft call, from the committed
+    rocprofv3 counter summary of the workload, if it was taken from the
+    current sources."""
+    p = os.path.join(ROOT, "profiles", f"verify_{workload}_pmc.txt")
     if not os.path.exists(p):
         return None
     text = open(p).read()
+    key = "hbm_bytes_per_launch" if kernel == "verify" else f"{kernel}_hbm_bytes_per_launch"
     m_hash = re.search(r"^kernel_source_hash:\s*(\S+)", text, re.M)
-    m_bytes = re.search(r"^hbm_bytes_per_launch:\s*([0-9.eE+]+)", text, re.M)
+    m_bytes = re.search(rf"^{key}:\s*([0-9.eE+]+)", text, re.M)
     if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash(path):
         return None
     return float(m_bytes.group(1))
