@@ -451,6 +451,18 @@ def main() -> int:
     return 0
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (first processor in /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wk, head, ids, hiddens, hv, drafts, budget_s):
     """The CPU oracle on the same step: its draft calls and verify call,
     repeated until the time budget is spent (at least once)."""
@@ -468,7 +480,7 @@ def cpu_baseline(wk, head, ids, hiddens, hv, drafts, budget_s):
             break
     step_s = statistics.median(times)
     return {"value": round((wk.draft_calls + 1) / step_s, 3), "unit": "calls/s",
-            "cores": oracle.threads(), "kind": "oracle",
+            "cores": oracle.threads(), "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"{len(times)} full {wk.name} step(s) ({wk.draft_calls} draft + 1 verify "
                       f"call), median {step_s:.3f} s per step"}
 

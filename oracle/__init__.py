@@ -72,10 +72,20 @@ class _Lib:
         lib.mtp_oracle_fp8_row_exponent.argtypes = [P, I64, P]
         lib.mtp_oracle_quantize_fp8.argtypes = [P, I64, I64, P, I64, P, P]
         lib.mtp_oracle_fp8_argmax.argtypes = [P, I64, P, P, P, I64, I64, P, P, P, P, P]
+        lib.mtp_oracle_e2m1_value.argtypes = [ctypes.c_uint8]
+        lib.mtp_oracle_e2m1_value.restype = ctypes.c_double
+        lib.mtp_oracle_e2m1_round.argtypes = [ctypes.c_double]
+        lib.mtp_oracle_e2m1_round.restype = ctypes.c_uint8
+        lib.mtp_oracle_e2m1_round_array.argtypes = [P, I64, P]
+        lib.mtp_oracle_mx_block_exponent.argtypes = [P, I64, P]
+        lib.mtp_oracle_quantize_mxfp4.argtypes = [P, I64, I64, P, I64, P, P]
+        lib.mtp_oracle_mxfp4_argmax.argtypes = [P, I64, P, P, P, I64, I64, P, P, P, P, P]
         for f in ("mtp_oracle_logits", "mtp_oracle_pair_logits", "mtp_oracle_argmax",
                   "mtp_oracle_accept", "mtp_oracle_check_ids", "mtp_oracle_pack",
                   "mtp_oracle_e4m3_round_array", "mtp_oracle_fp8_row_exponent",
-                  "mtp_oracle_quantize_fp8", "mtp_oracle_fp8_argmax"):
+                  "mtp_oracle_quantize_fp8", "mtp_oracle_fp8_argmax",
+                  "mtp_oracle_e2m1_round_array", "mtp_oracle_mx_block_exponent",
+                  "mtp_oracle_quantize_mxfp4", "mtp_oracle_mxfp4_argmax"):
             getattr(lib, f).restype = ctypes.c_int
         self.lib = lib
         self.path = path
@@ -316,4 +326,82 @@ def draft_fp8(h: np.ndarray, q: np.ndarray, exps: np.ndarray,
                                          _p(out["id"]), _p(out["logit"]), _p(out["exact"]),
                                          _p(out["runner_id"]), _p(out["runner_exact"])),
            "fp8_argmax")
+    return out
+
+
+# ---- MXFP4 candidate table --------------------------------------------------
+
+
+def e2m1_value(codes) -> np.ndarray:
+    """Exact values of E2M1 codes (low 4 bits)."""
+    lib = _load()
+    codes = np.asarray(codes, dtype=np.uint8)
+    table = np.array([lib.mtp_oracle_e2m1_value(c) for c in range(16)], dtype=np.float64)
+    return table[codes & 15]
+
+
+def e2m1_round(x) -> np.ndarray:
+    """Nearest E2M1 code of each value (ties to even, saturating at 6)."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(x.shape, dtype=np.uint8)
+    _check(_load().mtp_oracle_e2m1_round_array(_p(x), x.size, _p(out)), "e2m1_round")
+    return out
+
+
+def mx_block_exponent(w_block: np.ndarray) -> int:
+    """Scale exponent of one block of bf16 values (OCP MX rule)."""
+    w = _bf16(np.atleast_1d(w_block))
+    e = np.zeros(1, np.int32)
+    _check(_load().mtp_oracle_mx_block_exponent(_p(w), w.size, _p(e)), "mx_block_exponent")
+    return int(e[0])
+
+
+def quantize_mxfp4(head: np.ndarray, ids: Optional[np.ndarray] = None):
+    """The MXFP4 candidate table of head rows ids (None: every row): packed
+    E2M1 codes [C][H/2] (element 2i in the low nibble) and E8M0 block scales
+    [C][H/32] (code e + 127)."""
+    head = _bf16(head)
+    V, H = head.shape
+    if ids is not None:
+        ids = np.ascontiguousarray(ids, dtype=np.int32)
+    C = V if ids is None else len(ids)
+    q = np.empty((C, H // 2), dtype=np.uint8)
+    scales = np.empty((C, H // 32), dtype=np.uint8)
+    _check(_load().mtp_oracle_quantize_mxfp4(_p(head), V, H, _p(ids), C, _p(q), _p(scales)),
+           "quantize_mxfp4")
+    return q, scales
+
+
+def mxfp4_values(q: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """The table's element values [C][H] (float64): value(code) * 2^(scale - 127)."""
+    q = np.asarray(q, dtype=np.uint8)
+    codes = np.stack([q & 15, q >> 4], axis=-1).reshape(q.shape[0], -1)
+    e = np.repeat(np.asarray(scales, dtype=np.int64) - 127, 32, axis=1)
+    return np.ldexp(e2m1_value(codes), e)
+
+
+def draft_mxfp4(h: np.ndarray, q: np.ndarray, scales: np.ndarray,
+                ids: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+    """Draft over an MXFP4 candidate table: first maximum of the fp32-rounded
+    logits sum_j h[j] * 2^e(j/32) * value(q[n][j]), reported as ids."""
+    x = _bf16(np.atleast_2d(h))
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    M, H = x.shape
+    N = q.shape[0]
+    if q.shape[1] * 2 != H or scales.shape != (N, H // 32):
+        raise ValueError("shapes differ")
+    if ids is not None:
+        ids = np.ascontiguousarray(ids, dtype=np.int32)
+    out = {
+        "id": np.empty(M, np.int32),
+        "logit": np.empty(M, np.float32),
+        "exact": np.empty(M, np.float64),
+        "runner_id": np.empty(M, np.int32),
+        "runner_exact": np.empty(M, np.float64),
+    }
+    _check(_load().mtp_oracle_mxfp4_argmax(_p(x), M, _p(q), _p(scales), _p(ids), N, H,
+                                           _p(out["id"]), _p(out["logit"]), _p(out["exact"]),
+                                           _p(out["runner_id"]), _p(out["runner_exact"])),
+           "mxfp4_argmax")
     return out

@@ -45,6 +45,20 @@
  * j as the E4M3 value nearest to w[j] * 2^-e (ties to the even code). A
  * row's logit is 2^e * sum_j x[j] * value(q[j]), summed as above in double.
  *
+ * MXFP4 candidate table (4-bit rows; the last functions of this file). The
+ * same section names 4-bit float candidate rows for the upstream work; the
+ * pages fix no block size or scale format, and the format taken here is the
+ * OCP microscaling one, MXFP4: elements E2M1 (sign, 2 exponent bits with
+ * bias 1, 1 mantissa bit; exponent field 0 holds 0 and 0.5; magnitudes
+ * 0, 0.5, 1, 1.5, 2, 3, 4, 6; no infinities or NaN), one E8M0 scale 2^e per
+ * block of 32 consecutive elements of a row (code e + 127). The scale follows
+ * the OCP MX rule: e = floor(log2(max |w| over the block)) - 2, clamped to
+ * [-127, 127], e = -127 for an all-zero block; element j is the E2M1 value
+ * nearest to w[j] * 2^-e (ties to the even code, magnitudes past 6 saturate
+ * to 6; a negative value keeps its sign bit even when it rounds to zero).
+ * Two codes share a byte, element 2i in the low nibble. A row's logit is
+ * sum_j x[j] * 2^e(j / 32) * value(q[j]), summed as above in double.
+ *
  * Build: gcc -O2 -fopenmp -ffp-contract=off -shared -fPIC (no fast-math).
  */
 #include <float.h>
@@ -307,6 +321,119 @@ int mtp_oracle_fp8_argmax(const uint16_t *x, int64_t M, const uint8_t *q, const 
   for (int64_t m = 0; m < M && rc == ORC_OK; ++m) {
 #pragma omp parallel for schedule(static)
     for (int64_t n = 0; n < N; ++n) z[n] = dot_fp8(x + m * H, q + n * H, exps[n], H);
+    rc = decide_row(z, N, ids, top_id + m, top_logit + m, top_exact + m, runner_id + m,
+                    runner_exact + m);
+  }
+  free(z);
+  return rc;
+}
+
+/* ---- MXFP4 candidate table ---------------------------------------------- */
+
+/* The value of an E2M1 code (low 4 bits). */
+double mtp_oracle_e2m1_value(uint8_t code) {
+  const int e = (code >> 1) & 3;
+  const int m = code & 1;
+  /* exponent 0: m * 0.5; otherwise (1 + m/2) * 2^(e-1) = (2 + m) * 2^(e-2) */
+  const double v = e == 0 ? 0.5 * m : ldexp((double)(2 + m), e - 2);
+  return (code & 8) ? -v : v;
+}
+
+/* The E2M1 code nearest to x (ties to the even code, i.e. mantissa bit 0
+ * clear); magnitudes beyond 6 saturate to 6; x < 0 sets the sign bit. */
+uint8_t mtp_oracle_e2m1_round(double x) {
+  const uint8_t s = x < 0.0 ? 8 : 0;
+  const double a = fabs(x);
+  if (!(a < 6.0)) return s | 7;                 /* also NaN (out of contract) */
+  if (a < 1.0) {
+    /* spacing 0.5: round 2a to an integer, ties to even; 2 is the code of 1.0 */
+    return s | (uint8_t)nearbyint(2.0 * a);
+  }
+  int E;
+  frexp(a, &E);                                 /* a = f * 2^E, f in [0.5, 1) */
+  int ue = E - 1;                               /* a in [2^ue, 2^(ue+1)), ue 0..2 */
+  double r = nearbyint(ldexp(a, 1 - ue));       /* 2 or 3 in halves of 2^ue; 4: next binade */
+  if (r == 4.0) { r = 2.0; ue += 1; }
+  return s | (uint8_t)(((ue + 1) << 1) | ((int)r - 2));
+}
+
+int mtp_oracle_e2m1_round_array(const double *x, int64_t n, uint8_t *out) {
+  if (!x || !out || n < 0) return ORC_BAD_ARG;
+  for (int64_t i = 0; i < n; ++i) out[i] = mtp_oracle_e2m1_round(x[i]);
+  return ORC_OK;
+}
+
+/* A block's scale exponent: floor(log2(max |w|)) - 2, clamped to [-127, 127];
+ * -127 for an all-zero block. */
+int mtp_oracle_mx_block_exponent(const uint16_t *w, int64_t n, int32_t *e_out) {
+  if (!w || !e_out || n <= 0) return ORC_BAD_ARG;
+  double amax = 0.0;
+  for (int64_t j = 0; j < n; ++j) {
+    const double v = fabs(bf16_to_double(w[j]));
+    if (!isfinite(v)) return ORC_NOT_FINITE;
+    if (v > amax) amax = v;
+  }
+  int e = amax == 0.0 ? -127 : ilogb(amax) - 2;
+  if (e < -127) e = -127;
+  if (e > 127) e = 127;
+  *e_out = e;
+  return ORC_OK;
+}
+
+/* Quantise the candidate rows head[ids[i]] (ids NULL: rows 0..C-1) to MXFP4:
+ * q[i][j / 2] holds the codes of elements j (low nibble, j even) and j + 1;
+ * scales[i][b] = e + 127 of block b (elements 32b .. 32b + 31). H % 32 == 0. */
+int mtp_oracle_quantize_mxfp4(const uint16_t *head, int64_t V, int64_t H, const int32_t *ids,
+                              int64_t C, uint8_t *q, uint8_t *scales) {
+  if (!head || !q || !scales || V <= 0 || H <= 0 || H % 32 != 0 || C <= 0) return ORC_BAD_ARG;
+  if (ids && mtp_oracle_check_ids(ids, C, V) != ORC_OK) return ORC_BAD_IDS;
+  if (!ids && C > V) return ORC_BAD_ARG;
+  const int64_t nb = H / 32;
+  for (int64_t i = 0; i < C; ++i) {
+    const uint16_t *w = head + (int64_t)(ids ? ids[i] : i) * H;
+    for (int64_t b = 0; b < nb; ++b) {
+      int32_t e = 0;
+      const int r = mtp_oracle_mx_block_exponent(w + 32 * b, 32, &e);
+      if (r != ORC_OK) return r;
+      scales[i * nb + b] = (uint8_t)(e + 127);
+      for (int64_t j = 32 * b; j < 32 * b + 32; j += 2) {
+        const uint8_t lo = mtp_oracle_e2m1_round(ldexp(bf16_to_double(w[j]), -e));
+        const uint8_t hi = mtp_oracle_e2m1_round(ldexp(bf16_to_double(w[j + 1]), -e));
+        q[i * (H / 2) + j / 2] = (uint8_t)(lo | (hi << 4));
+      }
+    }
+  }
+  return ORC_OK;
+}
+
+/* One MXFP4 row's logit: sum over j of x[j] * 2^e(j / 32) * value(q[j]), in
+ * order, in double (each term is exact). */
+static double dot_mxfp4(const uint16_t *x, const uint8_t *q, const uint8_t *scales, int64_t H) {
+  double s = 0.0;
+  for (int64_t j = 0; j < H; ++j) {
+    const uint8_t code = (j & 1) ? (q[j / 2] >> 4) : (q[j / 2] & 15);
+    const int e = (int)scales[j / 32] - 127;
+    s += bf16_to_double(x[j]) * ldexp(mtp_oracle_e2m1_value(code), e);
+  }
+  return s;
+}
+
+/* Argmax of every query row over an MXFP4 table of N rows (as
+ * mtp_oracle_argmax, with each row's logit from dot_mxfp4). */
+int mtp_oracle_mxfp4_argmax(const uint16_t *x, int64_t M, const uint8_t *q,
+                            const uint8_t *scales, const int32_t *ids, int64_t N, int64_t H,
+                            int32_t *top_id, float *top_logit, double *top_exact,
+                            int32_t *runner_id, double *runner_exact) {
+  if (!x || !q || !scales || !top_id || !top_logit || !top_exact || !runner_id ||
+      !runner_exact || M < 0 || N <= 0 || H <= 0 || H % 32 != 0)
+    return ORC_BAD_ARG;
+  double *z = (double *)malloc((size_t)N * sizeof(double));
+  if (!z) return ORC_NO_MEMORY;
+  int rc = ORC_OK;
+  for (int64_t m = 0; m < M && rc == ORC_OK; ++m) {
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n)
+      z[n] = dot_mxfp4(x + m * H, q + n * (H / 2), scales + n * (H / 32), H);
     rc = decide_row(z, N, ids, top_id + m, top_logit + m, top_exact + m, runner_id + m,
                     runner_exact + m);
   }

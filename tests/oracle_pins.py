@@ -335,6 +335,132 @@ def pin_fp8_draft(oracle, seed=47):
     assert np.array_equal(d8["id"], oracle.draft(h, oracle.pack(W, ids), ids)["id"])
 
 
+def _minifloat_magnitudes(ebits: int, mbits: int, bias: int) -> np.ndarray:
+    """Values of the non-negative codes of a sign / exponent / mantissa float
+    without infinities, indexed by code: exponent field 0 holds the
+    subnormals m * 2^(1 - bias - mbits), field e > 0 holds
+    (1 + m / 2^mbits) * 2^(e - bias)."""
+    vals = []
+    for e in range(2 ** ebits):
+        for m in range(2 ** mbits):
+            vals.append(m * 2.0 ** (1 - bias - mbits) if e == 0
+                        else (1 + m / 2 ** mbits) * 2.0 ** (e - bias))
+    return np.array(vals)
+
+
+def _nearest_even_code(x: float, mags: np.ndarray, sign_bit: int) -> int:
+    """Brute force: the code of the magnitude nearest to |x| (past the largest,
+    the largest; ties to the even code), with the sign bit set for x < 0."""
+    a = abs(x)
+    d = np.abs(mags - a)
+    best = np.flatnonzero(d == d.min())
+    code = int(best[0]) if len(best) == 1 else int([c for c in best if c % 2 == 0][0])
+    return code | (sign_bit if x < 0 else 0)
+
+
+def pin_e2m1_format(oracle, seed=53):
+    """The field enumeration reproduces torch's E4M3 decode (all finite codes),
+    which pins the enumeration; with 2 exponent bits, bias 1 and 1 mantissa
+    bit it gives the E2M1 decode (sign in bit 3). Rounding equals a brute-force
+    nearest-even search over the 8 magnitudes, at every midpoint and on
+    random values, saturating at 6."""
+    import torch
+    e4 = _minifloat_magnitudes(4, 3, 7)
+    t = torch.arange(128, dtype=torch.uint8).view(torch.float8_e4m3fn).float().numpy()
+    assert np.array_equal(e4[:127], t[:127].astype(np.float64))
+    mags = _minifloat_magnitudes(2, 1, 1)
+    assert np.array_equal(mags, [0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    got = oracle.e2m1_value(np.arange(16, dtype=np.uint8))
+    assert np.array_equal(got[:8], mags) and np.array_equal(got[8:], -mags)
+    assert np.all(np.signbit(got[8:]))
+    mids = (mags[1:] + mags[:-1]) / 2
+    r = wl.rng(seed, 1)
+    x = np.concatenate([mags, mids, r.uniform(0, 8, 2000), np.exp2(r.uniform(-4, 3, 1000)),
+                        [6.5, 7.0, 100.0, 1e9]])
+    x = np.concatenate([x, -x[1:]])
+    codes = oracle.e2m1_round(x)
+    for v, c in zip(x, codes):
+        assert int(c) == _nearest_even_code(float(v), mags, 8), (v, c)
+
+
+def pin_mxfp4_quantize(oracle, seed=59):
+    """Block scales follow the OCP MX rule 2^(e+2) <= max|w| < 2^(e+3) (clamped
+    to [-127, 127]; -127 for an all-zero block); every element is the
+    nearest-even E2M1 code of w * 2^-e; two codes per byte with the even
+    element in the low nibble, one scale byte (e + 127) per 32 elements;
+    rows on the scaled grid round-trip; ids select head rows."""
+    V, H = 24, 128
+    W = wl.normal_bf16_rows(V, H, 0.02, seed, 1)
+    W[2] = 0
+    W[3, 32:64] = 0                                      # one zero block
+    W[4, :32] = 0x0001                                   # smallest subnormal: clamp at -127
+    W[4, 32:64] = 0x7F7F                                 # largest finite bf16: e = 125
+    q, sc = oracle.quantize_mxfp4(W)
+    assert q.shape == (V, H // 2) and sc.shape == (V, H // 32)
+    wf = wl.bf16_bits_to_f32(W).astype(np.float64)
+    mags = _minifloat_magnitudes(2, 1, 1)
+    for i in range(V):
+        for b in range(H // 32):
+            blk = wf[i, 32 * b:32 * b + 32]
+            e = int(sc[i, b]) - 127
+            amax = np.abs(blk).max()
+            if amax == 0:
+                assert e == -127
+            elif 2.0 ** -125 <= amax < 2.0 ** 130:
+                assert 2.0 ** (e + 2) <= amax < 2.0 ** (e + 3), (i, b, e, amax)
+            assert e == oracle.mx_block_exponent(W[i, 32 * b:32 * b + 32])
+            for j in range(32 * b, 32 * b + 32):
+                byte = int(q[i, j // 2])
+                code = byte & 15 if j % 2 == 0 else byte >> 4
+                assert code == _nearest_even_code(float(wf[i, j] * 2.0 ** -e), mags, 8), (i, j)
+    assert sc[4, 0] == 0 and sc[4, 1] == 125 + 127
+    # a row on the scaled grid: element j = +-mags[j % 8] * 2^e_b, block max 6 * 2^e_b
+    eb = np.array([-3, -5, 0, 2])
+    vals = np.array([mags[j % 8] * (-1) ** (j // 8) * 2.0 ** eb[j // 32] for j in range(H)])
+    Wg = wl.f32_to_bf16_bits(vals.astype(np.float32)[None, :])
+    qg, sg = oracle.quantize_mxfp4(Wg)
+    assert np.array_equal(sg[0], eb + 127)
+    for j in range(H):
+        code = (j % 8) | (8 if (j // 8) % 2 and j % 8 else 0)
+        byte = int(qg[0, j // 2])
+        assert (byte & 15 if j % 2 == 0 else byte >> 4) == code, j
+    assert np.array_equal(oracle.mxfp4_values(qg, sg)[0], vals)
+    ids = np.array([0, 4, 9, 23], np.int32)
+    qi, si = oracle.quantize_mxfp4(W, ids)
+    assert np.array_equal(qi, q[ids]) and np.array_equal(si, sc[ids])
+
+
+def pin_mxfp4_draft(oracle, seed=61):
+    """Rows built on the scaled E2M1 grid (every block's max 6 * 2^e, so the
+    scale rule returns e) quantise exactly; with hidden rows on the q/16 grid
+    every logit is an exact multiple of 2^-8. The pick is the first maximum
+    of the exact logits of the original rows, and equals the bf16 draft over
+    the same rows, logit included."""
+    V, H, C = 600, 96, 250
+    r = wl.rng(seed, 1)
+    mags = _minifloat_magnitudes(2, 1, 1)
+    codes = r.integers(0, 16, size=(V, H))
+    codes[:, ::32] = 7                                   # +6 leads every block
+    e = r.integers(-3, 1, size=(V, H // 32))
+    vals = np.where(codes >= 8, -1.0, 1.0) * mags[codes & 7] * np.exp2(np.repeat(e, 32, axis=1))
+    W = wl.f32_to_bf16_bits(vals.astype(np.float32))
+    h = wl.exact_grid_bf16((4, H), seed, 2)
+    ids = wl.candidate_ids(V, C, seed)
+    q, sc = oracle.quantize_mxfp4(W, ids)
+    assert np.array_equal(sc.astype(np.int64) - 127, e[ids])
+    d4 = oracle.draft_mxfp4(h, q, sc, ids)
+    hf = wl.bf16_bits_to_f32(h).astype(np.float64)
+    num = np.rint((hf @ vals[ids].T) * 256).astype(np.int64)
+    assert np.array_equal(num / 256.0, hf @ vals[ids].T)
+    for m in range(4):
+        row = [int(v) for v in num[m]]
+        best = _first_max(row)
+        assert d4["id"][m] == ids[best]
+        assert d4["logit"][m] == np.float32(row[best] / 256.0)
+    d16 = oracle.draft(h, oracle.pack(W, ids), ids)
+    assert np.array_equal(d4["id"], d16["id"]) and np.array_equal(d4["logit"], d16["logit"])
+
+
 def pin_pack(oracle):
     """Packing copies head rows ids[i]; invalid id lists are refused."""
     V, H = 50, 16
@@ -445,6 +571,9 @@ ALL_PINS = [
     pin_e4m3_format,
     pin_fp8_quantize,
     pin_fp8_draft,
+    pin_e2m1_format,
+    pin_mxfp4_quantize,
+    pin_mxfp4_draft,
     pin_pack,
     pin_worked_accept,
     pin_accept_invariants,

@@ -30,6 +30,18 @@ MUTATIONS = [
     ("fp8_scale_search_dropped", "while (ldexp(448.0, e) < amax) ++e;\n  while (ldexp(448.0, e - 1) >= amax) --e;", ""),
     ("fp8_scale_ignored", "return ldexp(s, e);", "return s;"),
     ("fp8_code_ignores_scale", "mtp_oracle_e4m3_round(ldexp(bf16_to_double(w[j]), -e))", "mtp_oracle_e4m3_round(bf16_to_double(w[j]))"),
+    ("e2m1_bias_2", "ldexp((double)(2 + m), e - 2)", "ldexp((double)(2 + m), e - 3)"),
+    ("e2m1_ties_away_from_zero", "nearbyint(ldexp(a, 1 - ue))", "round(ldexp(a, 1 - ue))"),
+    ("e2m1_subnormal_ties_away", "nearbyint(2.0 * a)", "round(2.0 * a)"),
+    ("e2m1_no_saturation", "if (!(a < 6.0)) return s | 7;", "if (!(a < 8.0)) return s | 7;"),
+    ("e2m1_sign_lost", "const uint8_t s = x < 0.0 ? 8 : 0;", "const uint8_t s = 0;"),
+    ("mx_scale_one_too_high", "ilogb(amax) - 2", "ilogb(amax) - 1"),
+    ("mx_zero_block_scale", "amax == 0.0 ? -127", "amax == 0.0 ? 0"),
+    ("mx_no_low_clamp", "if (e < -127) e = -127;", ""),
+    ("mx_nibbles_swapped", "(uint8_t)(lo | (hi << 4))", "(uint8_t)(hi | (lo << 4))"),
+    ("mx_logit_scale_stride_16", "const int e = (int)scales[j / 32] - 127;", "const int e = (int)scales[j / 16] - 127;"),
+    ("mx_logit_ignores_scale", "s += bf16_to_double(x[j]) * ldexp(mtp_oracle_e2m1_value(code), e);", "s += bf16_to_double(x[j]) * mtp_oracle_e2m1_value(code);"),
+    ("mx_logit_nibble_order", "(j & 1) ? (q[j / 2] >> 4) : (q[j / 2] & 15)", "(j & 1) ? (q[j / 2] & 15) : (q[j / 2] >> 4)"),
 ]
 
 
