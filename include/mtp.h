@@ -326,6 +326,51 @@ mtp_status mtp_draft_argmax_fp8_cfg(const mtp_bf16 *hidden, int M, int H, const 
                                     const mtp_config *cfg);
 
 /*
+ * MXFP4 candidate table (4-bit rows; draft calls only).
+ *
+ * The candidate rows in the OCP microscaling 4-bit format, a quarter of the
+ * bf16 bytes: elements E2M1 (sign, 2 exponent bits with bias 1, 1 mantissa
+ * bit; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6) and one E8M0 scale 2^e per
+ * block of 32 consecutive elements of a row, e = floor(log2(max |w| over the
+ * block)) - 2 clamped to [-127, 127] (-127 for an all-zero block). Element j
+ * is the E2M1 value nearest to w[j] * 2^-e (ties to the even code; past 6 it
+ * saturates; a negative value keeps its sign bit when it rounds to zero).
+ * [Qwen3.8 Flash dual-Spark tuning log, section "read one fewer big table":
+ * the upstream work stores the candidate rows in a 4-bit float format and
+ * reports a further gain over bf16 rows; the pages fix no block size or
+ * scale format, and MXFP4 is the 4-bit block format gfx950 converts in
+ * hardware.] The verify keeps the bf16 head.
+ *
+ * Layout: table_q [C][H/2] bytes, row-major, byte j/2 of a row holding
+ * element j in its low nibble when j is even and in its high nibble when j is
+ * odd; scales [C][H/32] bytes, the code e + 127 of block b = j/32. H must be
+ * a multiple of 32. A row's logit is sum_j x[j] * 2^e(j/32) * value(q[j]),
+ * accumulated in fp32 (each block's partial sum is scaled, exactly, by its
+ * power of two); argmax and ids as mtp_draft_argmax.
+ *
+ * mtp_mxfp4_table_bytes / mtp_mxfp4_scale_bytes: C*H/2 and C*H/32 (0 if out
+ * of range). mtp_pack_candidates_mxfp4 quantises head rows ids[i] (ids NULL:
+ * the first C rows); an id outside [0, V) gives a zero row (scale code 0).
+ * mtp_draft_argmax_mxfp4 runs on the vector-ALU kernel (any M; more than a
+ * few hidden rows take several passes); cfg->path MTP_PATH_MFMA gives
+ * MTP_ERR_UNSUPPORTED. Workspace as mtp_draft_argmax.
+ */
+size_t mtp_mxfp4_table_bytes(int64_t C, int H);
+size_t mtp_mxfp4_scale_bytes(int64_t C, int H);
+mtp_status mtp_pack_candidates_mxfp4(const mtp_bf16 *head, int64_t V, int H, const int32_t *ids,
+                                     int64_t C, uint8_t *table_q, uint8_t *scales,
+                                     hipStream_t stream);
+mtp_status mtp_draft_argmax_mxfp4(const mtp_bf16 *hidden, int M, int H, const uint8_t *table_q,
+                                  const uint8_t *scales, const int32_t *ids, int64_t C,
+                                  int32_t *out_ids, float *out_logit, void *ws, size_t ws_bytes,
+                                  hipStream_t stream);
+mtp_status mtp_draft_argmax_mxfp4_cfg(const mtp_bf16 *hidden, int M, int H,
+                                      const uint8_t *table_q, const uint8_t *scales,
+                                      const int32_t *ids, int64_t C, int32_t *out_ids,
+                                      float *out_logit, void *ws, size_t ws_bytes,
+                                      hipStream_t stream, const mtp_config *cfg);
+
+/*
  * FP8 candidate table in the tiled layout (batched draft rows: the
  * matrix-core kernel). Same codes and scales as mtp_pack_candidates_fp8,
  * stored as the fp8 form of the 64-row tiled layout: rows in tiles of 64

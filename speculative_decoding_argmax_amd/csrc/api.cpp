@@ -498,6 +498,73 @@ mtp_status mtp_draft_argmax_fp8(const mtp_bf16 *hidden, int M, int H, const uint
                                   ws_bytes, stream, nullptr);
 }
 
+size_t mtp_mxfp4_table_bytes(int64_t C, int H) {
+  if (C < 1 || C > INT32_MAX || H < 32 || H > MTP_MAX_HIDDEN || H % 32 != 0) return 0;
+  return (size_t)C * (size_t)(H / 2);
+}
+
+size_t mtp_mxfp4_scale_bytes(int64_t C, int H) {
+  if (mtp_mxfp4_table_bytes(C, H) == 0) return 0;
+  return (size_t)C * (size_t)(H / 32);
+}
+
+mtp_status mtp_pack_candidates_mxfp4(const mtp_bf16 *head, int64_t V, int H, const int32_t *ids,
+                                     int64_t C, uint8_t *table_q, uint8_t *scales,
+                                     hipStream_t stream) {
+  if (!head || !table_q || !scales) return MTP_ERR_INVALID_ARG;
+  if (V < 1 || V > INT32_MAX || mtp_mxfp4_table_bytes(C, H) == 0) return MTP_ERR_INVALID_ARG;
+  if (!ids && C > V) return MTP_ERR_INVALID_ARG;
+  if (!aligned(head, 16) || !aligned(table_q, 16) || (ids && !aligned(ids, 4)))
+    return MTP_ERR_INVALID_ARG;
+  int cus = 0;
+  hipError_t e = current_cus(&cus);
+  if (e != hipSuccess) return hip_fail(e);
+  e = mtp::launch_pack_mxfp4(head, V, H, ids, C, table_q, scales, cus, stream);
+  if (e != hipSuccess) return hip_fail(e);
+  return MTP_OK;
+}
+
+mtp_status mtp_draft_argmax_mxfp4_cfg(const mtp_bf16 *hidden, int M, int H,
+                                      const uint8_t *table_q, const uint8_t *scales,
+                                      const int32_t *ids, int64_t C, int32_t *out_ids,
+                                      float *out_logit, void *ws, size_t ws_bytes,
+                                      hipStream_t stream, const mtp_config *cfg) {
+  if (!scales || H % 32 != 0) return MTP_ERR_INVALID_ARG;
+  mtp_status st =
+      check_draft_args(hidden, M, H, table_q, ids, C, out_ids, out_logit, ws, ws_bytes, cfg);
+  if (st != MTP_OK) return st;
+  if (cfg && cfg->path == MTP_PATH_MFMA) return MTP_ERR_UNSUPPORTED;
+  const int nblk = H / 32;
+  const int ncl = mtp::fp4_ncl_for(nblk);
+  if (ncl == 0) return MTP_ERR_UNSUPPORTED;
+  int cus = 0;
+  hipError_t e = current_cus(&cus);
+  if (e != hipSuccess) return hip_fail(e);
+  const int mr = mtp::fp4_rows_for(M, ncl);
+  const int per_cu = (cfg && cfg->blocks_per_cu > 0) ? cfg->blocks_per_cu : 1;
+  mtp::Fp4Launch L;
+  L.X = hidden;
+  L.Q = table_q;
+  L.scales = scales;
+  L.M = M;
+  L.N = C;
+  L.nblk = nblk;
+  L.max_blocks_x = per_cu * cus;
+  L.sink = draft_sink(ws, ids, out_ids, out_logit, M);
+  L.stream = stream;
+  e = mtp::launch_fp4(L, mr, ncl);
+  if (e != hipSuccess) return hip_fail(e);
+  return MTP_OK;
+}
+
+mtp_status mtp_draft_argmax_mxfp4(const mtp_bf16 *hidden, int M, int H, const uint8_t *table_q,
+                                  const uint8_t *scales, const int32_t *ids, int64_t C,
+                                  int32_t *out_ids, float *out_logit, void *ws, size_t ws_bytes,
+                                  hipStream_t stream) {
+  return mtp_draft_argmax_mxfp4_cfg(hidden, M, H, table_q, scales, ids, C, out_ids, out_logit, ws,
+                                    ws_bytes, stream, nullptr);
+}
+
 size_t mtp_tiled_fp8_bytes(int64_t rows, int H) {
   if (rows < 1 || rows > INT32_MAX || H < 16 || H > MTP_MAX_HIDDEN || H % 16 != 0) return 0;
   return (size_t)mtp::tiled_rows(rows) * (size_t)mtp::tiled_cols(H);

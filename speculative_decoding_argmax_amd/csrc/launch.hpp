@@ -97,6 +97,25 @@ hipError_t launch_pack_fp8(const void *head, int64_t V, int H, const int32_t *id
                            void *q, float *scales, int num_cus, hipStream_t stream);
 hipError_t launch_fill_zero(void *ws, size_t bytes, hipStream_t stream);
 
+struct Fp4Launch {
+  const void *X;          // hidden [M][H] bf16
+  const void *Q;          // MXFP4 codes [N][H/2]
+  const uint8_t *scales;  // [N][H/32] E8M0 block scales
+  int M;
+  int64_t N;
+  int nblk;               // H / 32 (blocks per row)
+  int max_blocks_x;
+  RowSink sink;
+  hipStream_t stream;
+};
+
+// Blocks per lane that have an instantiation (0: too wide).
+int fp4_ncl_for(int nblk);
+int fp4_rows_for(int M, int ncl);
+hipError_t launch_fp4(const Fp4Launch &L, int mr, int ncl);
+hipError_t launch_pack_mxfp4(const void *head, int64_t V, int H, const int32_t *ids, int64_t C,
+                             void *q, uint8_t *scales, int num_cus, hipStream_t stream);
+
 // Streaming-read reference (probe.hip): sink words written per call, at most.
 constexpr int kStreamSinkWords = 8192;
 hipError_t launch_stream_read(const void *buf, size_t bytes, uint32_t *sink, int cus,

@@ -88,6 +88,11 @@ def _load() -> ctypes.CDLL:
         "mtp_draft_argmax_gather": ([P, I, I, P, I64, P, I64, P, P, P, S, P], I),
         "mtp_draft_argmax_gather_cfg": ([P, I, I, P, I64, P, I64, P, P, P, S, P, P], I),
         "mtp_fp8_table_bytes": ([I64, I], S),
+        "mtp_mxfp4_table_bytes": ([I64, I], S),
+        "mtp_mxfp4_scale_bytes": ([I64, I], S),
+        "mtp_pack_candidates_mxfp4": ([P, I64, I, P, I64, P, P, P], I),
+        "mtp_draft_argmax_mxfp4": ([P, I, I, P, P, P, I64, P, P, P, S, P], I),
+        "mtp_draft_argmax_mxfp4_cfg": ([P, I, I, P, P, P, I64, P, P, P, S, P, P], I),
         "mtp_pack_candidates_fp8": ([P, I64, I, P, I64, P, P, P], I),
         "mtp_draft_argmax_fp8": ([P, I, I, P, P, P, I64, P, P, P, S, P], I),
         "mtp_draft_argmax_fp8_cfg": ([P, I, I, P, P, P, I64, P, P, P, S, P, P], I),
@@ -437,6 +442,55 @@ def mtp_draft_argmax_fp8(hidden, table_q, scales, ids, out_ids, out_logit=None, 
         _ptr(out_logit, "out_logit", (torch.float32,), allow_none=True),
         _ptr(ws, "ws", (torch.int64, torch.uint8, torch.int32)), ws.numel() * ws.element_size(),
         _stream(stream), ctypes.byref(cfg)), "mtp_draft_argmax_fp8")
+
+
+def mtp_mxfp4_table_bytes(C: int, H: int) -> int:
+    return int(lib.mtp_mxfp4_table_bytes(C, H))
+
+
+def mtp_mxfp4_scale_bytes(C: int, H: int) -> int:
+    return int(lib.mtp_mxfp4_scale_bytes(C, H))
+
+
+def mtp_pack_candidates_mxfp4(head, ids, table_q, scales, C: Optional[int] = None,
+                              stream=None) -> None:
+    """Quantise head rows ids (None: the first C rows) to MXFP4: packed E2M1
+    codes table_q [C][H/2] and E8M0 block scales [C][H/32] (both uint8)."""
+    torch = _torch()
+    V, H = head.shape
+    C = ids.numel() if ids is not None else (V if C is None else C)
+    if tuple(table_q.shape) != (C, H // 2) or tuple(scales.shape) != (C, H // 32):
+        raise ValueError("table_q must be [C][H/2] and scales [C][H/32]")
+    _check(lib.mtp_pack_candidates_mxfp4(
+        _ptr(head, "head", _bf16_types()), V, H, _ptr(ids, "ids", (torch.int32,), allow_none=True),
+        C, _ptr(table_q, "table_q", (torch.uint8,)), _ptr(scales, "scales", (torch.uint8,)),
+        _stream(stream)), "mtp_pack_candidates_mxfp4")
+
+
+def mtp_draft_argmax_mxfp4(hidden, table_q, scales, ids, out_ids, out_logit=None, ws=None,
+                           stream=None, path: int = MTP_PATH_AUTO, blocks_per_cu: int = 0) -> None:
+    """Draft over an MXFP4 candidate table (see include/mtp.h)."""
+    torch = _torch()
+    M, H = hidden.shape
+    C, H2 = table_q.shape
+    if 2 * H2 != H or tuple(scales.shape) != (C, H // 32):
+        raise ValueError("shapes differ")
+    if ids is not None and ids.numel() != C:
+        raise ValueError("ids must have C entries")
+    if out_ids.numel() != M or (out_logit is not None and out_logit.numel() != M):
+        raise ValueError("outputs must have M entries")
+    if ws is None:
+        _no_alloc_in_capture("mtp_draft_argmax_mxfp4")
+        ws = alloc_workspace(mtp_draft_workspace_bytes(M, C, H), hidden.device, stream)
+    cfg = _cfg(path, blocks_per_cu)
+    _check(lib.mtp_draft_argmax_mxfp4_cfg(
+        _ptr(hidden, "hidden", _bf16_types()), M, H, _ptr(table_q, "table_q", (torch.uint8,)),
+        _ptr(scales, "scales", (torch.uint8,)),
+        _ptr(ids, "ids", (torch.int32,), allow_none=True), C,
+        _ptr(out_ids, "out_ids", (torch.int32,)),
+        _ptr(out_logit, "out_logit", (torch.float32,), allow_none=True),
+        _ptr(ws, "ws", (torch.int64, torch.uint8, torch.int32)), ws.numel() * ws.element_size(),
+        _stream(stream), ctypes.byref(cfg)), "mtp_draft_argmax_mxfp4")
 
 
 def mtp_tiled_fp8_bytes(rows: int, H: int) -> int:

@@ -165,3 +165,20 @@ def check_fp8_rows(g_ids, g_logit, ref, x, q, e, ids):
             zg = float(oracle.draft_fp8(x[m:m + 1], q[row:row + 1], e[row:row + 1])["exact"][0])
             assert zg >= top - tol
         assert abs(float(g_logit[m]) - zg) <= LOGIT_REL * abs(zg)
+
+
+def check_mxfp4_rows(g_ids, g_logit, ref, x, q, sc, ids):
+    """Near-tie rule of the bf16 path, with logits recomputed as MXFP4 logits."""
+    pos = {int(v): i for i, v in enumerate(ids)} if ids is not None else None
+    for m in range(len(g_ids)):
+        top, runner = float(ref["exact"][m]), float(ref["runner_exact"][m])
+        tol = NEAR_TIE_REL * abs(top)
+        g = int(g_ids[m])
+        row = pos[g] if pos is not None else g
+        if g == ref["id"][m]:
+            zg = top
+        else:
+            assert runner >= top - tol, f"row {m}: {g} vs {ref['id'][m]} outside a near tie"
+            zg = float(oracle.draft_mxfp4(x[m:m + 1], q[row:row + 1], sc[row:row + 1])["exact"][0])
+            assert zg >= top - tol
+        assert abs(float(g_logit[m]) - zg) <= LOGIT_REL * abs(zg)

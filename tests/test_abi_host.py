@@ -277,3 +277,26 @@ def test_wide_tiled_calls_need_the_staging_area():
     v = mtp.lib.mtp_verify_accept_tiled
     assert v(FAKE, 32, 4, 5120, FAKE, 248320, FAKE, FAKE, None, FAKE, FAKE, FAKE, counters(160),
              None) == mtp.MTP_ERR_WORKSPACE
+
+
+def test_mxfp4_entry_points_reject_bad_arguments():
+    assert mtp.mtp_mxfp4_table_bytes(100, 2048) == 100 * 1024
+    assert mtp.mtp_mxfp4_scale_bytes(100, 2048) == 100 * 64
+    assert mtp.mtp_mxfp4_table_bytes(100, 48) == 0       # H % 32 != 0
+    assert mtp.mtp_mxfp4_table_bytes(0, 64) == 0
+    assert mtp.mtp_mxfp4_scale_bytes(100, 16) == 0
+    p = mtp.lib.mtp_pack_candidates_mxfp4
+    ok = (FAKE, 100, 64, FAKE, 50, FAKE, FAKE, None)
+    assert p(None, *ok[1:]) == INVALID
+    assert p(*ok[:2], 48, *ok[3:]) == INVALID            # H % 32
+    assert p(*ok[:3], None, 101, *ok[5:]) == INVALID     # C > V without ids
+    assert p(*ok[:5], P(0x10008), *ok[6:]) == INVALID    # codes not 16-byte aligned
+    assert p(*ok[:6], None, None) == INVALID             # no scales
+    d = mtp.lib.mtp_draft_argmax_mxfp4
+    dk = (FAKE, 1, 64, FAKE, FAKE, None, 100, FAKE, None, FAKE, 4096, None)
+    assert d(*dk[:2], 48, *dk[3:]) == INVALID
+    assert d(*dk[:4], None, *dk[5:]) == INVALID          # no scales
+    assert d(*dk[:9], None, *dk[10:]) == mtp.MTP_ERR_WORKSPACE
+    c = mtp.mtp_config()
+    c.path = mtp.MTP_PATH_MFMA
+    assert mtp.lib.mtp_draft_argmax_mxfp4_cfg(*dk, ctypes.byref(c)) == mtp.MTP_ERR_UNSUPPORTED
