@@ -54,11 +54,12 @@ def parse_args():
     ap.add_argument("--layout", choices=("auto", "rows", "tiled"), default="auto",
                     help="table layout: row-major, or the 64-row tiled layout of include/mtp.h "
                          "(auto: rows when every call has at most 8 hidden rows)")
-    ap.add_argument("--table", choices=("bf16", "fp8"), default="bf16",
-                    help="precision of the draft's candidate table: bf16 rows, or E4M3 rows "
+    ap.add_argument("--table", choices=("bf16", "fp8", "mxfp4"), default="bf16",
+                    help="precision of the draft's candidate table: bf16 rows, E4M3 rows "
                          "with power-of-two row scales (mtp_pack_candidates_fp8, or "
-                         "mtp_pack_tiled_fp8 with --layout tiled); the verify always reads the "
-                         "bf16 head")
+                         "mtp_pack_tiled_fp8 with --layout tiled), or MXFP4 rows (E2M1 codes, "
+                         "one E8M0 scale per 32 elements; mtp_pack_candidates_mxfp4, row-major "
+                         "layout); the verify always reads the bf16 head")
     ap.add_argument("--draft-source", choices=("table", "gather"), default="table",
                     help="draft calls read a packed candidate table (default), or head rows "
                          "through a per-call id list (mtp_draft_argmax_gather; row-major only)")
@@ -131,13 +132,17 @@ def main() -> int:
         return torch.from_numpy(np.ascontiguousarray(a).view(dt)).to(dev)
 
     layout = args.layout
+    fp4 = args.table == "mxfp4"
     if layout == "auto":
-        layout = "rows" if max(wk.Md, wk.Mv) <= 8 else "tiled"
+        layout = "rows" if max(wk.Md, wk.Mv) <= 8 or fp4 else "tiled"
     gather = args.draft_source == "gather"
     fp8 = args.table == "fp8"
-    if fp8 and gather:
-        print("--table fp8 runs on a packed candidate table (use --draft-source table)",
+    if (fp8 or fp4) and gather:
+        print("--table fp8/mxfp4 runs on a packed candidate table (use --draft-source table)",
               file=sys.stderr)
+        return 2
+    if fp4 and layout != "rows":
+        print("--table mxfp4 runs on the row-major table (use --layout rows)", file=sys.stderr)
         return 2
     if gather and layout != "rows":
         print("--draft-source gather runs on the row-major head (use --layout rows)",
@@ -147,6 +152,12 @@ def main() -> int:
     ids_d = up(ids, np.int32)
     tables = []
     for _ in range(max(1, args.table_copies)):
+        if fp4:
+            tq = torch.empty((wk.C, wk.H // 2), dtype=torch.uint8, device=dev)
+            ts = torch.empty((wk.C, wk.H // 32), dtype=torch.uint8, device=dev)
+            mtp.mtp_pack_candidates_mxfp4(head_d, ids_d, tq, ts)
+            tables.append((tq, ts))
+            continue
         if fp8 and layout == "rows":
             tq = torch.empty((wk.C, wk.H), dtype=torch.uint8, device=dev)
             ts = torch.empty(wk.C, dtype=torch.float32, device=dev)
@@ -165,7 +176,7 @@ def main() -> int:
             t = mtp.alloc_tiled(wk.C, wk.H, dev)
             mtp.mtp_pack_tiled(head_d, ids_d, t)
         tables.append(t)
-    if layout == "tiled" or fp8:
+    if layout == "tiled" or fp8 or fp4:
         # counter calibration for rocprofv3 runs (untimed): one plain
         # gather-copy of known size, the row-major candidate pack, which
         # these layouts do not otherwise run
@@ -197,7 +208,10 @@ def main() -> int:
                   for c in range(wk.draft_calls)] if gather else None
 
     def draft_call(c, table):
-        if fp8 and layout == "rows":
+        if fp4:
+            mtp.mtp_draft_argmax_mxfp4(h_d[c], table[0], table[1], ids_d, out_ids[c],
+                                       out_logit[c], ws=ws_d)
+        elif fp8 and layout == "rows":
             mtp.mtp_draft_argmax_fp8(h_d[c], table[0], table[1], ids_d, out_ids[c], out_logit[c],
                                      ws=ws_d)
         elif fp8:
@@ -343,9 +357,9 @@ def main() -> int:
                    "head_GBps": stream_gbps([head_v], head_bytes, 20)}
 
     agreement = None
-    if fp8:
-        # how often the fp8 draft picks the bf16 draft's token (512 hidden rows
-        # of the workload's distribution; untimed)
+    if fp8 or fp4:
+        # how often the quantised draft picks the bf16 draft's token (512
+        # hidden rows of the workload's distribution; untimed)
         n_rows = 512
         hx = up(wl.hidden_states(n_rows, wk.H, wk.seed, block=900))
         t16 = torch.empty((wk.C, wk.H), dtype=torch.int16, device=dev)
@@ -353,7 +367,9 @@ def main() -> int:
         a8 = torch.empty(n_rows, dtype=torch.int32, device=dev)
         a16 = torch.empty(n_rows, dtype=torch.int32, device=dev)
         ws_x = mtp.alloc_workspace(mtp.mtp_draft_workspace_bytes(n_rows, wk.C, wk.H), dev)
-        if layout == "rows":
+        if fp4:
+            mtp.mtp_draft_argmax_mxfp4(hx, tables[0][0], tables[0][1], ids_d, a8, ws=ws_x)
+        elif layout == "rows":
             mtp.mtp_draft_argmax_fp8(hx, tables[0][0], tables[0][1], ids_d, a8, ws=ws_x)
         else:
             mtp.mtp_draft_argmax_tiled_fp8(hx, tables[0][0], tables[0][1], wk.C, ids_d, a8,
@@ -365,7 +381,10 @@ def main() -> int:
     H, C, V, Md, Mv = wk.H, wk.C, wk.V, wk.Md, wk.Mv
     # algorithmic bytes: weight rows + hidden rows + small outputs (winner ids,
     # logits; verify also reads drafts and writes acceptance)
-    if fp8:
+    if fp4:
+        # codes (half a byte per element) + one scale byte per 32 elements
+        draft_bytes = C * H // 2 + C * H // 32 + Md * H * 2 + Md * (4 + 4 + 4)
+    elif fp8:
         # codes + one scale per row
         draft_bytes = C * H + C * 4 + Md * H * 2 + Md * (4 + 4 + 4)
     else:
@@ -419,7 +438,9 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8-e4m3 draft rows, bf16 hidden and head" if fp8 else "bf16",
+        "dtype": ("fp8-e4m3 draft rows, bf16 hidden and head" if fp8 else
+                  "mxfp4 draft rows (e2m1, e8m0 block scales), bf16 hidden and head" if fp4
+                  else "bf16"),
         "data": "synthetic",
         "config": {
             "workload": f"{wk.name}: {wk.draft_calls} draft calls (M={Md}, {C}-row table) + 1 "
@@ -439,7 +460,7 @@ def main() -> int:
             "draft_same_table_us": round(warm_draft_us, 2),
             "single_call_us": {"draft": single_draft_us, "verify": single_verify_us},
             "stream_read": stream_read,
-            "fp8_draft_agrees_with_bf16": agreement,
+            "quantised_draft_agrees_with_bf16": agreement,
             "setup_s": round(setup_s, 1),
         },
         "roofline": roofline,
