@@ -450,8 +450,8 @@ void mtp_graph_destroy(mtp_graph *graph);
  * loads, and writes one XOR word per wave into `sink` (at most
  * MTP_STREAM_SINK_WORDS words; their values carry no meaning). Timing it
  * over a buffer of a call's size gives the read rate this device actually
- * reaches, against which the draft and verify calls, whose cost is the bytes
- * of the rows they read, are judged. [Qwen3.8 Flash dual-Spark tuning log,
+ * reaches: the practical ceiling of the draft and verify calls, whose cost is
+ * the bytes of the rows they read. [Qwen3.8 Flash dual-Spark tuning log,
  * section "read one fewer big table": the draft's time follows the size of
  * the table it reads.]
  *
