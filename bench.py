@@ -58,8 +58,9 @@ def parse_args():
                     help="precision of the draft's candidate table: bf16 rows, E4M3 rows "
                          "with power-of-two row scales (mtp_pack_candidates_fp8, or "
                          "mtp_pack_tiled_fp8 with --layout tiled), or MXFP4 rows (E2M1 codes, "
-                         "one E8M0 scale per 32 elements; mtp_pack_candidates_mxfp4, row-major "
-                         "layout); the verify always reads the bf16 head")
+                         "one E8M0 scale per 32 elements; mtp_pack_candidates_mxfp4, or "
+                         "mtp_pack_tiled_mxfp4 with --layout tiled); the verify always reads "
+                         "the bf16 head")
     ap.add_argument("--draft-source", choices=("table", "gather"), default="table",
                     help="draft calls read a packed candidate table (default), or head rows "
                          "through a per-call id list (mtp_draft_argmax_gather; row-major only)")
@@ -134,15 +135,12 @@ def main() -> int:
     layout = args.layout
     fp4 = args.table == "mxfp4"
     if layout == "auto":
-        layout = "rows" if max(wk.Md, wk.Mv) <= 8 or fp4 else "tiled"
+        layout = "rows" if max(wk.Md, wk.Mv) <= 8 else "tiled"
     gather = args.draft_source == "gather"
     fp8 = args.table == "fp8"
     if (fp8 or fp4) and gather:
         print("--table fp8/mxfp4 runs on a packed candidate table (use --draft-source table)",
               file=sys.stderr)
-        return 2
-    if fp4 and layout != "rows":
-        print("--table mxfp4 runs on the row-major table (use --layout rows)", file=sys.stderr)
         return 2
     if gather and layout != "rows":
         print("--draft-source gather runs on the row-major head (use --layout rows)",
@@ -152,6 +150,11 @@ def main() -> int:
     ids_d = up(ids, np.int32)
     tables = []
     for _ in range(max(1, args.table_copies)):
+        if fp4 and layout == "tiled":
+            tq, ts = mtp.alloc_tiled_mxfp4(wk.C, wk.H, dev)
+            mtp.mtp_pack_tiled_mxfp4(head_d, ids_d, tq, ts)
+            tables.append((tq, ts))
+            continue
         if fp4:
             tq = torch.empty((wk.C, wk.H // 2), dtype=torch.uint8, device=dev)
             ts = torch.empty((wk.C, wk.H // 32), dtype=torch.uint8, device=dev)
@@ -208,7 +211,10 @@ def main() -> int:
                   for c in range(wk.draft_calls)] if gather else None
 
     def draft_call(c, table):
-        if fp4:
+        if fp4 and layout == "tiled":
+            mtp.mtp_draft_argmax_tiled_mxfp4(h_d[c], table[0], table[1], wk.C, ids_d, out_ids[c],
+                                             out_logit[c], ws=ws_d)
+        elif fp4:
             mtp.mtp_draft_argmax_mxfp4(h_d[c], table[0], table[1], ids_d, out_ids[c],
                                        out_logit[c], ws=ws_d)
         elif fp8 and layout == "rows":
@@ -367,7 +373,10 @@ def main() -> int:
         a8 = torch.empty(n_rows, dtype=torch.int32, device=dev)
         a16 = torch.empty(n_rows, dtype=torch.int32, device=dev)
         ws_x = mtp.alloc_workspace(mtp.mtp_draft_workspace_bytes(n_rows, wk.C, wk.H), dev)
-        if fp4:
+        if fp4 and layout == "tiled":
+            mtp.mtp_draft_argmax_tiled_mxfp4(hx, tables[0][0], tables[0][1], wk.C, ids_d, a8,
+                                             ws=ws_x)
+        elif fp4:
             mtp.mtp_draft_argmax_mxfp4(hx, tables[0][0], tables[0][1], ids_d, a8, ws=ws_x)
         elif layout == "rows":
             mtp.mtp_draft_argmax_fp8(hx, tables[0][0], tables[0][1], ids_d, a8, ws=ws_x)

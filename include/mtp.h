@@ -371,6 +371,43 @@ mtp_status mtp_draft_argmax_mxfp4_cfg(const mtp_bf16 *hidden, int M, int H,
                                       hipStream_t stream, const mtp_config *cfg);
 
 /*
+ * MXFP4 candidate table in the tiled layout (batched draft rows: the
+ * matrix-core kernel). Same codes and scales as mtp_pack_candidates_mxfp4,
+ * stored for the 64-row tiled kernel: rows in tiles of 64 (zero rows pad the
+ * last), columns padded with zeros to a multiple of 256 and grouped in fours
+ * of 32-column steps.
+ *   - codes: fragment (t, p, rb), 1 KiB, ordered (t, p, rb); lane j + 16g
+ *     holds, for u = 0..3, 4 bytes (8 codes, the even element in the low
+ *     nibble) of row 64t + 16rb + j at columns 32(4p + u) + 8g .. + 7;
+ *   - scales: group (t, p), 256 bytes, ordered (t, p); byte rb*64 + j*4 + u
+ *     is the E8M0 code of row 64t + 16rb + j, block 4p + u. Padding blocks
+ *     have zero codes and scale code 0.
+ * The kernel converts each step's codes with their block's scale into the
+ * bf16 operand of one v_mfma_f32_16x16x32_bf16 step (exact), so the logits
+ * are those of the bf16 tiled kernel over the dequantised rows.
+ * mtp_tiled_mxfp4_bytes(R, H) = ceil64(R) * ceil256(H) / 2 and
+ * mtp_tiled_mxfp4_scale_bytes(R, H) = ceil64(R) * ceil256(H) / 32 (0 if out
+ * of range; H a multiple of 32). The draft takes up to 64 hidden rows per
+ * pass (more take further passes); cfg->path MTP_PATH_VALU gives
+ * MTP_ERR_UNSUPPORTED.
+ */
+size_t mtp_tiled_mxfp4_bytes(int64_t rows, int H);
+size_t mtp_tiled_mxfp4_scale_bytes(int64_t rows, int H);
+mtp_status mtp_pack_tiled_mxfp4(const mtp_bf16 *head, int64_t V, int H, const int32_t *ids,
+                                int64_t C, void *tiled_q, size_t q_bytes, uint8_t *tiled_scales,
+                                size_t scale_bytes, hipStream_t stream);
+mtp_status mtp_draft_argmax_tiled_mxfp4(const mtp_bf16 *hidden, int M, int H,
+                                        const void *table_q, const uint8_t *tiled_scales,
+                                        const int32_t *ids, int64_t C, int32_t *out_ids,
+                                        float *out_logit, void *ws, size_t ws_bytes,
+                                        hipStream_t stream);
+mtp_status mtp_draft_argmax_tiled_mxfp4_cfg(const mtp_bf16 *hidden, int M, int H,
+                                            const void *table_q, const uint8_t *tiled_scales,
+                                            const int32_t *ids, int64_t C, int32_t *out_ids,
+                                            float *out_logit, void *ws, size_t ws_bytes,
+                                            hipStream_t stream, const mtp_config *cfg);
+
+/*
  * FP8 candidate table in the tiled layout (batched draft rows: the
  * matrix-core kernel). Same codes and scales as mtp_pack_candidates_fp8,
  * stored as the fp8 form of the 64-row tiled layout: rows in tiles of 64

@@ -568,6 +568,76 @@ mtp_status mtp_draft_argmax_mxfp4(const mtp_bf16 *hidden, int M, int H, const ui
                                     ws_bytes, stream, nullptr);
 }
 
+size_t mtp_tiled_mxfp4_bytes(int64_t rows, int H) {
+  if (rows < 1 || rows > INT32_MAX || H < 32 || H > MTP_MAX_HIDDEN || H % 32 != 0) return 0;
+  return (size_t)mtp::tiled_rows(rows) * (size_t)(mtp::tiled_cols_fp4(H) / 2);
+}
+
+size_t mtp_tiled_mxfp4_scale_bytes(int64_t rows, int H) {
+  if (mtp_tiled_mxfp4_bytes(rows, H) == 0) return 0;
+  return (size_t)mtp::tiled_rows(rows) * (size_t)(mtp::tiled_cols_fp4(H) / 32);
+}
+
+mtp_status mtp_pack_tiled_mxfp4(const mtp_bf16 *head, int64_t V, int H, const int32_t *ids,
+                                int64_t C, void *tiled_q, size_t q_bytes, uint8_t *tiled_scales,
+                                size_t scale_bytes, hipStream_t stream) {
+  if (!head || !tiled_q || !tiled_scales) return MTP_ERR_INVALID_ARG;
+  if (V < 1 || V > INT32_MAX || (!ids && C > V)) return MTP_ERR_INVALID_ARG;
+  const size_t need = mtp_tiled_mxfp4_bytes(C, H);
+  if (need == 0 || q_bytes < need || scale_bytes < mtp_tiled_mxfp4_scale_bytes(C, H))
+    return MTP_ERR_INVALID_ARG;
+  if (!aligned(head, 16) || !aligned(tiled_q, 16) || !aligned(tiled_scales, 4) ||
+      (ids && !aligned(ids, 4)))
+    return MTP_ERR_INVALID_ARG;
+  int cus = 0;
+  hipError_t e = current_cus(&cus);
+  if (e != hipSuccess) return hip_fail(e);
+  e = mtp::launch_pack_tiled_mxfp4(head, V, H, ids, C, tiled_q, tiled_scales, cus, stream);
+  if (e != hipSuccess) return hip_fail(e);
+  return MTP_OK;
+}
+
+mtp_status mtp_draft_argmax_tiled_mxfp4_cfg(const mtp_bf16 *hidden, int M, int H,
+                                            const void *table_q, const uint8_t *tiled_scales,
+                                            const int32_t *ids, int64_t C, int32_t *out_ids,
+                                            float *out_logit, void *ws, size_t ws_bytes,
+                                            hipStream_t stream, const mtp_config *cfg) {
+  if (!tiled_scales || !aligned(tiled_scales, 4) || H % 32 != 0) return MTP_ERR_INVALID_ARG;
+  mtp_status st =
+      check_draft_args(hidden, M, H, table_q, ids, C, out_ids, out_logit, ws, ws_bytes, cfg);
+  if (st != MTP_OK) return st;
+  if (cfg && cfg->path == MTP_PATH_VALU) return MTP_ERR_UNSUPPORTED;
+  int cus = 0;
+  hipError_t e = current_cus(&cus);
+  if (e != hipSuccess) return hip_fail(e);
+  const int nb = mtp::dma_nb_for_fp4(M);
+  // 16-row passes: two workgroups per CU (their 128-row tiles fit twice)
+  const int per_cu = (cfg && cfg->blocks_per_cu > 0) ? cfg->blocks_per_cu : (nb == 1 ? 2 : 1);
+  mtp::DmaLaunch L;
+  L.X = hidden;
+  L.WT = table_q;
+  L.M = M;
+  L.N = C;
+  L.nch = H / 8;
+  L.S = mtp::tiled_cols_fp4(H) / 32;
+  L.max_blocks_x = per_cu * cus;
+  L.sink = draft_sink(ws, ids, out_ids, out_logit, M);
+  L.stream = stream;
+  L.scales = reinterpret_cast<const float *>(tiled_scales);
+  e = mtp::launch_dma_fp4(L, nb);
+  if (e != hipSuccess) return hip_fail(e);
+  return MTP_OK;
+}
+
+mtp_status mtp_draft_argmax_tiled_mxfp4(const mtp_bf16 *hidden, int M, int H,
+                                        const void *table_q, const uint8_t *tiled_scales,
+                                        const int32_t *ids, int64_t C, int32_t *out_ids,
+                                        float *out_logit, void *ws, size_t ws_bytes,
+                                        hipStream_t stream) {
+  return mtp_draft_argmax_tiled_mxfp4_cfg(hidden, M, H, table_q, tiled_scales, ids, C, out_ids,
+                                          out_logit, ws, ws_bytes, stream, nullptr);
+}
+
 size_t mtp_tiled_fp8_bytes(int64_t rows, int H) {
   if (rows < 1 || rows > INT32_MAX || H < 16 || H > MTP_MAX_HIDDEN || H % 16 != 0) return 0;
   return (size_t)mtp::tiled_rows(rows) * (size_t)mtp::tiled_cols(H);

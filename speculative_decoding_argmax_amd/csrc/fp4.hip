@@ -34,15 +34,6 @@ typedef unsigned u32x4_fp4_t __attribute__((ext_vector_type(4)));
 
 // ---- quantising pack ------------------------------------------------------
 
-__device__ __forceinline__ uint32_t wave_max_u32_fp4(uint32_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const uint32_t o = (uint32_t)__shfl_xor((int)v, off, kWave);
-    v = o > v ? o : v;
-  }
-  return v;
-}
-
 // Scale exponent of a block from the bf16 bits of its largest magnitude
 // (0: all-zero block).
 __device__ __forceinline__ int mx_exponent(uint32_t mx) {
@@ -120,6 +111,85 @@ hipError_t launch_pack_mxfp4(const void *head, int64_t V, int H, const int32_t *
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL(pack_mxfp4, dim3((unsigned)blocks), dim3(256), 0, stream,
                      (const uint4 *)head, V, H, ids, C, (uint4 *)q, scales);
+  return hipGetLastError();
+}
+
+// MXFP4 tiled layout (batched draft rows on the matrix cores): rows in tiles
+// of 64 (zero rows pad the last), columns padded with zeros to a multiple of
+// 256 and grouped in fours of 32-column steps. Code fragment (t, p, rb), 1 KiB,
+// ordered (t, p, rb): lane j + 16g holds, for u = 0..3, 4 bytes (8 codes, the
+// even element in the low nibble) of row 64t + 16rb + j at columns
+// 32(4p + u) + 8g .. 32(4p + u) + 8g + 7. Scale group (t, p), 256 bytes: byte
+// rb * 64 + j * 4 + u is the E8M0 code of that row's block 4p + u. One wave
+// per row (padding rows included), one 32-element block per lane and step;
+// padding blocks get zero codes and scale code 0.
+__global__ void __launch_bounds__(256)
+    pack_tiled_mxfp4(const uint4 *__restrict__ head, int64_t V, int H,
+                     const int32_t *__restrict__ ids, int64_t C, int64_t Cp, int Hp,
+                     uint8_t *__restrict__ tiled, uint8_t *__restrict__ tscales) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t waves = (int64_t)gridDim.x * (blockDim.x / kWave);
+  const int nblk = H / 32;
+  const int nblkp = Hp / 32;
+  const int SP = Hp / 128;
+  for (int64_t row = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave; row < Cp;
+       row += waves) {
+    const int64_t id = row < C ? (ids ? (int64_t)ids[row] : row) : -1;
+    const bool valid = id >= 0 && id < V;
+    const uint4 *src = head + (valid ? id : 0) * (int64_t)(H / 8);
+    const int64_t t = row / 64;
+    const int rb = (int)((row % 64) / 16);
+    const int j = (int)(row % 16);
+    for (int b = lane; b < nblkp; b += kWave) {
+      uint32_t words[4] = {0u, 0u, 0u, 0u};
+      int e = -127;
+      if (valid && b < nblk) {
+        uint32_t w[16];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint4 v = src[4 * b + k];
+          w[4 * k] = v.x;
+          w[4 * k + 1] = v.y;
+          w[4 * k + 2] = v.z;
+          w[4 * k + 3] = v.w;
+        }
+        uint32_t mx = 0;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          const uint32_t lo = w[k] & 0x7FFFu, hi = (w[k] >> 16) & 0x7FFFu;
+          mx = lo > mx ? lo : mx;
+          mx = hi > mx ? hi : mx;
+        }
+        e = mx_exponent(mx);
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          const uint32_t byte = e2m1_code(w[k] & 0xFFFFu, e) | (e2m1_code(w[k] >> 16, e) << 4);
+          words[k >> 2] |= byte << (8 * (k & 3));
+        }
+      }
+      const int p = b / 4;
+      const int u = b % 4;
+      const int64_t frag = (t * SP + p) * 4 + rb;
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<uint32_t *>(tiled + (frag * kWave + j + 16 * g) * 16 + 4 * u) = words[g];
+      tscales[(t * SP + p) * 256 + rb * 64 + j * 4 + u] = (uint8_t)(e + 127);
+    }
+  }
+}
+
+hipError_t launch_pack_tiled_mxfp4(const void *head, int64_t V, int H, const int32_t *ids,
+                                   int64_t C, void *tiled, uint8_t *tscales, int num_cus,
+                                   hipStream_t stream) {
+  const int64_t Cp = (C + 63) / 64 * 64;
+  const int Hp = (H + 255) / 256 * 256;
+  const int64_t waves_per_block = 4;
+  int64_t blocks = (Cp + waves_per_block - 1) / waves_per_block;
+  const int64_t cap = (int64_t)num_cus * 8;
+  if (blocks > cap) blocks = cap;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(pack_tiled_mxfp4, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     (const uint4 *)head, V, H, ids, C, Cp, Hp, (uint8_t *)tiled, tscales);
   return hipGetLastError();
 }
 

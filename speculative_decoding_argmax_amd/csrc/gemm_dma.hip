@@ -83,14 +83,23 @@ __device__ __forceinline__ void wait_vmcnt() {
 // fragment carries two 32-column steps of a 16-row block: lane j + 16g holds
 // the 8 codes of step 2p, columns 8g..8g+7, then those of step 2p + 1), and
 // scales[row] multiplies each finished logit.
-template <int NB, int RW, int KS, int NBUF, int WV, int CP, bool FP8 = false>
+// FP4: the table holds MXFP4 codes in the MXFP4 tiled layout (one 1 KiB
+// fragment carries four steps: lane j + 16g holds 4 bytes, 8 codes, per step)
+// and `scales` points at its scale groups (256 bytes per 64 rows and four
+// steps); each step's codes are converted with their block's scale into the
+// bf16 operand (exact), so no scale touches the logit.
+template <int NB, int RW, int KS, int NBUF, int WV, int CP, bool FP8 = false, bool FP4 = false>
 __global__ void __launch_bounds__(WV * 64)
     gemm_argmax_dma(const uint4 *__restrict__ X, const uint4 *__restrict__ WT, int M, int N,
                     int nch, int S, RowSink sink, const float *__restrict__ scales) {
   constexpr int RBT = WV * RW;                 // 16-row blocks per workgroup tile
   constexpr int TV = RBT * 16;                 // table rows per workgroup tile
   static_assert(!FP8 || KS % 2 == 0, "fp8 chunks hold whole step pairs");
-  constexpr int AF = FP8 ? RBT * KS / 2 : RBT * KS;  // weight fragments per chunk
+  static_assert(!FP4 || KS % 4 == 0, "fp4 chunks hold whole step groups");
+  static_assert(!(FP8 && FP4), "one table format");
+  static_assert(!FP4 || (RBT / 4) * (KS / 4) <= WV, "one wave per scale piece");
+  // weight fragments per chunk
+  constexpr int AF = FP4 ? RBT * KS / 4 : FP8 ? RBT * KS / 2 : RBT * KS;
   constexpr int FR = AF + KS * NB;             // fragments per chunk
   constexpr int PER_WAVE = (FR + WV - 1) / WV; // copies per wave per chunk
   static_assert(NBUF >= 3 && NBUF <= 4, "three or four slots");
@@ -109,6 +118,14 @@ __global__ void __launch_bounds__(WV * 64)
   __shared__ float scale1[SCN];
   __shared__ float scale2[SCN];
   __shared__ float scale3[NBUF > 3 ? SCN : 1];
+  // fp4: the scale groups of a chunk, one 256-byte piece per 64-row tile and
+  // step group, copied with the chunk into the slot's array
+  constexpr int NPC = FP4 ? (RBT / 4) * (KS / 4) : 0;   // pieces per chunk
+  constexpr int SC4 = FP4 ? NPC * 64 : 1;               // 32-bit words per slot
+  __shared__ uint32_t s4_0[SC4];
+  __shared__ uint32_t s4_1[SC4];
+  __shared__ uint32_t s4_2[SC4];
+  __shared__ uint32_t s4_3[NBUF > 3 ? SC4 : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -134,6 +151,13 @@ __global__ void __launch_bounds__(WV * 64)
     else if constexpr (SL == 1) return slot1;
     else if constexpr (SL == 2) return slot2;
     else return slot3;
+  };
+  auto scl4 = [&](auto tag) -> uint32_t * {
+    constexpr int SL = decltype(tag)::value;
+    if constexpr (SL == 0) return s4_0;
+    else if constexpr (SL == 1) return s4_1;
+    else if constexpr (SL == 2) return s4_2;
+    else return s4_3;
   };
   auto scl = [&](auto tag) -> float * {
     constexpr int SL = decltype(tag)::value;
@@ -162,12 +186,13 @@ __global__ void __launch_bounds__(WV * 64)
       int f = wave + WV * q;
       f = f < FR ? f : FR - 1;
       if (f < AF) {
-        const int s = f / RBT;                 // step (bf16) or step pair (fp8) of the chunk
+        const int s = f / RBT;  // step (bf16), step pair (fp8) or step group (fp4) of the chunk
         int rb = tile * RBT + f % RBT;
         rb = rb < nrb ? rb : nrb - 1;          // past the table: valid, never reported
         const uint4 *src =
-            FP8 ? WT + (((int64_t)(rb >> 2) * (S / 2) + c * (KS / 2) + s) * 4 + (rb & 3)) * kWave + lane
-                : WT + (((int64_t)(rb >> 2) * S + c * KS + s) * 4 + (rb & 3)) * kWave + lane;
+            FP4   ? WT + (((int64_t)(rb >> 2) * (S / 4) + c * (KS / 4) + s) * 4 + (rb & 3)) * kWave + lane
+            : FP8 ? WT + (((int64_t)(rb >> 2) * (S / 2) + c * (KS / 2) + s) * 4 + (rb & 3)) * kWave + lane
+                  : WT + (((int64_t)(rb >> 2) * S + c * KS + s) * 4 + (rb & 3)) * kWave + lane;
         __builtin_amdgcn_global_load_lds((const void *)src, MTP_LDS(base + f * kWave), 16, 0, CP);
       } else {
         const int fb = f - AF;
@@ -180,6 +205,18 @@ __global__ void __launch_bounds__(WV * 64)
         const int col = min((c * KS + s) * 4 + g, nch - 1);
         const uint4 *src = X + (int64_t)m * nch + col;
         __builtin_amdgcn_global_load_lds((const void *)src, MTP_LDS(base + f * kWave), 16, 0, 0);
+      }
+    }
+    if constexpr (FP4) {
+      // every chunk brings its scale groups: wave w < NPC copies piece w
+      // (64-row tile w / (KS/4) of the workgroup tile, step group w % (KS/4));
+      // issued after the chunk's fragments, so the chunk's wait covers it
+      if (wave < NPC) {
+        int t64 = tile * (RBT / 4) + wave / (KS / 4);
+        t64 = t64 < nrb / 4 ? t64 : nrb / 4 - 1;  // past the table: valid, never reported
+        const uint32_t *src = reinterpret_cast<const uint32_t *>(scales) +
+                              ((int64_t)t64 * (S / 4) + c * (KS / 4) + wave % (KS / 4)) * kWave + lane;
+        __builtin_amdgcn_global_load_lds((const void *)src, MTP_LDS(scl4(tag) + wave * 64), 4, 0, 0);
       }
     }
     if constexpr (FP8) {
@@ -226,12 +263,30 @@ __global__ void __launch_bounds__(WV * 64)
     const uint4 *A = slot(tag);
     const uint4 *Bf = A + AF * kWave;
     uint4 raw[RW];
+    uint32_t sc4[RW];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       uint4 a[RW];
 #pragma unroll
       for (int rw = 0; rw < RW; ++rw) {
-        if constexpr (FP8) {
+        if constexpr (FP4) {
+          // one fragment and one scale word per step group; each step's 4
+          // code bytes become that step's bf16 operand, scaled by its block's
+          // 2^e inside the conversion (exact)
+          const int blk = wave * RW + rw;
+          if (s % 4 == 0) {
+            raw[rw] = A[((s / 4) * RBT + blk) * kWave + lane];
+            sc4[rw] = scl4(tag)[((blk / 4) * (KS / 4) + s / 4) * 64 + (blk % 4) * 16 + j];
+          }
+          const uint32_t cw = s % 4 == 0 ? raw[rw].x : s % 4 == 1 ? raw[rw].y : s % 4 == 2 ? raw[rw].z : raw[rw].w;
+          const uint32_t code = (sc4[rw] >> (8 * (s % 4))) & 0xFFu;
+          const float sf = __uint_as_float(code ? code << 23 : 0x00400000u);
+          a[rw] = make_uint4(
+              __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, sf, 0)),
+              __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, sf, 1)),
+              __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, sf, 2)),
+              __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, sf, 3)));
+        } else if constexpr (FP8) {
           // one read per step pair; each half converts to that step's
           // bf16 operand (E4M3 -> bf16 is exact)
           if (s % 2 == 0) raw[rw] = A[((s / 2) * RBT + wave * RW + rw) * kWave + lane];
@@ -567,13 +622,13 @@ __global__ void __launch_bounds__(WV * 64)
 int64_t tiled_rows(int64_t rows) { return (rows + 63) / 64 * 64; }
 int tiled_cols(int H) { return (H + 127) / 128 * 128; }
 
-template <int NB, int RW, int KS, int NBUF, int WV, int CP, bool FP8 = false>
+template <int NB, int RW, int KS, int NBUF, int WV, int CP, bool FP8 = false, bool FP4 = false>
 static hipError_t launch_dma_cfg(const DmaLaunch &L) {
   constexpr int TV = WV * RW * 16;
   const int64_t ntiles = (L.N + TV - 1) / TV;
   const int gx = (int)(ntiles < L.max_blocks_x ? ntiles : L.max_blocks_x);
   const int gy = (L.M + NB * 16 - 1) / (NB * 16);
-  hipLaunchKernelGGL((gemm_argmax_dma<NB, RW, KS, NBUF, WV, CP, FP8>), dim3(gx, gy),
+  hipLaunchKernelGGL((gemm_argmax_dma<NB, RW, KS, NBUF, WV, CP, FP8, FP4>), dim3(gx, gy),
                      dim3(WV * 64), 0, L.stream, (const uint4 *)L.X, (const uint4 *)L.WT, L.M,
                      (int)L.N, L.nch, L.S, L.sink, L.scales);
   return hipGetLastError();
@@ -644,6 +699,31 @@ hipError_t launch_dma(const DmaLaunch &L, int nb) {
 int dma_nb_for_fp8(int M) {
   const int need = (M + 15) / 16;
   return need < 4 ? need : 4;
+}
+
+// MXFP4 tiled tables (columns padded to a multiple of 256): hidden-row blocks
+// per pass 1..4. With a quarter of the bf16 bytes per step, chunks hold one
+// or two step groups (4 or 8 steps). Shapes from a sweep on MI355X (65,536
+// rows; all bit-identical): 16 rows at H = 4,096 run 29.9 us with 128-row
+// tiles, 8-step chunks and two workgroups per CU, against 31.8 us with
+// 256-row tiles; 32 rows at H = 5,120 run 40.0 us with 4-step chunks in four
+// slots, against 41.0 us with 8-step chunks in three.
+int dma_nb_for_fp4(int M) {
+  const int need = (M + 15) / 16;
+  return need < 4 ? need : 4;
+}
+
+int tiled_cols_fp4(int H) { return (H + 255) / 256 * 256; }
+
+hipError_t launch_dma_fp4(const DmaLaunch &L, int nb) {
+  constexpr int NT = 2;
+  switch (nb) {
+    case 1: return launch_dma_cfg<1, 1, 8, 3, 8, NT, false, true>(L);
+    case 2: return launch_dma_cfg<2, 2, 4, 4, 8, NT, false, true>(L);
+    case 3: return launch_dma_cfg<3, 4, 4, 3, 8, NT, false, true>(L);
+    case 4: return launch_dma_cfg<4, 4, 4, 3, 8, NT, false, true>(L);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_dma_fp8(const DmaLaunch &L, int nb) {

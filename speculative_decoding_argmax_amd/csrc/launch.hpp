@@ -68,6 +68,12 @@ hipError_t launch_dma(const DmaLaunch &L, int nb);
 size_t ring_stage_bytes(int M, int H);
 int dma_nb_for_fp8(int M);
 hipError_t launch_dma_fp8(const DmaLaunch &L, int nb);
+int dma_nb_for_fp4(int M);
+int tiled_cols_fp4(int H);
+hipError_t launch_dma_fp4(const DmaLaunch &L, int nb);
+hipError_t launch_pack_tiled_mxfp4(const void *head, int64_t V, int H, const int32_t *ids,
+                                   int64_t C, void *tiled, uint8_t *tscales, int num_cus,
+                                   hipStream_t stream);
 hipError_t launch_pack_tiled_fp8(const void *head, int64_t V, int H, const int32_t *ids,
                                  int64_t C, void *tiled, float *scales, int num_cus,
                                  hipStream_t stream);

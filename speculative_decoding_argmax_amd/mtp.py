@@ -97,6 +97,11 @@ def _load() -> ctypes.CDLL:
         "mtp_draft_argmax_fp8": ([P, I, I, P, P, P, I64, P, P, P, S, P], I),
         "mtp_draft_argmax_fp8_cfg": ([P, I, I, P, P, P, I64, P, P, P, S, P, P], I),
         "mtp_tiled_fp8_bytes": ([I64, I], S),
+        "mtp_tiled_mxfp4_bytes": ([I64, I], S),
+        "mtp_tiled_mxfp4_scale_bytes": ([I64, I], S),
+        "mtp_pack_tiled_mxfp4": ([P, I64, I, P, I64, P, S, P, S, P], I),
+        "mtp_draft_argmax_tiled_mxfp4": ([P, I, I, P, P, P, I64, P, P, P, S, P], I),
+        "mtp_draft_argmax_tiled_mxfp4_cfg": ([P, I, I, P, P, P, I64, P, P, P, S, P, P], I),
         "mtp_pack_tiled_fp8": ([P, I64, I, P, I64, P, S, P, P], I),
         "mtp_draft_argmax_tiled_fp8": ([P, I, I, P, P, P, I64, P, P, P, S, P], I),
         "mtp_draft_argmax_tiled_fp8_cfg": ([P, I, I, P, P, P, I64, P, P, P, S, P, P], I),
@@ -491,6 +496,64 @@ def mtp_draft_argmax_mxfp4(hidden, table_q, scales, ids, out_ids, out_logit=None
         _ptr(out_logit, "out_logit", (torch.float32,), allow_none=True),
         _ptr(ws, "ws", (torch.int64, torch.uint8, torch.int32)), ws.numel() * ws.element_size(),
         _stream(stream), ctypes.byref(cfg)), "mtp_draft_argmax_mxfp4")
+
+
+def mtp_tiled_mxfp4_bytes(rows: int, H: int) -> int:
+    return int(lib.mtp_tiled_mxfp4_bytes(rows, H))
+
+
+def mtp_tiled_mxfp4_scale_bytes(rows: int, H: int) -> int:
+    return int(lib.mtp_tiled_mxfp4_scale_bytes(rows, H))
+
+
+def alloc_tiled_mxfp4(rows: int, H: int, device=None):
+    """uint8 buffers for an MXFP4 tiled table of `rows` rows: codes, scales."""
+    torch = _torch()
+    n = mtp_tiled_mxfp4_bytes(rows, H)
+    if n == 0:
+        raise ValueError("unsupported MXFP4 tiled shape")
+    return (torch.empty(n, dtype=torch.uint8, device=device or "cuda"),
+            torch.empty(mtp_tiled_mxfp4_scale_bytes(rows, H), dtype=torch.uint8,
+                        device=device or "cuda"))
+
+
+def mtp_pack_tiled_mxfp4(head, ids, tiled_q, tiled_scales, C: Optional[int] = None,
+                         stream=None) -> None:
+    torch = _torch()
+    V, H = head.shape
+    C = ids.numel() if ids is not None else (V if C is None else C)
+    _check(lib.mtp_pack_tiled_mxfp4(
+        _ptr(head, "head", _bf16_types()), V, H, _ptr(ids, "ids", (torch.int32,), allow_none=True),
+        C, _ptr(tiled_q, "tiled_q", (torch.uint8,)), tiled_q.numel(),
+        _ptr(tiled_scales, "tiled_scales", (torch.uint8,)), tiled_scales.numel(),
+        _stream(stream)), "mtp_pack_tiled_mxfp4")
+
+
+def mtp_draft_argmax_tiled_mxfp4(hidden, table_q, tiled_scales, C: int, ids, out_ids,
+                                 out_logit=None, ws=None, stream=None,
+                                 path: int = MTP_PATH_AUTO, blocks_per_cu: int = 0) -> None:
+    """Draft over an MXFP4 tiled candidate table of C rows (matrix cores)."""
+    torch = _torch()
+    M, H = hidden.shape
+    if table_q.numel() < mtp_tiled_mxfp4_bytes(C, H) or \
+            tiled_scales.numel() < mtp_tiled_mxfp4_scale_bytes(C, H):
+        raise ValueError("tiled table smaller than C rows")
+    if ids is not None and ids.numel() != C:
+        raise ValueError("ids must have C entries")
+    if out_ids.numel() != M or (out_logit is not None and out_logit.numel() != M):
+        raise ValueError("outputs must have M entries")
+    if ws is None:
+        _no_alloc_in_capture("mtp_draft_argmax_tiled_mxfp4")
+        ws = alloc_workspace(mtp_draft_workspace_bytes(M, C, H), hidden.device, stream)
+    cfg = _cfg(path, blocks_per_cu)
+    _check(lib.mtp_draft_argmax_tiled_mxfp4_cfg(
+        _ptr(hidden, "hidden", _bf16_types()), M, H, _ptr(table_q, "table_q", (torch.uint8,)),
+        _ptr(tiled_scales, "tiled_scales", (torch.uint8,)),
+        _ptr(ids, "ids", (torch.int32,), allow_none=True), C,
+        _ptr(out_ids, "out_ids", (torch.int32,)),
+        _ptr(out_logit, "out_logit", (torch.float32,), allow_none=True),
+        _ptr(ws, "ws", (torch.int64, torch.uint8, torch.int32)), ws.numel() * ws.element_size(),
+        _stream(stream), ctypes.byref(cfg)), "mtp_draft_argmax_tiled_mxfp4")
 
 
 def mtp_tiled_fp8_bytes(rows: int, H: int) -> int:

@@ -300,3 +300,30 @@ def test_mxfp4_entry_points_reject_bad_arguments():
     c = mtp.mtp_config()
     c.path = mtp.MTP_PATH_MFMA
     assert mtp.lib.mtp_draft_argmax_mxfp4_cfg(*dk, ctypes.byref(c)) == mtp.MTP_ERR_UNSUPPORTED
+
+
+def test_tiled_mxfp4_entry_points_reject_bad_arguments():
+    assert mtp.mtp_tiled_mxfp4_bytes(100, 2048) == 128 * 1024
+    assert mtp.mtp_tiled_mxfp4_scale_bytes(100, 2048) == 128 * 64
+    assert mtp.mtp_tiled_mxfp4_bytes(65, 96) == 128 * 128      # columns pad to 256
+    assert mtp.mtp_tiled_mxfp4_bytes(100, 48) == 0              # H % 32 != 0
+    assert mtp.mtp_tiled_mxfp4_scale_bytes(0, 64) == 0
+    p = mtp.lib.mtp_pack_tiled_mxfp4
+    nq, ns = mtp.mtp_tiled_mxfp4_bytes(50, 64), mtp.mtp_tiled_mxfp4_scale_bytes(50, 64)
+    ok = (FAKE, 100, 64, FAKE, 50, FAKE, nq, FAKE, ns, None)
+    assert p(None, *ok[1:]) == INVALID
+    assert p(*ok[:2], 48, *ok[3:]) == INVALID                   # H % 32
+    assert p(*ok[:3], None, 101, *ok[5:]) == INVALID            # C > V without ids
+    assert p(*ok[:6], nq - 1, *ok[7:]) == INVALID               # codes buffer too small
+    assert p(*ok[:8], ns - 1, None) == INVALID                  # scale buffer too small
+    assert p(*ok[:7], None, ns, None) == INVALID                # no scales
+    assert p(*ok[:5], P(0x10008), *ok[6:]) == INVALID           # codes not 16-byte aligned
+    d = mtp.lib.mtp_draft_argmax_tiled_mxfp4
+    dk = (FAKE, 1, 64, FAKE, FAKE, None, 100, FAKE, None, FAKE, 4096, None)
+    assert d(*dk[:2], 48, *dk[3:]) == INVALID
+    assert d(*dk[:4], None, *dk[5:]) == INVALID                 # no scales
+    assert d(*dk[:9], None, *dk[10:]) == mtp.MTP_ERR_WORKSPACE
+    c = mtp.mtp_config()
+    c.path = mtp.MTP_PATH_VALU
+    assert mtp.lib.mtp_draft_argmax_tiled_mxfp4_cfg(*dk, ctypes.byref(c)) == \
+        mtp.MTP_ERR_UNSUPPORTED
