@@ -327,3 +327,25 @@ def test_tiled_mxfp4_entry_points_reject_bad_arguments():
     c.path = mtp.MTP_PATH_VALU
     assert mtp.lib.mtp_draft_argmax_tiled_mxfp4_cfg(*dk, ctypes.byref(c)) == \
         mtp.MTP_ERR_UNSUPPORTED
+
+
+def test_binding_fails_loudly_without_the_library(tmp_path):
+    """With no built library the binding refuses to import (no CPU fallback):
+    a copy of the package's Python files without lib/ raises ImportError
+    naming the missing library."""
+    import os
+    import shutil
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    src = os.path.join(root, "speculative_decoding_argmax_amd")
+    dst = tmp_path / "speculative_decoding_argmax_amd"
+    dst.mkdir()
+    for name in os.listdir(src):
+        if name.endswith(".py"):
+            shutil.copy(os.path.join(src, name), dst / name)
+    code = "from speculative_decoding_argmax_amd import mtp\n"
+    out = subprocess.run([sys.executable, "-c", code], cwd=str(tmp_path), capture_output=True,
+                         text=True, timeout=300, env={**os.environ, "PYTHONPATH": str(tmp_path)})
+    assert out.returncode != 0
+    assert "ImportError" in out.stderr and "not built" in out.stderr, out.stderr[-2000:]
