@@ -499,19 +499,25 @@ def cpu_baseline(wk, head, ids, hiddens, hv, drafts, budget_s):
     repeated until the time budget is spent (at least once)."""
     import oracle
     table = oracle.pack(head, ids)
-    times = []
+    times, draft_s, verify_s = [], [], []
     t_begin = time.perf_counter()
     while True:
         t0 = time.perf_counter()
         for h in hiddens:
+            t1 = time.perf_counter()
             oracle.draft(h, table, ids)
+            draft_s.append(time.perf_counter() - t1)
+        t1 = time.perf_counter()
         oracle.verify(hv, head, wk.B, wk.k, drafts)
+        verify_s.append(time.perf_counter() - t1)
         times.append(time.perf_counter() - t0)
         if time.perf_counter() - t_begin >= budget_s:
             break
     step_s = statistics.median(times)
     return {"value": round((wk.draft_calls + 1) / step_s, 3), "unit": "calls/s",
             "cores": oracle.threads(), "cpu_model": cpu_model(), "kind": "oracle",
+            "draft_ms_median": round(statistics.median(draft_s) * 1e3, 3),
+            "verify_ms_median": round(statistics.median(verify_s) * 1e3, 3),
             "sample": f"{len(times)} full {wk.name} step(s) ({wk.draft_calls} draft + 1 verify "
                       f"call), median {step_s:.3f} s per step"}
 
