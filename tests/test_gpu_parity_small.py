@@ -166,6 +166,32 @@ def test_determinism_across_launch_shapes(torch, mtp, path, M):
         assert np.array_equal(g["logit"].view(np.uint32), vref["logit"].view(np.uint32))
 
 
+@pytest.mark.parametrize("bpc", [1, 2, 4, 16])
+def test_draft_ids_large_table_ties(torch, mtp, bpc):
+    """A packed table with ids on the vector-ALU kernel at 150,000 rows, with
+    one to sixteen workgroups per CU (a wave then covers about 146 down to 10
+    rows). Each hidden row's winner is copied once far above and once far
+    below it, so exact ties span rows of different waves and workgroups; ids
+    and logits must be the oracle's bit for bit, ties to the lowest id."""
+    M, N, H = 3, 150_000, 256
+    seed = 777
+    x = wl.exact_grid_bf16((M, H), seed, 1)
+    w = wl.exact_grid_bf16((N, H), seed, 2)
+    ids = np.sort(wl.rng(seed, 3).choice(3 * N, size=N, replace=False)).astype(np.int32)
+    win = np.searchsorted(ids, oracle.draft(x, w, ids)["id"])
+    for m in range(M):
+        j = int(win[m])
+        for j2 in ((j + 140_000 + 31 * m) % N, (j + 70_000 + 17 * m) % N):
+            if j2 != j:
+                w[j2] = w[j]
+    g_ids, g_logit = gpu_draft(dev_bf16(x), dev_bf16(w), dev_i32(ids), path=PATHS["valu"],
+                               blocks_per_cu=bpc)
+    exact_logit_match(g_ids, g_logit, x, w, ids)
+    ref = oracle.draft(x, w, ids)
+    for m in range(M):
+        assert ref["runner_exact"][m] == ref["exact"][m]      # the planted tie holds
+
+
 def test_workspace_left_zeroed(torch, mtp):
     V, H, M = 9000, 1024, 5
     W_d = dev_bf16(wl.head_weights(V, H, 3))
