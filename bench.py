@@ -14,8 +14,8 @@ states, seeded sorted candidate subset), resident in HBM before timing. The
 draft calls of one step read three different copies of the candidate table, so
 no call is served from the 256 MB Infinity Cache by its predecessor; the
 verify head (>= 1 GB) cannot stay cached between steps. Kernel durations come
-from HIP events recorded around every launch on the launch stream inside the
-timed region. Prints one JSON line.
+from HIP events recorded on the launch stream around the draft block and the
+verify launch of every fifth timed step (--event-every). Prints one JSON line.
 """
 
 from __future__ import annotations
@@ -68,6 +68,8 @@ def parse_args():
     ap.add_argument("--graph", action="store_true",
                     help="time the steps as replays of a captured HIP graph (mtp_graph_*); "
                          "per-call durations still come from event-bracketed eager launches")
+    ap.add_argument("--event-every", type=int, default=5,
+                    help="record the per-call HIP events on every n-th timed step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall-clock budget of the CPU oracle sample")
@@ -285,22 +287,28 @@ def main() -> int:
             graphs[i % n_tab].launch()
         torch.cuda.synchronize()
 
+    # Per-call events go on every n-th timed step only: each recorded event
+    # costs the stream a few microseconds, which on every step would slow the
+    # whole job by about 4%.
+    every = max(1, args.event_every)
+
     def timed_steps(with_events: bool, use_graph: bool):
-        evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(K)] \
-            if with_events else None
+        evs = {i: tuple(torch.cuda.Event(enable_timing=True) for _ in range(3))
+               for i in range(0, K, every)} if with_events else {}
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(K):
+            ev = evs.get(i)
             if use_graph:
-                if evs:
-                    evs[i][0].record(stream)
+                if ev:
+                    ev[0].record(stream)
                 graphs[i % n_tab].launch()
-                if evs:
-                    evs[i][2].record(stream)
+                if ev:
+                    ev[2].record(stream)
             else:
-                step(i, evs[i] if evs else None)
+                step(i, ev)
         torch.cuda.synchronize()
-        return time.perf_counter() - t0, evs
+        return time.perf_counter() - t0, list(evs.values())
 
     t_total, evs = timed_steps(True, bool(graphs))
     graph_step_ms = None
@@ -312,8 +320,8 @@ def main() -> int:
 
     # per-call durations: the draft block's span over its calls (inter-kernel
     # gaps included), the verify launch's own span
-    draft_ms = [evs[i][0].elapsed_time(evs[i][1]) / wk.draft_calls for i in range(K)]
-    verify_ms = [evs[i][1].elapsed_time(evs[i][2]) for i in range(K)]
+    draft_ms = [e[0].elapsed_time(e[1]) / wk.draft_calls for e in evs]
+    verify_ms = [e[1].elapsed_time(e[2]) for e in evs]
 
     # Untimed context: the same steps without per-launch events, and the
     # draft call re-reading one table (Infinity Cache may serve part of it).
@@ -464,6 +472,7 @@ def main() -> int:
         "calls": {"draft": draft_stats, "verify": verify_stats},
         "context": {
             "ms_per_step_without_kernel_events": round(t_noev * 1000.0 / K, 4),
+            "kernel_event_steps": f"1 in {every} timed steps ({len(evs)} of {K})",
             "step_mode": "hip_graph" if graphs else "eager",
             "graph_step_us_mean": round(statistics.mean(graph_step_ms) * 1000.0, 2)
             if graph_step_ms else None,
