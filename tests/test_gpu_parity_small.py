@@ -53,6 +53,7 @@ EXACT_SHAPES = [  # (M, N, H)
     (8, 3001, 4096), (2, 999, 5120), (1, 257, 16384), (9, 2000, 512), (32, 5000, 1024),
     (5, 777, 3000), (1, 65, 24), (16, 1025, 640), (17, 333, 1032), (48, 2049, 4096),
     (160, 1111, 5120), (161, 300, 256), (64, 4000, 2048),
+    (4096, 3001, 256),  # the most hidden rows one call takes (MTP_MAX_ROWS)
 ]
 
 
@@ -78,7 +79,8 @@ def test_draft_exact_grid(torch, mtp, M, N, H, with_ids, path):
 
 @pytest.mark.parametrize("B,k,H,V", [(1, 3, 256, 4096), (3, 2, 1024, 5003), (2, 15, 512, 3001),
                                      (8, 3, 4096, 20000), (1, 0, 2048, 777), (5, 1, 8, 300),
-                                     (32, 4, 5120, 3000), (40, 3, 1024, 999)])
+                                     (32, 4, 5120, 3000), (40, 3, 1024, 999),
+                                     (256, 15, 256, 3000)])  # B * (k + 1) = MTP_MAX_ROWS
 @pytest.mark.parametrize("path", ["auto", "mfma"])
 def test_verify_exact_grid(torch, mtp, B, k, H, V, path):
     seed = 77 + B + k + H + V

@@ -90,7 +90,8 @@ def test_tiled_draft_exact_grid(torch, mtp, M, N, H, with_ids):
 
 
 @pytest.mark.parametrize("B,k,H,V", [(1, 3, 256, 4096), (8, 3, 4096, 20000), (32, 4, 5120, 3000),
-                                     (1, 0, 2048, 777), (40, 3, 1024, 999), (64, 3, 1000, 1234)])
+                                     (1, 0, 2048, 777), (40, 3, 1024, 999), (64, 3, 1000, 1234),
+                                     (256, 15, 256, 3000)])  # B * (k + 1) = MTP_MAX_ROWS
 def test_tiled_verify_exact_grid(torch, mtp, B, k, H, V):
     seed = 91 + B + k + H + V
     hv = wl.exact_grid_bf16((B * (k + 1), H), seed, 1)
