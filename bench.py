@@ -16,6 +16,11 @@ no call is served from the 256 MB Infinity Cache by its predecessor; the
 verify head (>= 1 GB) cannot stay cached between steps. Kernel durations come
 from HIP events recorded on the launch stream around the draft block and the
 verify launch of every fifth timed step (--event-every). Prints one JSON line.
+
+--workload draft_ablation adds context.draft_tables: the M = 1 draft timed over
+the full head, the 65,536-row and the nested 32,768-row tables (and the pages'
+per-rank shard shape, 32,768 x 2,560), with us per call, GB/s and the fraction
+of peak and of the streaming-read ceiling for each.
 """
 
 from __future__ import annotations
@@ -371,6 +376,12 @@ def main() -> int:
                    "head_bytes": int(head_bytes),
                    "head_GBps": stream_gbps([head_v], head_bytes, 20)}
 
+    # Draft-head ablation (workloads that list table sizes): the same M = 1
+    # draft over each table, plus the pages' per-rank shard shape as context.
+    draft_tables = None
+    if wk.tables:
+        draft_tables = draft_table_ablation(wk, mtp, wl, head_d, dev, up, sink, stream)
+
     agreement = None
     if fp8 or fp4:
         # how often the quantised draft picks the bf16 draft's token (512
@@ -480,6 +491,7 @@ def main() -> int:
             "single_call_us": {"draft": single_draft_us, "verify": single_verify_us},
             "stream_read": stream_read,
             "quantised_draft_agrees_with_bf16": agreement,
+            "draft_tables": draft_tables,
             "setup_s": round(setup_s, 1),
         },
         "roofline": roofline,
@@ -489,6 +501,70 @@ def main() -> int:
                                               args.cpu_seconds)
     print(json.dumps(result), flush=True)
     return 0
+
+
+def draft_table_ablation(wk, mtp, wl, head_d, dev, up, sink, stream, reps=200, copies=3):
+    """M = 1 draft calls over each table size of the ablation: the full head
+    (identity ids), the 65,536-row subset and the nested 32,768-row subset,
+    all at the workload's width, plus 32,768 rows x 2,560 (the pages' per-rank
+    draft shard, drawn as its own rows: no head of that width exists here).
+
+    Each size is packed ``copies`` times and the calls rotate over the copies,
+    so no call is served from the Infinity Cache its predecessor filled. One
+    event pair brackets ``reps`` back-to-back calls, so the time per call
+    includes the gaps between launches. The streaming-read probe over the same
+    bytes gives the practical read ceiling for each size.
+    """
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    shapes = [(n, wk.H) for n in wk.tables] + [(32_768, 2_560)]
+    out = []
+    for n, H in shapes:
+        if H == wk.H:
+            ids = (np.arange(wk.V, dtype=np.int32) if n == wk.V
+                   else wl.candidate_ids(wk.V, n, wk.seed))
+            ids_d = up(ids, np.int32)
+            tabs = []
+            for _ in range(copies):
+                t = torch.empty((n, H), dtype=torch.int16, device=dev)
+                mtp.mtp_pack_candidates(head_d, ids_d, t)
+                tabs.append(t)
+        else:
+            ids_d = up(wl.candidate_ids(wk.V, n, wk.seed), np.int32)
+            rows = up(wl.head_weights(n, H, wk.seed + 1))
+            tabs = [rows] + [rows.clone() for _ in range(copies - 1)]
+        h = up(wl.hidden_states(1, H, wk.seed, block=0))
+        oid = torch.empty(1, dtype=torch.int32, device=dev)
+        olog = torch.empty(1, dtype=torch.float32, device=dev)
+        ws = mtp.alloc_workspace(mtp.mtp_draft_workspace_bytes(1, n, H), dev)
+        for i in range(20):
+            mtp.mtp_draft_argmax(h, tabs[i % copies], ids_d, oid, olog, ws=ws)
+        e0.record(stream)
+        for i in range(reps):
+            mtp.mtp_draft_argmax(h, tabs[i % copies], ids_d, oid, olog, ws=ws)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1000.0 / reps
+        nbytes = n * H * 2 + H * 2 + 12
+        tab_bytes = n * H * 2
+        for i in range(reps):
+            mtp.mtp_stream_read(tabs[i % copies], sink, tab_bytes)
+        e0.record(stream)
+        for i in range(reps):
+            mtp.mtp_stream_read(tabs[i % copies], sink, tab_bytes)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        sr_gbps = tab_bytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        gbps = nbytes / us / 1e3
+        out.append({"rows": n, "H": H, "bytes": int(nbytes), "us_per_call": round(us, 2),
+                    "calls_per_s": round(1e6 / us, 1), "GBps": round(gbps, 1),
+                    "frac_peak": round(gbps / HBM_PEAK_GBPS, 4),
+                    "stream_read_GBps": round(sr_gbps, 1),
+                    "frac_of_stream_read": round(gbps / sr_gbps, 4),
+                    "note": "pages' per-rank shard shape (context)" if H != wk.H else
+                            ("full head, identity ids" if n == wk.V else "candidate subset")})
+        del tabs
+    return out
 
 
 def cpu_model() -> str:
