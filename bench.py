@@ -382,6 +382,20 @@ def main() -> int:
     if wk.tables:
         draft_tables = draft_table_ablation(wk, mtp, wl, head_d, dev, up, sink, stream)
 
+    # Acceptance of the last timed verify call (the GPU's own outputs): the
+    # share of drafts accepted, and tokens emitted per verify (accepted drafts
+    # plus the bonus token).
+    torch.cuda.synchronize()
+    g_verify = {"argmax": v_arg.cpu().numpy(), "logit": v_logit.cpu().numpy(),
+                "accept": v_acc.cpu().numpy(), "tokens": v_tok.cpu().numpy()}
+    g_drafts = [(out_ids[c].cpu().numpy(), out_logit[c].cpu().numpy())
+                for c in range(wk.draft_calls)]
+    acceptance = {
+        "rate": round(float(g_verify["accept"].sum()) / (wk.B * wk.k), 4) if wk.k else None,
+        "mean_emitted_per_verify": round(float((g_verify["accept"] + 1).sum()) / wk.B, 4),
+        "drafts_per_sequence": wk.k,
+    }
+
     agreement = None
     if fp8 or fp4:
         # how often the quantised draft picks the bf16 draft's token (512
@@ -490,6 +504,7 @@ def main() -> int:
             "draft_same_table_us": round(warm_draft_us, 2),
             "single_call_us": {"draft": single_draft_us, "verify": single_verify_us},
             "stream_read": stream_read,
+            "acceptance": acceptance,
             "quantised_draft_agrees_with_bf16": agreement,
             "draft_tables": draft_tables,
             "setup_s": round(setup_s, 1),
@@ -497,8 +512,14 @@ def main() -> int:
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wk, head, ids, hiddens, hv, drafts,
-                                              args.cpu_seconds)
+        result["cpu_baseline"], orc = cpu_baseline(wk, head, ids, hiddens, hv, drafts,
+                                                   args.cpu_seconds)
+        # the oracle's outputs for the same inputs, against the GPU's outputs
+        # of the last timed step (bf16 packed-table drafts only: the other
+        # draft tables compute other logits)
+        bf16_drafts = not (fp8 or fp4 or gather)
+        result["parity"] = oracle_parity(wk, head, ids, hiddens, hv, drafts, orc,
+                                         g_drafts if bf16_drafts else None, g_verify)
     print(json.dumps(result), flush=True)
     return 0
 
@@ -585,16 +606,20 @@ def cpu_baseline(wk, head, ids, hiddens, hv, drafts, budget_s):
     import oracle
     table = oracle.pack(head, ids)
     times, draft_s, verify_s = [], [], []
+    first = None
     t_begin = time.perf_counter()
     while True:
         t0 = time.perf_counter()
+        outs = []
         for h in hiddens:
             t1 = time.perf_counter()
-            oracle.draft(h, table, ids)
+            outs.append(oracle.draft(h, table, ids))
             draft_s.append(time.perf_counter() - t1)
         t1 = time.perf_counter()
-        oracle.verify(hv, head, wk.B, wk.k, drafts)
+        v = oracle.verify(hv, head, wk.B, wk.k, drafts)
         verify_s.append(time.perf_counter() - t1)
+        if first is None:
+            first = {"drafts": outs, "verify": v, "table": table}
         times.append(time.perf_counter() - t0)
         if time.perf_counter() - t_begin >= budget_s:
             break
@@ -604,7 +629,72 @@ def cpu_baseline(wk, head, ids, hiddens, hv, drafts, budget_s):
             "draft_ms_median": round(statistics.median(draft_s) * 1e3, 3),
             "verify_ms_median": round(statistics.median(verify_s) * 1e3, 3),
             "sample": f"{len(times)} full {wk.name} step(s) ({wk.draft_calls} draft + 1 verify "
-                      f"call), median {step_s:.3f} s per step"}
+                      f"call), median {step_s:.3f} s per step"}, first
+
+
+def oracle_parity(wk, head, ids, hiddens, hv, drafts, orc, g_drafts, g_verify):
+    """The GPU outputs of the last timed step against the oracle's outputs for
+    the same inputs. A pick passes if it equals the oracle's, or if the row is a
+    near tie (oracle runner-up within 1e-3 x |max| of the max) and the pick
+    scores at least max - 1e-3 x |max| under the oracle; its logit must be
+    within 2e-3 x |oracle logit of the pick|. Acceptance must equal the
+    oracle's acceptance of the GPU's verify argmax."""
+    import oracle
+
+    def rows(gpu_ids, gpu_logit, ref, x, w, row_ids):
+        rep = {"rows": int(len(gpu_ids)), "exact": 0, "near_tie_rows": 0, "near_tie_diff": 0,
+               "violations": 0, "max_logit_rel": 0.0}
+        for m in range(len(gpu_ids)):
+            g = int(gpu_ids[m])
+            top, runner = float(ref["exact"][m]), float(ref["runner_exact"][m])
+            tol = 1e-3 * abs(top)
+            near = runner >= top - tol
+            rep["near_tie_rows"] += int(near)
+            if g == int(ref["id"][m]):
+                rep["exact"] += 1
+                zg = top
+            else:
+                row = g if row_ids is None else int(np.searchsorted(row_ids, g))
+                ok = 0 <= row < w.shape[0] and (row_ids is None or int(row_ids[row]) == g)
+                zg = float(oracle.pair_logits(x, w, np.array([m]), np.array([row]))[0]) \
+                    if ok else float("nan")
+                if not (ok and near and zg >= top - tol):
+                    rep["violations"] += 1
+                    continue
+                rep["near_tie_diff"] += 1
+            rel = abs(float(gpu_logit[m]) - zg) / max(abs(zg), 1e-30)
+            rep["max_logit_rel"] = max(rep["max_logit_rel"], rel)
+            if rel > 2e-3:
+                rep["violations"] += 1
+        rep["max_logit_rel"] = float(f"{rep['max_logit_rel']:.3g}")
+        return rep
+
+    out = {"rule": "ids equal, or a pick within 1e-3 relative of the max in a near-tie row; "
+                   "logits within 2e-3 relative; acceptance equal to the oracle's on the "
+                   "GPU argmax"}
+    if g_drafts is not None:
+        d = {"rows": 0, "exact": 0, "near_tie_rows": 0, "near_tie_diff": 0, "violations": 0,
+             "max_logit_rel": 0.0}
+        for (gi, gl), ref, h in zip(g_drafts, orc["drafts"], hiddens):
+            r = rows(gi, gl, ref, h, orc["table"], ids)
+            for key in ("rows", "exact", "near_tie_rows", "near_tie_diff", "violations"):
+                d[key] += r[key]
+            d["max_logit_rel"] = max(d["max_logit_rel"], r["max_logit_rel"])
+        out["draft"] = d
+    else:
+        out["draft"] = None
+    ref = {key: np.asarray(v).reshape(-1) for key, v in orc["verify"].items()
+           if key in ("id", "exact", "runner_exact")}
+    out["verify"] = rows(g_verify["argmax"].reshape(-1), g_verify["logit"].reshape(-1), ref,
+                         hv, head, None)
+    exp = oracle.accept(np.asarray(drafts, np.int32).reshape(wk.B, wk.k),
+                        g_verify["argmax"].reshape(wk.B, wk.k + 1))
+    out["accept_equal"] = bool(np.array_equal(g_verify["accept"].reshape(-1), exp["accept"]) and
+                               np.array_equal(g_verify["tokens"].reshape(wk.B, wk.k + 1),
+                                              exp["tokens"]))
+    out["ok"] = bool(out["accept_equal"] and out["verify"]["violations"] == 0 and
+                     (out["draft"] is None or out["draft"]["violations"] == 0))
+    return out
 
 
 if __name__ == "__main__":
