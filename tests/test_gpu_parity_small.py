@@ -221,6 +221,39 @@ def test_workspace_left_zeroed(torch, mtp):
     assert int(ws.abs().sum()) == 0
 
 
+@pytest.mark.parametrize("N", [2056, 2408, 8008, 23992])
+def test_ragged_grids_above_one_workgroup_per_cu(torch, mtp, N):
+    """Grids of more workgroups than compute units, of sizes that divide
+    nothing: with two rows per wave and four waves per workgroup these tables
+    take 257, 301, 1,001 and 2,999 workgroups (sixteen per CU allowed), so
+    several workgroups share each CU and the last one to finish changes from
+    call to call. Three draft calls and a verify call on one workspace must
+    each give the oracle's ids and logits bit for bit (exact-grid inputs) and
+    leave the whole workspace zeroed."""
+    M, H = 3, 256
+    x = wl.exact_grid_bf16((M, H), N, 1)
+    w = wl.exact_grid_bf16((N, H), N, 2)
+    x_d, w_d = dev_bf16(x), dev_bf16(w)
+    nbytes = max(mtp.mtp_draft_workspace_bytes(M, N, H),
+                 mtp.mtp_verify_workspace_bytes(1, 3, N, H))
+    ws = torch.zeros((nbytes // 8,), dtype=torch.int64, device="cuda")
+    for _ in range(3):
+        g_ids, g_logit = gpu_draft(x_d, w_d, None, ws=ws, blocks_per_cu=16, path=PATHS["valu"])
+        exact_logit_match(g_ids, g_logit, x, w, None)
+        assert int(ws.abs().sum()) == 0
+    hv = wl.exact_grid_bf16((4, H), N, 3)
+    orc = oracle.argmax(hv, w)
+    drafts = orc["id"][:3].reshape(1, 3).copy()
+    drafts[0, 2] = -1
+    g = gpu_verify(dev_bf16(hv), w_d, drafts, 1, 3, ws=ws, blocks_per_cu=16,
+                   path=PATHS["valu"])
+    assert np.array_equal(g["argmax"].ravel(), orc["id"])
+    assert np.array_equal(g["logit"].ravel().astype(np.float32), orc["logit"])
+    check_accept(g, drafts, 1, 3)
+    assert int(g["accept"][0]) == 2
+    assert int(ws.abs().sum()) == 0
+
+
 def test_pack_candidates(torch, mtp):
     V, H, C = 20000, 2560, 5000
     W = wl.head_weights(V, H, 8)
