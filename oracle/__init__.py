@@ -380,6 +380,29 @@ def mxfp4_values(q: np.ndarray, scales: np.ndarray) -> np.ndarray:
     return np.ldexp(e2m1_value(codes), e)
 
 
+def draft_mxfp4_gather(h: np.ndarray, q_head: np.ndarray, scales_head: np.ndarray,
+                       ids: np.ndarray) -> Dict[str, np.ndarray]:
+    """Draft over a candidate id list on an MXFP4 head (codes [V][H/2], block
+    scales [V][H/32], every head row quantised once). Qwen3.8 Flash dual-Spark
+    tuning log, section "read one fewer big table": the upstream work pairs a
+    fixed candidate set with rows chosen per step, stored in a 4-bit float
+    format. The candidates are the distinct ids of the list that name a head
+    row; the result is the MXFP4 draft over that set's rows in ascending id
+    order, so ties go to the lowest id whatever the order of the list. With no
+    valid id: id -1, logit NaN."""
+    q_head = np.asarray(q_head, dtype=np.uint8)
+    scales_head = np.asarray(scales_head, dtype=np.uint8)
+    V = q_head.shape[0]
+    ids = np.asarray(ids, dtype=np.int64).ravel()
+    valid = np.unique(ids[(ids >= 0) & (ids < V)]).astype(np.int32)
+    M = np.atleast_2d(h).shape[0]
+    if valid.size == 0:
+        return {"id": np.full(M, -1, np.int32), "logit": np.full(M, np.nan, np.float32),
+                "exact": np.full(M, np.nan), "runner_id": np.full(M, -1, np.int32),
+                "runner_exact": np.full(M, np.nan)}
+    return draft_mxfp4(h, q_head[valid], scales_head[valid], valid)
+
+
 def draft_mxfp4(h: np.ndarray, q: np.ndarray, scales: np.ndarray,
                 ids: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
     """Draft over an MXFP4 candidate table: first maximum of the fp32-rounded

@@ -461,6 +461,52 @@ def pin_mxfp4_draft(oracle, seed=61):
     assert np.array_equal(d4["id"], d16["id"]) and np.array_equal(d4["logit"], d16["logit"])
 
 
+def pin_mxfp4_gathered_candidates(oracle, seed=67):
+    """Drafting over an id list on an MXFP4 head (unsorted, repeated and
+    out-of-range ids) picks the lowest id among the maximal exact logits of
+    the valid distinct ids. Head rows are built on the scaled E2M1 grid, so
+    quantisation is exact and every logit is a multiple of 2^-8, checked here
+    by integer brute force; quantising the whole head and gathering rows
+    equals quantising the gathered rows; an exact tie planted between two
+    valid ids, the larger listed first, goes to the lower one; a list of only
+    invalid ids gives id -1."""
+    V, H = 700, 64
+    r = wl.rng(seed, 1)
+    mags = _minifloat_magnitudes(2, 1, 1)
+    codes = r.integers(0, 16, size=(V, H))
+    codes[:, ::32] = 7                                   # +6 leads every block
+    e = r.integers(-3, 1, size=(V, H // 32))
+    vals = np.where(codes >= 8, -1.0, 1.0) * mags[codes & 7] * np.exp2(np.repeat(e, 32, axis=1))
+    vals[433] = vals[58]                                 # the planted tie
+    W = wl.f32_to_bf16_bits(vals.astype(np.float32))
+    h = wl.exact_grid_bf16((3, H), seed, 2)
+    ids = r.integers(-40, V + 40, size=300).astype(np.int32)
+    ids = np.concatenate([[433], ids, ids[:50], [58]]).astype(np.int32)
+    q, sc = oracle.quantize_mxfp4(W)
+    d = oracle.draft_mxfp4_gather(h, q, sc, ids)
+    hf = wl.bf16_bits_to_f32(h).astype(np.float64)
+    num = np.rint((hf @ vals.T) * 256).astype(np.int64)
+    assert np.array_equal(num / 256.0, hf @ vals.T)
+    valid = sorted({int(i) for i in ids if 0 <= i < V})
+    for m in range(3):
+        best = max(int(num[m, i]) for i in valid)
+        expect = min(i for i in valid if int(num[m, i]) == best)
+        assert d["id"][m] == expect, (m, d["id"][m], expect)
+        assert d["logit"][m] == np.float32(best / 256.0)
+    srt = np.array(valid, np.int32)
+    q2, sc2 = oracle.quantize_mxfp4(W, srt)
+    assert np.array_equal(q2, q[srt]) and np.array_equal(sc2, sc[srt])
+    h2 = wl.f32_to_bf16_bits(np.sign(vals[[58]]).astype(np.float32))
+    d2 = oracle.draft_mxfp4_gather(h2, q, sc, ids)
+    n2 = np.sign(vals[58]) @ vals.T
+    best2 = max(n2[i] for i in valid)
+    assert d2["id"][0] == min(i for i in valid if n2[i] == best2)
+    if n2[58] == best2:
+        assert d2["id"][0] == 58
+    none = oracle.draft_mxfp4_gather(h, q, sc, np.array([-1, V, V + 9], np.int32))
+    assert np.all(none["id"] == -1) and np.all(np.isnan(none["logit"]))
+
+
 def pin_pack(oracle):
     """Packing copies head rows ids[i]; invalid id lists are refused."""
     V, H = 50, 16
@@ -574,6 +620,7 @@ ALL_PINS = [
     pin_e2m1_format,
     pin_mxfp4_quantize,
     pin_mxfp4_draft,
+    pin_mxfp4_gathered_candidates,
     pin_pack,
     pin_worked_accept,
     pin_accept_invariants,
