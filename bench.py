@@ -69,7 +69,9 @@ def parse_args():
                          "the bf16 head")
     ap.add_argument("--draft-source", choices=("table", "gather"), default="table",
                     help="draft calls read a packed candidate table (default), or head rows "
-                         "through a per-call id list (mtp_draft_argmax_gather; row-major only)")
+                         "through a per-call id list (mtp_draft_argmax_gather; with --table "
+                         "mxfp4, mtp_draft_argmax_mxfp4_gather over an MXFP4 head; row-major "
+                         "only)")
     ap.add_argument("--graph", action="store_true",
                     help="time the steps as replays of a captured HIP graph (mtp_graph_*); "
                          "per-call durations still come from event-bracketed eager launches")
@@ -146,8 +148,8 @@ def main() -> int:
         layout = "rows" if max(wk.Md, wk.Mv) <= 8 else "tiled"
     gather = args.draft_source == "gather"
     fp8 = args.table == "fp8"
-    if (fp8 or fp4) and gather:
-        print("--table fp8/mxfp4 runs on a packed candidate table (use --draft-source table)",
+    if fp8 and gather:
+        print("--table fp8 runs on a packed candidate table (use --draft-source table)",
               file=sys.stderr)
         return 2
     if gather and layout != "rows":
@@ -157,7 +159,14 @@ def main() -> int:
     head_d = up(head)
     ids_d = up(ids, np.int32)
     tables = []
-    for _ in range(max(1, args.table_copies)):
+    for _ in range(1 if gather else max(1, args.table_copies)):
+        if fp4 and gather:
+            # every head row quantised once; each call gathers its own rows
+            tq = torch.empty((wk.V, wk.H // 2), dtype=torch.uint8, device=dev)
+            ts = torch.empty((wk.V, wk.H // 32), dtype=torch.uint8, device=dev)
+            mtp.mtp_pack_candidates_mxfp4(head_d, None, tq, ts, C=wk.V)
+            tables.append((tq, ts))
+            continue
         if fp4 and layout == "tiled":
             tq, ts = mtp.alloc_tiled_mxfp4(wk.C, wk.H, dev)
             mtp.mtp_pack_tiled_mxfp4(head_d, ids_d, tq, ts)
@@ -219,7 +228,10 @@ def main() -> int:
                   for c in range(wk.draft_calls)] if gather else None
 
     def draft_call(c, table):
-        if fp4 and layout == "tiled":
+        if fp4 and gather:
+            mtp.mtp_draft_argmax_mxfp4_gather(h_d[c], table[0], table[1], gather_ids[c],
+                                              out_ids[c], out_logit[c], ws=ws_d)
+        elif fp4 and layout == "tiled":
             mtp.mtp_draft_argmax_tiled_mxfp4(h_d[c], table[0], table[1], wk.C, ids_d, out_ids[c],
                                              out_logit[c], ws=ws_d)
         elif fp4:
@@ -407,7 +419,10 @@ def main() -> int:
         a8 = torch.empty(n_rows, dtype=torch.int32, device=dev)
         a16 = torch.empty(n_rows, dtype=torch.int32, device=dev)
         ws_x = mtp.alloc_workspace(mtp.mtp_draft_workspace_bytes(n_rows, wk.C, wk.H), dev)
-        if fp4 and layout == "tiled":
+        if fp4 and gather:
+            mtp.mtp_draft_argmax_mxfp4_gather(hx, tables[0][0], tables[0][1], gather_ids[0], a8,
+                                              ws=ws_x)
+        elif fp4 and layout == "tiled":
             mtp.mtp_draft_argmax_tiled_mxfp4(hx, tables[0][0], tables[0][1], wk.C, ids_d, a8,
                                              ws=ws_x)
         elif fp4:
@@ -417,7 +432,10 @@ def main() -> int:
         else:
             mtp.mtp_draft_argmax_tiled_fp8(hx, tables[0][0], tables[0][1], wk.C, ids_d, a8,
                                            ws=ws_x)
-        mtp.mtp_draft_argmax(hx, t16, ids_d, a16)
+        if gather:
+            mtp.mtp_draft_argmax_gather(hx, head_d, gather_ids[0], a16)
+        else:
+            mtp.mtp_draft_argmax(hx, t16, ids_d, a16)
         agreement = round(float((a8 == a16).float().mean().item()), 4)
         del t16
 
@@ -426,7 +444,9 @@ def main() -> int:
     # logits; verify also reads drafts and writes acceptance)
     if fp4:
         # codes (half a byte per element) + one scale byte per 32 elements
-        draft_bytes = C * H // 2 + C * H // 32 + Md * H * 2 + Md * (4 + 4 + 4)
+        # (+ the id list when gathered)
+        draft_bytes = C * H // 2 + C * H // 32 + Md * H * 2 + Md * (4 + 4 + 4) + \
+            (C * 4 if gather else 0)
     elif fp8:
         # codes + one scale per row
         draft_bytes = C * H + C * 4 + Md * H * 2 + Md * (4 + 4 + 4)

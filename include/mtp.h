@@ -371,6 +371,38 @@ mtp_status mtp_draft_argmax_mxfp4_cfg(const mtp_bf16 *hidden, int M, int H,
                                       hipStream_t stream, const mtp_config *cfg);
 
 /*
+ * Draft over gathered candidates on an MXFP4 head (no packed table): the
+ * dynamic candidate list of mtp_draft_argmax_gather, read from a head whose
+ * every row was quantised once by mtp_pack_candidates_mxfp4 (ids NULL,
+ * C = V):
+ *   out_ids[m] = argmax over i < C of  hidden[m] . mxfp4(head row ids[i])
+ * with the MXFP4 logit of mtp_draft_argmax_mxfp4. Ties go to the lowest id,
+ * whatever the order of the list; an id outside [0, V) is not a candidate;
+ * with no valid id, out_ids[m] = -1 and out_logit[m] = NaN. Reads C rows of
+ * H/2 code bytes and H/32 scale bytes in list order.
+ * hidden device [M][H] bf16; head_q device [V][H/2] codes (16-byte aligned);
+ * head_scales device [V][H/32] E8M0 scales; ids device int32 [C]; H % 32 == 0;
+ * out_ids / out_logit / ws as mtp_draft_argmax (workspace size
+ * mtp_draft_workspace_bytes(M, C, H)). Runs on the vector-ALU kernel;
+ * cfg->path must be MTP_PATH_AUTO or MTP_PATH_VALU (MTP_ERR_UNSUPPORTED
+ * otherwise).
+ * [Qwen3.8 Flash dual-Spark tuning log, section "read one fewer big table":
+ * the upstream work drafts over a fixed candidate set plus rows picked per
+ * step, with the candidate rows in a 4-bit float format.]
+ */
+mtp_status mtp_draft_argmax_mxfp4_gather(const mtp_bf16 *hidden, int M, int H,
+                                         const uint8_t *head_q, const uint8_t *head_scales,
+                                         int64_t V, const int32_t *ids, int64_t C,
+                                         int32_t *out_ids, float *out_logit, void *ws,
+                                         size_t ws_bytes, hipStream_t stream);
+mtp_status mtp_draft_argmax_mxfp4_gather_cfg(const mtp_bf16 *hidden, int M, int H,
+                                             const uint8_t *head_q, const uint8_t *head_scales,
+                                             int64_t V, const int32_t *ids, int64_t C,
+                                             int32_t *out_ids, float *out_logit, void *ws,
+                                             size_t ws_bytes, hipStream_t stream,
+                                             const mtp_config *cfg);
+
+/*
  * MXFP4 candidate table in the tiled layout (batched draft rows: the
  * matrix-core kernel). Same codes and scales as mtp_pack_candidates_mxfp4,
  * stored for the 64-row tiled kernel: rows in tiles of 64 (zero rows pad the

@@ -230,11 +230,15 @@ __device__ __forceinline__ float dot32_fp4(const uint4 &c, const uint4 (&h)[4]) 
 
 // MR hidden rows, NCL blocks per lane and row, RB table rows per wave
 // iteration, next iteration's rows in flight; EXACT: H is NCL * 2048 (no
-// block predication).
-template <int MR, int NCL, int RB, bool EXACT>
+// block predication). GATHER: candidate i is head row gids[i] of a head of
+// gV rows (any order, repeats allowed) and its argmax key is that id, so
+// ties go to the lowest id; an id outside [0, gV) is no candidate (its loads
+// read row 0 and it is never reported). Otherwise candidate i is row i.
+template <int MR, int NCL, int RB, bool EXACT, bool GATHER>
 __global__ void __launch_bounds__(kFp4Threads)
     gemv_argmax_mxfp4(const uint4 *__restrict__ X, const uint4 *__restrict__ Q,
-                      const uint8_t *__restrict__ S, int M, int64_t N, int nblk, RowSink sink) {
+                      const uint8_t *__restrict__ S, int M, int64_t N, int nblk,
+                      const int32_t *__restrict__ gids, int64_t gV, RowSink sink) {
   __shared__ float s_val[kFp4Waves][MR];
   __shared__ int64_t s_row[kFp4Waves][MR];
   __shared__ float f_val[MR];
@@ -266,11 +270,23 @@ __global__ void __launch_bounds__(kFp4Threads)
     bi[r] = -1;
   }
 
-  auto load = [&](uint4(&w)[RB][NCL], uint32_t(&s)[RB][NCL], int64_t r0) {
+  // key[i]: the argmax key of candidate r0 + i (its row, or its id when
+  // gathered), -1 when it is past N or not a candidate
+  auto load = [&](uint4(&w)[RB][NCL], uint32_t(&s)[RB][NCL], int32_t(&key)[RB], int64_t r0) {
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
-      // rows past N read row 0 (never reported)
-      const int64_t row = r0 + i < N ? r0 + i : 0;
+      int32_t k = -1;
+      if (r0 + i < N) {
+        if (GATHER) {
+          const int32_t id = gids[r0 + i];
+          k = (id >= 0 && id < gV) ? id : -1;
+        } else {
+          k = (int32_t)(r0 + i);
+        }
+      }
+      key[i] = k;
+      // rows past N and non-candidates read row 0 (never reported)
+      const int64_t row = k >= 0 ? k : 0;
 #pragma unroll
       for (int c = 0; c < NCL; ++c) {
         const int blk = lane + kWave * c;
@@ -285,18 +301,22 @@ __global__ void __launch_bounds__(kFp4Threads)
   int64_t r0 = ((int64_t)blockIdx.x * kFp4Waves + __builtin_amdgcn_readfirstlane(wave)) * RB;
   uint4 nxt[RB][NCL];
   uint32_t snxt[RB][NCL];
-  if (r0 < N) load(nxt, snxt, r0);
+  int32_t knxt[RB];
+  if (r0 < N) load(nxt, snxt, knxt, r0);
   for (; r0 < N; r0 += stride) {
     uint4 w[RB][NCL];
     uint32_t sc[RB][NCL];
+    int32_t key[RB];
 #pragma unroll
-    for (int i = 0; i < RB; ++i)
+    for (int i = 0; i < RB; ++i) {
+      key[i] = knxt[i];
 #pragma unroll
       for (int c = 0; c < NCL; ++c) {
         w[i][c] = nxt[i][c];
         sc[i][c] = snxt[i][c];
       }
-    if (r0 + stride < N) load(nxt, snxt, r0 + stride);
+    }
+    if (r0 + stride < N) load(nxt, snxt, knxt, r0 + stride);
     float acc[MR][RB];
 #pragma unroll
     for (int r = 0; r < MR; ++r)
@@ -315,9 +335,9 @@ __global__ void __launch_bounds__(kFp4Threads)
 #pragma unroll
       for (int r = 0; r < MR; ++r) {
         const float s = wave_sum(acc[r][i]);
-        if (r0 + i < N && better(s, r0 + i, bv[r], bi[r])) {
+        if (key[i] >= 0 && better(s, key[i], bv[r], bi[r])) {
           bv[r] = s;
-          bi[r] = r0 + i;
+          bi[r] = key[i];
         }
       }
     }
@@ -365,14 +385,24 @@ static hipError_t launch_fp4_cfg(const Fp4Launch &L) {
     const int64_t want = (row_blocks + kFp4Waves - 1) / kFp4Waves;
     const int gx = (int)(want < L.max_blocks_x ? want : L.max_blocks_x);
     const int gy = (L.M + MR - 1) / MR;
-    if (L.nblk == NCL * kWave)
-      hipLaunchKernelGGL((gemv_argmax_mxfp4<MR, NCL, RB, true>), dim3(gx, gy),
-                         dim3(kFp4Threads), 0, L.stream, (const uint4 *)L.X, (const uint4 *)L.Q,
-                         L.scales, L.M, L.N, L.nblk, L.sink);
-    else
-      hipLaunchKernelGGL((gemv_argmax_mxfp4<MR, NCL, RB, false>), dim3(gx, gy),
-                         dim3(kFp4Threads), 0, L.stream, (const uint4 *)L.X, (const uint4 *)L.Q,
-                         L.scales, L.M, L.N, L.nblk, L.sink);
+    const bool exact = L.nblk == NCL * kWave;
+    const dim3 grid(gx, gy), block(kFp4Threads);
+    const uint4 *X = (const uint4 *)L.X, *Q = (const uint4 *)L.Q;
+    if (L.gather_ids) {
+      if (exact)
+        hipLaunchKernelGGL((gemv_argmax_mxfp4<MR, NCL, RB, true, true>), grid, block, 0, L.stream,
+                           X, Q, L.scales, L.M, L.N, L.nblk, L.gather_ids, L.gather_V, L.sink);
+      else
+        hipLaunchKernelGGL((gemv_argmax_mxfp4<MR, NCL, RB, false, true>), grid, block, 0,
+                           L.stream, X, Q, L.scales, L.M, L.N, L.nblk, L.gather_ids, L.gather_V,
+                           L.sink);
+    } else if (exact) {
+      hipLaunchKernelGGL((gemv_argmax_mxfp4<MR, NCL, RB, true, false>), grid, block, 0, L.stream,
+                         X, Q, L.scales, L.M, L.N, L.nblk, nullptr, (int64_t)0, L.sink);
+    } else {
+      hipLaunchKernelGGL((gemv_argmax_mxfp4<MR, NCL, RB, false, false>), grid, block, 0, L.stream,
+                         X, Q, L.scales, L.M, L.N, L.nblk, nullptr, (int64_t)0, L.sink);
+    }
     return hipGetLastError();
   }
 }

@@ -349,3 +349,30 @@ def test_binding_fails_loudly_without_the_library(tmp_path):
                          text=True, timeout=300, env={**os.environ, "PYTHONPATH": str(tmp_path)})
     assert out.returncode != 0
     assert "ImportError" in out.stderr and "not built" in out.stderr, out.stderr[-2000:]
+
+
+def test_mxfp4_gather_rejects_bad_arguments():
+    f = mtp.lib.mtp_draft_argmax_mxfp4_gather
+    # hidden, M, H, head_q, head_scales, V, ids, C, out_ids, out_logit, ws, ws_bytes, stream
+    ok = [FAKE, 1, 64, FAKE, FAKE, 100, FAKE, 50, FAKE, None, FAKE, 4096, None]
+
+    def call(changes):
+        a = list(ok)
+        for k, v in changes.items():
+            a[k] = v
+        return f(*a)
+
+    assert call({6: None}) == INVALID                          # no id list
+    assert call({5: 0}) == INVALID                             # V < 1
+    assert call({5: 2 ** 31}) == INVALID                       # V too large
+    assert call({7: 0}) == INVALID                             # C < 1
+    assert call({2: 48}) == INVALID                            # H % 32
+    assert call({4: None}) == INVALID                          # no scales
+    assert call({3: FAKE_ODD}) == INVALID                      # codes alignment
+    assert call({0: None}) == INVALID
+    assert call({10: None}) == mtp.MTP_ERR_WORKSPACE
+    assert call({11: 8}) == mtp.MTP_ERR_WORKSPACE
+    c = mtp.mtp_config()
+    c.path = mtp.MTP_PATH_MFMA
+    assert mtp.lib.mtp_draft_argmax_mxfp4_gather_cfg(*ok, ctypes.byref(c)) == \
+        mtp.MTP_ERR_UNSUPPORTED
