@@ -329,6 +329,28 @@ def draft_fp8(h: np.ndarray, q: np.ndarray, exps: np.ndarray,
     return out
 
 
+def draft_fp8_gather(h: np.ndarray, q_head: np.ndarray, exps_head: np.ndarray,
+                     ids: np.ndarray) -> Dict[str, np.ndarray]:
+    """Draft over a candidate id list on an fp8 head (codes [V][H], row scale
+    exponents [V], every head row quantised once): the candidate set of
+    draft_gather with the fp8 logit of draft_fp8. Qwen3.8 Flash dual-Spark
+    tuning log, section "read one fewer big table": a fixed candidate set plus
+    rows chosen per step, in a low-precision float format. Ties go to the
+    lowest id whatever the order of the list; with no valid id: id -1,
+    logit NaN."""
+    q_head = np.asarray(q_head, dtype=np.uint8)
+    exps_head = np.asarray(exps_head, dtype=np.int32)
+    V = q_head.shape[0]
+    ids = np.asarray(ids, dtype=np.int64).ravel()
+    valid = np.unique(ids[(ids >= 0) & (ids < V)]).astype(np.int32)
+    M = np.atleast_2d(h).shape[0]
+    if valid.size == 0:
+        return {"id": np.full(M, -1, np.int32), "logit": np.full(M, np.nan, np.float32),
+                "exact": np.full(M, np.nan), "runner_id": np.full(M, -1, np.int32),
+                "runner_exact": np.full(M, np.nan)}
+    return draft_fp8(h, q_head[valid], exps_head[valid], valid)
+
+
 # ---- MXFP4 candidate table --------------------------------------------------
 
 

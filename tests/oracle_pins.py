@@ -335,6 +335,48 @@ def pin_fp8_draft(oracle, seed=47):
     assert np.array_equal(d8["id"], oracle.draft(h, oracle.pack(W, ids), ids)["id"])
 
 
+def pin_fp8_gathered_candidates(oracle, seed=71):
+    """Drafting over an id list on an fp8 head (unsorted, repeated and
+    out-of-range ids) picks the lowest id among the maximal exact logits of
+    the valid distinct ids. Head rows of multiples of 1/8 up to 2 quantise
+    exactly (scale 2^-7), so every fp8 logit is an exact integer sum over 128,
+    checked here by brute force; quantising the whole head and gathering rows
+    equals quantising the gathered rows; an exact tie planted between two
+    valid ids, the larger listed first, goes to the lower one; a list of only
+    invalid ids gives id -1."""
+    V, H = 800, 48
+    r = wl.rng(seed, 1)
+    kq = r.integers(-16, 17, size=(V, H))
+    kq[:, 0] = 16                                       # max|w| = 2 in every row
+    kq[517] = kq[44]                                    # the planted tie
+    W = wl.f32_to_bf16_bits((kq / 8.0).astype(np.float32))
+    h = wl.exact_grid_bf16((3, H), seed, 2)
+    ids = r.integers(-30, V + 30, size=350).astype(np.int32)
+    ids = np.concatenate([[517], ids, ids[:40], [44]]).astype(np.int32)
+    q, e = oracle.quantize_fp8(W)
+    assert np.all(e == -7)
+    d = oracle.draft_fp8_gather(h, q, e, ids)
+    num = np.rint(wl.bf16_bits_to_f32(h) * 16).astype(np.int64) @ kq.T    # logits * 128
+    valid = sorted({int(i) for i in ids if 0 <= i < V})
+    for m in range(3):
+        best = max(int(num[m, i]) for i in valid)
+        expect = min(i for i in valid if int(num[m, i]) == best)
+        assert d["id"][m] == expect, (m, d["id"][m], expect)
+        assert d["logit"][m] == np.float32(best / 128.0)
+    srt = np.array(valid, np.int32)
+    q2, e2 = oracle.quantize_fp8(W, srt)
+    assert np.array_equal(q2, q[srt]) and np.array_equal(e2, e[srt])
+    h2 = wl.f32_to_bf16_bits(np.sign(kq[[44]]).astype(np.float32))
+    d2 = oracle.draft_fp8_gather(h2, q, e, ids)
+    n2 = np.sign(kq[44]) @ kq.T
+    best2 = max(n2[i] for i in valid)
+    assert d2["id"][0] == min(i for i in valid if n2[i] == best2)
+    if n2[44] == best2:
+        assert d2["id"][0] == 44
+    none = oracle.draft_fp8_gather(h, q, e, np.array([-3, V, V + 2], np.int32))
+    assert np.all(none["id"] == -1) and np.all(np.isnan(none["logit"]))
+
+
 def _minifloat_magnitudes(ebits: int, mbits: int, bias: int) -> np.ndarray:
     """Values of the non-negative codes of a sign / exponent / mantissa float
     without infinities, indexed by code: exponent field 0 holds the
@@ -617,6 +659,7 @@ ALL_PINS = [
     pin_e4m3_format,
     pin_fp8_quantize,
     pin_fp8_draft,
+    pin_fp8_gathered_candidates,
     pin_e2m1_format,
     pin_mxfp4_quantize,
     pin_mxfp4_draft,
