@@ -70,8 +70,8 @@ def parse_args():
     ap.add_argument("--draft-source", choices=("table", "gather"), default="table",
                     help="draft calls read a packed candidate table (default), or head rows "
                          "through a per-call id list (mtp_draft_argmax_gather; with --table "
-                         "mxfp4, mtp_draft_argmax_mxfp4_gather over an MXFP4 head; row-major "
-                         "only)")
+                         "fp8 or mxfp4, the gathered draft over a head quantised once; "
+                         "row-major only)")
     ap.add_argument("--graph", action="store_true",
                     help="time the steps as replays of a captured HIP graph (mtp_graph_*); "
                          "per-call durations still come from event-bracketed eager launches")
@@ -148,10 +148,6 @@ def main() -> int:
         layout = "rows" if max(wk.Md, wk.Mv) <= 8 else "tiled"
     gather = args.draft_source == "gather"
     fp8 = args.table == "fp8"
-    if fp8 and gather:
-        print("--table fp8 runs on a packed candidate table (use --draft-source table)",
-              file=sys.stderr)
-        return 2
     if gather and layout != "rows":
         print("--draft-source gather runs on the row-major head (use --layout rows)",
               file=sys.stderr)
@@ -160,6 +156,13 @@ def main() -> int:
     ids_d = up(ids, np.int32)
     tables = []
     for _ in range(1 if gather else max(1, args.table_copies)):
+        if fp8 and gather:
+            # every head row quantised once; each call gathers its own rows
+            tq = torch.empty((wk.V, wk.H), dtype=torch.uint8, device=dev)
+            ts = torch.empty(wk.V, dtype=torch.float32, device=dev)
+            mtp.mtp_pack_candidates_fp8(head_d, None, tq, ts, C=wk.V)
+            tables.append((tq, ts))
+            continue
         if fp4 and gather:
             # every head row quantised once; each call gathers its own rows
             tq = torch.empty((wk.V, wk.H // 2), dtype=torch.uint8, device=dev)
@@ -228,7 +231,10 @@ def main() -> int:
                   for c in range(wk.draft_calls)] if gather else None
 
     def draft_call(c, table):
-        if fp4 and gather:
+        if fp8 and gather:
+            mtp.mtp_draft_argmax_fp8_gather(h_d[c], table[0], table[1], gather_ids[c],
+                                            out_ids[c], out_logit[c], ws=ws_d)
+        elif fp4 and gather:
             mtp.mtp_draft_argmax_mxfp4_gather(h_d[c], table[0], table[1], gather_ids[c],
                                               out_ids[c], out_logit[c], ws=ws_d)
         elif fp4 and layout == "tiled":
@@ -419,7 +425,10 @@ def main() -> int:
         a8 = torch.empty(n_rows, dtype=torch.int32, device=dev)
         a16 = torch.empty(n_rows, dtype=torch.int32, device=dev)
         ws_x = mtp.alloc_workspace(mtp.mtp_draft_workspace_bytes(n_rows, wk.C, wk.H), dev)
-        if fp4 and gather:
+        if fp8 and gather:
+            mtp.mtp_draft_argmax_fp8_gather(hx, tables[0][0], tables[0][1], gather_ids[0], a8,
+                                            ws=ws_x)
+        elif fp4 and gather:
             mtp.mtp_draft_argmax_mxfp4_gather(hx, tables[0][0], tables[0][1], gather_ids[0], a8,
                                               ws=ws_x)
         elif fp4 and layout == "tiled":
@@ -448,8 +457,8 @@ def main() -> int:
         draft_bytes = C * H // 2 + C * H // 32 + Md * H * 2 + Md * (4 + 4 + 4) + \
             (C * 4 if gather else 0)
     elif fp8:
-        # codes + one scale per row
-        draft_bytes = C * H + C * 4 + Md * H * 2 + Md * (4 + 4 + 4)
+        # codes + one scale per row (+ the id list when gathered)
+        draft_bytes = C * H + C * 4 + Md * H * 2 + Md * (4 + 4 + 4) + (C * 4 if gather else 0)
     else:
         draft_bytes = C * H * 2 + Md * H * 2 + Md * (4 + 4 + 4) + (C * 4 if gather else 0)
     verify_bytes = V * H * 2 + Mv * H * 2 + wk.B * wk.k * 4 + Mv * (4 + 4 + 4) + wk.B * 4

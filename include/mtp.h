@@ -326,6 +326,37 @@ mtp_status mtp_draft_argmax_fp8_cfg(const mtp_bf16 *hidden, int M, int H, const 
                                     const mtp_config *cfg);
 
 /*
+ * Draft over gathered candidates on an fp8 head (no packed table): the
+ * dynamic candidate list of mtp_draft_argmax_gather, read from a head whose
+ * every row was quantised once by mtp_pack_candidates_fp8 (ids NULL, C = V):
+ *   out_ids[m] = argmax over i < C of  hidden[m] . fp8(head row ids[i])
+ * with the fp8 logit of mtp_draft_argmax_fp8. Ties go to the lowest id,
+ * whatever the order of the list; an id outside [0, V) is not a candidate;
+ * with no valid id, out_ids[m] = -1 and out_logit[m] = NaN. Reads C rows of
+ * H code bytes and one row scale each, in list order.
+ * hidden device [M][H] bf16; head_q device [V][H] E4M3 codes (16-byte
+ * aligned); head_scales device float [V]; ids device int32 [C]; H % 16 == 0;
+ * out_ids / out_logit / ws as mtp_draft_argmax (workspace size
+ * mtp_draft_workspace_bytes(M, C, H)). Runs on the vector-ALU kernel;
+ * cfg->path must be MTP_PATH_AUTO or MTP_PATH_VALU (MTP_ERR_UNSUPPORTED
+ * otherwise).
+ * [Qwen3.8 Flash dual-Spark tuning log, section "read one fewer big table":
+ * a fixed candidate set plus rows picked per step, in a low-precision float
+ * format.]
+ */
+mtp_status mtp_draft_argmax_fp8_gather(const mtp_bf16 *hidden, int M, int H,
+                                       const uint8_t *head_q, const float *head_scales,
+                                       int64_t V, const int32_t *ids, int64_t C, int32_t *out_ids,
+                                       float *out_logit, void *ws, size_t ws_bytes,
+                                       hipStream_t stream);
+mtp_status mtp_draft_argmax_fp8_gather_cfg(const mtp_bf16 *hidden, int M, int H,
+                                           const uint8_t *head_q, const float *head_scales,
+                                           int64_t V, const int32_t *ids, int64_t C,
+                                           int32_t *out_ids, float *out_logit, void *ws,
+                                           size_t ws_bytes, hipStream_t stream,
+                                           const mtp_config *cfg);
+
+/*
  * MXFP4 candidate table (4-bit rows; draft calls only).
  *
  * The candidate rows in the OCP microscaling 4-bit format, a quarter of the

@@ -452,11 +452,12 @@ mtp_status mtp_pack_candidates_fp8(const mtp_bf16 *head, int64_t V, int H, const
   return MTP_OK;
 }
 
-mtp_status mtp_draft_argmax_fp8_cfg(const mtp_bf16 *hidden, int M, int H, const uint8_t *table_q,
-                                    const float *scales, const int32_t *ids, int64_t C,
-                                    int32_t *out_ids, float *out_logit, void *ws,
-                                    size_t ws_bytes, hipStream_t stream,
-                                    const mtp_config *cfg) {
+// fp8 draft over C candidates: table rows 0..C-1, or (gather_ids) head rows
+// gather_ids[i] of a head of gather_V rows, keyed by id.
+static mtp_status run_fp8(const mtp_bf16 *hidden, int M, int H, const uint8_t *table_q,
+                          const float *scales, const int32_t *ids, int64_t C, int32_t *out_ids,
+                          float *out_logit, void *ws, size_t ws_bytes, hipStream_t stream,
+                          const mtp_config *cfg, const int32_t *gather_ids, int64_t gather_V) {
   if (!scales || !aligned(scales, 4)) return MTP_ERR_INVALID_ARG;
   if (H % 16 != 0) return MTP_ERR_INVALID_ARG;
   mtp_status st =
@@ -483,11 +484,44 @@ mtp_status mtp_draft_argmax_fp8_cfg(const mtp_bf16 *hidden, int M, int H, const 
   L.N = C;
   L.ncq = ncq;
   L.max_blocks_x = per_cu * cus;
-  L.sink = draft_sink(ws, ids, out_ids, out_logit, M);
+  // gathered candidates are keyed by id: the finish needs no id map
+  L.sink = draft_sink(ws, gather_ids ? nullptr : ids, out_ids, out_logit, M);
   L.stream = stream;
+  L.gather_ids = gather_ids;
+  L.gather_V = gather_V;
   e = mtp::launch_fp8(L, mr, ncl);
   if (e != hipSuccess) return hip_fail(e);
   return MTP_OK;
+}
+
+mtp_status mtp_draft_argmax_fp8_cfg(const mtp_bf16 *hidden, int M, int H, const uint8_t *table_q,
+                                    const float *scales, const int32_t *ids, int64_t C,
+                                    int32_t *out_ids, float *out_logit, void *ws,
+                                    size_t ws_bytes, hipStream_t stream,
+                                    const mtp_config *cfg) {
+  return run_fp8(hidden, M, H, table_q, scales, ids, C, out_ids, out_logit, ws, ws_bytes, stream,
+                 cfg, nullptr, 0);
+}
+
+mtp_status mtp_draft_argmax_fp8_gather_cfg(const mtp_bf16 *hidden, int M, int H,
+                                           const uint8_t *head_q, const float *head_scales,
+                                           int64_t V, const int32_t *ids, int64_t C,
+                                           int32_t *out_ids, float *out_logit, void *ws,
+                                           size_t ws_bytes, hipStream_t stream,
+                                           const mtp_config *cfg) {
+  if (!ids) return MTP_ERR_INVALID_ARG;
+  if (V < 1 || V > INT32_MAX) return MTP_ERR_INVALID_ARG;
+  return run_fp8(hidden, M, H, head_q, head_scales, ids, C, out_ids, out_logit, ws, ws_bytes,
+                 stream, cfg, ids, V);
+}
+
+mtp_status mtp_draft_argmax_fp8_gather(const mtp_bf16 *hidden, int M, int H,
+                                       const uint8_t *head_q, const float *head_scales,
+                                       int64_t V, const int32_t *ids, int64_t C, int32_t *out_ids,
+                                       float *out_logit, void *ws, size_t ws_bytes,
+                                       hipStream_t stream) {
+  return mtp_draft_argmax_fp8_gather_cfg(hidden, M, H, head_q, head_scales, V, ids, C, out_ids,
+                                         out_logit, ws, ws_bytes, stream, nullptr);
 }
 
 mtp_status mtp_draft_argmax_fp8(const mtp_bf16 *hidden, int M, int H, const uint8_t *table_q,

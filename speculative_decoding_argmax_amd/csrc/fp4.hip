@@ -270,23 +270,25 @@ __global__ void __launch_bounds__(kFp4Threads)
     bi[r] = -1;
   }
 
-  // key[i]: the argmax key of candidate r0 + i (its row, or its id when
-  // gathered), -1 when it is past N or not a candidate
+  // key[i] (gathered candidates only): the id of candidate r0 + i, -1 when
+  // it is past N or not a candidate
   auto load = [&](uint4(&w)[RB][NCL], uint32_t(&s)[RB][NCL], int32_t(&key)[RB], int64_t r0) {
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
-      int32_t k = -1;
-      if (r0 + i < N) {
-        if (GATHER) {
+      // rows past N and non-candidates read row 0 (never reported); a packed
+      // table keeps no keys, its row is a wave-uniform expression of r0
+      int64_t row;
+      if constexpr (GATHER) {
+        int32_t k = -1;
+        if (r0 + i < N) {
           const int32_t id = gids[r0 + i];
           k = (id >= 0 && id < gV) ? id : -1;
-        } else {
-          k = (int32_t)(r0 + i);
         }
+        key[i] = k;
+        row = k >= 0 ? k : 0;
+      } else {
+        row = r0 + i < N ? r0 + i : 0;
       }
-      key[i] = k;
-      // rows past N and non-candidates read row 0 (never reported)
-      const int64_t row = k >= 0 ? k : 0;
 #pragma unroll
       for (int c = 0; c < NCL; ++c) {
         const int blk = lane + kWave * c;
@@ -309,7 +311,7 @@ __global__ void __launch_bounds__(kFp4Threads)
     int32_t key[RB];
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
-      key[i] = knxt[i];
+      if constexpr (GATHER) key[i] = knxt[i];
 #pragma unroll
       for (int c = 0; c < NCL; ++c) {
         w[i][c] = nxt[i][c];
@@ -335,9 +337,15 @@ __global__ void __launch_bounds__(kFp4Threads)
 #pragma unroll
       for (int r = 0; r < MR; ++r) {
         const float s = wave_sum(acc[r][i]);
-        if (key[i] >= 0 && better(s, key[i], bv[r], bi[r])) {
+        // a packed table's candidate is row r0 + i; a gathered one its id
+        if constexpr (GATHER) {
+          if (key[i] >= 0 && better(s, key[i], bv[r], bi[r])) {
+            bv[r] = s;
+            bi[r] = key[i];
+          }
+        } else if (r0 + i < N && better(s, r0 + i, bv[r], bi[r])) {
           bv[r] = s;
-          bi[r] = key[i];
+          bi[r] = r0 + i;
         }
       }
     }

@@ -234,12 +234,16 @@ __device__ __forceinline__ float dot16_fp8(const uint4 &c, const uint4 &h0, cons
 
 // MR hidden rows, NCL code chunks (16 columns) per lane and row, RB table
 // rows per wave iteration, next iteration's rows in flight; EXACT: H is
-// NCL * 1024 (no column predication).
-template <int MR, int NCL, int RB, bool EXACT>
+// NCL * 1024 (no column predication). GATHER: candidate i is head row
+// gids[i] of a head of gV rows (any order, repeats allowed), keyed by that
+// id, so ties go to the lowest id; an id outside [0, gV) is no candidate
+// (its loads read row 0 and it is never reported). Otherwise candidate i is
+// row i.
+template <int MR, int NCL, int RB, bool EXACT, bool GATHER>
 __global__ void __launch_bounds__(kFp8Threads)
     gemv_argmax_fp8(const uint4 *__restrict__ X, const uint4 *__restrict__ Q,
                     const float *__restrict__ scales, int M, int64_t N, int ncq,
-                    RowSink sink) {
+                    const int32_t *__restrict__ gids, int64_t gV, RowSink sink) {
   __shared__ float s_val[kFp8Waves][MR];
   __shared__ int64_t s_row[kFp8Waves][MR];
   __shared__ float f_val[MR];
@@ -271,11 +275,25 @@ __global__ void __launch_bounds__(kFp8Threads)
     bi[r] = -1;
   }
 
-  auto load = [&](uint4(&w)[RB][NCL], int64_t r0) {
+  // key[i] (gathered candidates only): the id of candidate r0 + i, -1 when
+  // it is past N or not a candidate
+  auto load = [&](uint4(&w)[RB][NCL], int32_t(&key)[RB], int64_t r0) {
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
-      // rows past N read row 0 (never reported)
-      const int64_t row = r0 + i < N ? r0 + i : 0;
+      // rows past N and non-candidates read row 0 (never reported); a packed
+      // table keeps no keys, its row is a wave-uniform expression of r0
+      int64_t row;
+      if constexpr (GATHER) {
+        int32_t k = -1;
+        if (r0 + i < N) {
+          const int32_t id = gids[r0 + i];
+          k = (id >= 0 && id < gV) ? id : -1;
+        }
+        key[i] = k;
+        row = k >= 0 ? k : 0;
+      } else {
+        row = r0 + i < N ? r0 + i : 0;
+      }
       const uint4 *p = Q + row * ncq + lane;
 #pragma unroll
       for (int c = 0; c < NCL; ++c)
@@ -287,14 +305,18 @@ __global__ void __launch_bounds__(kFp8Threads)
   const int64_t stride = (int64_t)gridDim.x * kFp8Waves * RB;
   int64_t r0 = ((int64_t)blockIdx.x * kFp8Waves + __builtin_amdgcn_readfirstlane(wave)) * RB;
   uint4 nxt[RB][NCL];
-  if (r0 < N) load(nxt, r0);
+  int32_t knxt[RB];
+  if (r0 < N) load(nxt, knxt, r0);
   for (; r0 < N; r0 += stride) {
     uint4 w[RB][NCL];
+    int32_t key[RB];
 #pragma unroll
-    for (int i = 0; i < RB; ++i)
+    for (int i = 0; i < RB; ++i) {
+      if constexpr (GATHER) key[i] = knxt[i];
 #pragma unroll
       for (int c = 0; c < NCL; ++c) w[i][c] = nxt[i][c];
-    if (r0 + stride < N) load(nxt, r0 + stride);
+    }
+    if (r0 + stride < N) load(nxt, knxt, r0 + stride);
     float acc[MR][RB];
 #pragma unroll
     for (int r = 0; r < MR; ++r)
@@ -309,11 +331,22 @@ __global__ void __launch_bounds__(kFp8Threads)
           acc[r][i] = dot16_fp8(w[i][c], h[r][c][0], h[r][c][1], acc[r][i]);
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
-      const float scale = r0 + i < N ? scales[r0 + i] : 0.0f;
+      // a packed table's candidate is row r0 + i (wave-uniform); a gathered
+      // one is keyed by its id
+      float scale;
+      if constexpr (GATHER)
+        scale = key[i] >= 0 ? scales[key[i]] : 0.0f;
+      else
+        scale = r0 + i < N ? scales[r0 + i] : 0.0f;
 #pragma unroll
       for (int r = 0; r < MR; ++r) {
         const float s = wave_sum(acc[r][i]) * scale;
-        if (r0 + i < N && better(s, r0 + i, bv[r], bi[r])) {
+        if constexpr (GATHER) {
+          if (key[i] >= 0 && better(s, key[i], bv[r], bi[r])) {
+            bv[r] = s;
+            bi[r] = key[i];
+          }
+        } else if (r0 + i < N && better(s, r0 + i, bv[r], bi[r])) {
           bv[r] = s;
           bi[r] = r0 + i;
         }
@@ -363,14 +396,23 @@ static hipError_t launch_fp8_cfg(const Fp8Launch &L) {
   const int64_t want = (row_blocks + kFp8Waves - 1) / kFp8Waves;
   const int gx = (int)(want < L.max_blocks_x ? want : L.max_blocks_x);
   const int gy = (L.M + MR - 1) / MR;
-  if (L.ncq == NCL * kWave)
-    hipLaunchKernelGGL((gemv_argmax_fp8<MR, NCL, RB, true>), dim3(gx, gy), dim3(kFp8Threads), 0,
-                       L.stream, (const uint4 *)L.X, (const uint4 *)L.Q, L.scales, L.M, L.N,
-                       L.ncq, L.sink);
-  else
-    hipLaunchKernelGGL((gemv_argmax_fp8<MR, NCL, RB, false>), dim3(gx, gy), dim3(kFp8Threads),
-                       0, L.stream, (const uint4 *)L.X, (const uint4 *)L.Q, L.scales, L.M, L.N,
-                       L.ncq, L.sink);
+  const bool exact = L.ncq == NCL * kWave;
+  const dim3 grid(gx, gy), block(kFp8Threads);
+  const uint4 *X = (const uint4 *)L.X, *Q = (const uint4 *)L.Q;
+  if (L.gather_ids) {
+    if (exact)
+      hipLaunchKernelGGL((gemv_argmax_fp8<MR, NCL, RB, true, true>), grid, block, 0, L.stream, X,
+                         Q, L.scales, L.M, L.N, L.ncq, L.gather_ids, L.gather_V, L.sink);
+    else
+      hipLaunchKernelGGL((gemv_argmax_fp8<MR, NCL, RB, false, true>), grid, block, 0, L.stream, X,
+                         Q, L.scales, L.M, L.N, L.ncq, L.gather_ids, L.gather_V, L.sink);
+  } else if (exact) {
+    hipLaunchKernelGGL((gemv_argmax_fp8<MR, NCL, RB, true, false>), grid, block, 0, L.stream, X,
+                       Q, L.scales, L.M, L.N, L.ncq, nullptr, (int64_t)0, L.sink);
+  } else {
+    hipLaunchKernelGGL((gemv_argmax_fp8<MR, NCL, RB, false, false>), grid, block, 0, L.stream, X,
+                       Q, L.scales, L.M, L.N, L.ncq, nullptr, (int64_t)0, L.sink);
+  }
   return hipGetLastError();
   }
 }

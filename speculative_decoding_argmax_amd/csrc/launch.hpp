@@ -93,6 +93,10 @@ struct Fp8Launch {
   int max_blocks_x;
   RowSink sink;
   hipStream_t stream;
+  // gathered candidates: candidate i is row gather_ids[i] of a head of
+  // gather_V rows (Q and scales are then the head's); nullptr for a table
+  const int32_t *gather_ids = nullptr;
+  int64_t gather_V = 0;
 };
 
 // Code chunks per lane that have an instantiation (0: too wide).

@@ -99,6 +99,9 @@ def _load() -> ctypes.CDLL:
         "mtp_pack_candidates_fp8": ([P, I64, I, P, I64, P, P, P], I),
         "mtp_draft_argmax_fp8": ([P, I, I, P, P, P, I64, P, P, P, S, P], I),
         "mtp_draft_argmax_fp8_cfg": ([P, I, I, P, P, P, I64, P, P, P, S, P, P], I),
+        "mtp_draft_argmax_fp8_gather": ([P, I, I, P, P, I64, P, I64, P, P, P, S, P], I),
+        "mtp_draft_argmax_fp8_gather_cfg": ([P, I, I, P, P, I64, P, I64, P, P, P, S, P, P],
+                                            I),
         "mtp_tiled_fp8_bytes": ([I64, I], S),
         "mtp_tiled_mxfp4_bytes": ([I64, I], S),
         "mtp_tiled_mxfp4_scale_bytes": ([I64, I], S),
@@ -499,6 +502,32 @@ def mtp_draft_argmax_mxfp4(hidden, table_q, scales, ids, out_ids, out_logit=None
         _ptr(out_logit, "out_logit", (torch.float32,), allow_none=True),
         _ptr(ws, "ws", (torch.int64, torch.uint8, torch.int32)), ws.numel() * ws.element_size(),
         _stream(stream), ctypes.byref(cfg)), "mtp_draft_argmax_mxfp4")
+
+
+def mtp_draft_argmax_fp8_gather(hidden, head_q, head_scales, ids, out_ids, out_logit=None,
+                                ws=None, stream=None, path: int = MTP_PATH_AUTO,
+                                blocks_per_cu: int = 0) -> None:
+    """Draft over a candidate id list on an fp8 head (see include/mtp.h)."""
+    torch = _torch()
+    M, H = hidden.shape
+    V, H2 = head_q.shape
+    if H2 != H or tuple(head_scales.shape) != (V,):
+        raise ValueError("shapes differ")
+    C = ids.numel()
+    if out_ids.numel() != M or (out_logit is not None and out_logit.numel() != M):
+        raise ValueError("outputs must have M entries")
+    if ws is None:
+        _no_alloc_in_capture("mtp_draft_argmax_fp8_gather")
+        ws = alloc_workspace(mtp_draft_workspace_bytes(M, C, H), hidden.device, stream)
+    cfg = _cfg(path, blocks_per_cu)
+    _check(lib.mtp_draft_argmax_fp8_gather_cfg(
+        _ptr(hidden, "hidden", _bf16_types()), M, H, _ptr(head_q, "head_q", (torch.uint8,)),
+        _ptr(head_scales, "head_scales", (torch.float32,)), V,
+        _ptr(ids, "ids", (torch.int32,)), C,
+        _ptr(out_ids, "out_ids", (torch.int32,)),
+        _ptr(out_logit, "out_logit", (torch.float32,), allow_none=True),
+        _ptr(ws, "ws", (torch.int64, torch.uint8, torch.int32)), ws.numel() * ws.element_size(),
+        _stream(stream), ctypes.byref(cfg)), "mtp_draft_argmax_fp8_gather")
 
 
 def mtp_draft_argmax_mxfp4_gather(hidden, head_q, head_scales, ids, out_ids, out_logit=None,

@@ -87,6 +87,10 @@ int main() {
   EXPECT(mtp_draft_argmax_fp8(F, 1, 64, FQ, nullptr, FI, 100, FO, FL, WS, 4096, nullptr) == INV);
   EXPECT(mtp_draft_argmax_fp8(F, 1, 40, FQ, FL, FI, 100, FO, FL, WS, 4096, nullptr) == INV);
   EXPECT(mtp_draft_argmax_mxfp4(F, 1, 48, FQ, FQ, FI, 100, FO, FL, WS, 4096, nullptr) == INV);
+  EXPECT(mtp_draft_argmax_fp8_gather(F, 1, 64, FQ, FL, 100, nullptr, 10, FO, FL, WS, 4096,
+                                     nullptr) == INV);
+  EXPECT(mtp_draft_argmax_fp8_gather(F, 1, 40, FQ, FL, 100, FI, 10, FO, FL, WS, 4096,
+                                     nullptr) == INV);
   EXPECT(mtp_draft_argmax_mxfp4_gather(F, 1, 64, FQ, FQ, 100, nullptr, 10, FO, FL, WS, 4096,
                                        nullptr) == INV);
   EXPECT(mtp_draft_argmax_mxfp4_gather(F, 1, 48, FQ, FQ, 100, FI, 10, FO, FL, WS, 4096,

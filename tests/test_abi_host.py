@@ -376,3 +376,29 @@ def test_mxfp4_gather_rejects_bad_arguments():
     c.path = mtp.MTP_PATH_MFMA
     assert mtp.lib.mtp_draft_argmax_mxfp4_gather_cfg(*ok, ctypes.byref(c)) == \
         mtp.MTP_ERR_UNSUPPORTED
+
+
+def test_fp8_gather_rejects_bad_arguments():
+    f = mtp.lib.mtp_draft_argmax_fp8_gather
+    # hidden, M, H, head_q, head_scales, V, ids, C, out_ids, out_logit, ws, ws_bytes, stream
+    ok = [FAKE, 1, 64, FAKE, FAKE, 100, FAKE, 50, FAKE, None, FAKE, 4096, None]
+
+    def call(changes):
+        a = list(ok)
+        for k, v in changes.items():
+            a[k] = v
+        return f(*a)
+
+    assert call({6: None}) == INVALID                            # no id list
+    assert call({5: 0}) == INVALID                               # V < 1
+    assert call({5: 2 ** 31}) == INVALID                         # V too large
+    assert call({7: 0}) == INVALID                               # C < 1
+    assert call({2: 40}) == INVALID                              # H % 16
+    assert call({4: None}) == INVALID                            # no scales
+    assert call({4: P(0x10002)}) == INVALID                      # scales alignment
+    assert call({3: FAKE_ODD}) == INVALID                        # codes alignment
+    assert call({10: None}) == mtp.MTP_ERR_WORKSPACE
+    c = mtp.mtp_config()
+    c.path = mtp.MTP_PATH_MFMA
+    assert mtp.lib.mtp_draft_argmax_fp8_gather_cfg(*ok, ctypes.byref(c)) == \
+        mtp.MTP_ERR_UNSUPPORTED
