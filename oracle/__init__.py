@@ -18,6 +18,16 @@ the pages each one follows):
   quantize_fp8(head, ids)     fp8 candidate table: E4M3 rows and per-row
                               power-of-two scale exponents
   draft_fp8(h, q, exps, ids)  argmax over the fp8 table, mapped to ids
+  draft_fp8_gather(h, q, exps, ids)
+                              draft_gather's candidates on an fp8 head
+  e2m1_value(codes), e2m1_round(x), mx_block_exponent(w)
+                              the OCP E2M1 element and the MX block scale rule
+  quantize_mxfp4(head, ids)   MXFP4 candidate table: packed E2M1 codes and
+                              E8M0 scales per block of 32
+  draft_mxfp4(h, q, scales, ids)
+                              argmax over the MXFP4 table, mapped to ids
+  draft_mxfp4_gather(h, q, scales, ids)
+                              draft_gather's candidates on an MXFP4 head
   verify(hv, head, B, k)      argmax over the full head, shaped [B][k+1]
   accept(draft, target)       greedy acceptance plus bonus token
 """
