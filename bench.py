@@ -544,11 +544,11 @@ def main() -> int:
         result["cpu_baseline"], orc = cpu_baseline(wk, head, ids, hiddens, hv, drafts,
                                                    args.cpu_seconds)
         # the oracle's outputs for the same inputs, against the GPU's outputs
-        # of the last timed step (bf16 packed-table drafts only: the other
-        # draft tables compute other logits)
-        bf16_drafts = not (fp8 or fp4 or gather)
-        result["parity"] = oracle_parity(wk, head, ids, hiddens, hv, drafts, orc,
-                                         g_drafts if bf16_drafts else None, g_verify)
+        # of the last timed step
+        lists = [wl.candidate_ids(wk.V, wk.C, wk.seed + 1000 * (c + 1))
+                 for c in range(wk.draft_calls)] if gather else None
+        result["parity"] = oracle_parity(wk, head, ids, hiddens, hv, drafts, orc, g_drafts,
+                                         g_verify, args.table, lists)
     print(json.dumps(result), flush=True)
     return 0
 
@@ -661,16 +661,20 @@ def cpu_baseline(wk, head, ids, hiddens, hv, drafts, budget_s):
                       f"call), median {step_s:.3f} s per step"}, first
 
 
-def oracle_parity(wk, head, ids, hiddens, hv, drafts, orc, g_drafts, g_verify):
+def oracle_parity(wk, head, ids, hiddens, hv, drafts, orc, g_drafts, g_verify, table="bf16",
+                  gather_lists=None):
     """The GPU outputs of the last timed step against the oracle's outputs for
     the same inputs. A pick passes if it equals the oracle's, or if the row is a
     near tie (oracle runner-up within 1e-3 x |max| of the max) and the pick
     scores at least max - 1e-3 x |max| under the oracle; its logit must be
     within 2e-3 x |oracle logit of the pick|. Acceptance must equal the
-    oracle's acceptance of the GPU's verify argmax."""
+    oracle's acceptance of the GPU's verify argmax. Draft logits are the
+    table's own: bf16, or the oracle's fp8 / MXFP4 quantisation of the same
+    rows; gathered drafts (gather_lists: each call's id list) take the
+    candidate set of their list."""
     import oracle
 
-    def rows(gpu_ids, gpu_logit, ref, x, w, row_ids):
+    def rows(gpu_ids, gpu_logit, ref, pick_logit):
         rep = {"rows": int(len(gpu_ids)), "exact": 0, "near_tie_rows": 0, "near_tie_diff": 0,
                "violations": 0, "max_logit_rel": 0.0}
         for m in range(len(gpu_ids)):
@@ -683,11 +687,8 @@ def oracle_parity(wk, head, ids, hiddens, hv, drafts, orc, g_drafts, g_verify):
                 rep["exact"] += 1
                 zg = top
             else:
-                row = g if row_ids is None else int(np.searchsorted(row_ids, g))
-                ok = 0 <= row < w.shape[0] and (row_ids is None or int(row_ids[row]) == g)
-                zg = float(oracle.pair_logits(x, w, np.array([m]), np.array([row]))[0]) \
-                    if ok else float("nan")
-                if not (ok and near and zg >= top - tol):
+                zg = pick_logit(m, g)
+                if zg is None or not (near and zg >= top - tol):
                     rep["violations"] += 1
                     continue
                 rep["near_tie_diff"] += 1
@@ -698,31 +699,79 @@ def oracle_parity(wk, head, ids, hiddens, hv, drafts, orc, g_drafts, g_verify):
         rep["max_logit_rel"] = float(f"{rep['max_logit_rel']:.3g}")
         return rep
 
+    def position(row_ids, g):
+        """Index of id g in the sorted id list row_ids (None: not there)."""
+        k = int(np.searchsorted(row_ids, g))
+        return k if k < len(row_ids) and int(row_ids[k]) == g else None
+
+    def draft_check(c, h):
+        """Oracle result and pick-logit function of draft call c."""
+        if gather_lists is not None:
+            lst = np.asarray(gather_lists[c])
+            rows_ = np.unique(lst[(lst >= 0) & (lst < wk.V)]).astype(np.int32)
+        else:
+            rows_ = np.asarray(ids, np.int32)
+        if table == "bf16":
+            w = orc["table"] if gather_lists is None else oracle.pack(head, rows_)
+            ref = oracle.draft(h, w, rows_)
+
+            def pick(m, g):
+                k = position(rows_, g)
+                return None if k is None else \
+                    float(oracle.pair_logits(h, w, np.array([m]), np.array([k]))[0])
+        elif table == "fp8":
+            q, e = quant["fp8"]
+            q, e = (q, e) if gather_lists is None else (q[rows_], e[rows_])
+            ref = oracle.draft_fp8(h, q, e, rows_)
+
+            def pick(m, g):
+                k = position(rows_, g)
+                return None if k is None else \
+                    float(oracle.draft_fp8(h[m:m + 1], q[k:k + 1], e[k:k + 1])["exact"][0])
+        else:
+            q, sc = quant["mxfp4"]
+            q, sc = (q, sc) if gather_lists is None else (q[rows_], sc[rows_])
+            ref = oracle.draft_mxfp4(h, q, sc, rows_)
+
+            def pick(m, g):
+                k = position(rows_, g)
+                return None if k is None else \
+                    float(oracle.draft_mxfp4(h[m:m + 1], q[k:k + 1], sc[k:k + 1])["exact"][0])
+        return ref, pick
+
+    # the oracle's quantisation of the drafted rows (the whole head when gathered)
+    quant = {}
+    if table == "fp8":
+        quant["fp8"] = oracle.quantize_fp8(head, None if gather_lists is not None else ids)
+    elif table == "mxfp4":
+        quant["mxfp4"] = oracle.quantize_mxfp4(head, None if gather_lists is not None else ids)
+
     out = {"rule": "ids equal, or a pick within 1e-3 relative of the max in a near-tie row; "
                    "logits within 2e-3 relative; acceptance equal to the oracle's on the "
-                   "GPU argmax"}
-    if g_drafts is not None:
-        d = {"rows": 0, "exact": 0, "near_tie_rows": 0, "near_tie_diff": 0, "violations": 0,
-             "max_logit_rel": 0.0}
-        for (gi, gl), ref, h in zip(g_drafts, orc["drafts"], hiddens):
-            r = rows(gi, gl, ref, h, orc["table"], ids)
-            for key in ("rows", "exact", "near_tie_rows", "near_tie_diff", "violations"):
-                d[key] += r[key]
-            d["max_logit_rel"] = max(d["max_logit_rel"], r["max_logit_rel"])
-        out["draft"] = d
-    else:
-        out["draft"] = None
+                   "GPU argmax",
+           "draft_table": table, "draft_source": "gather" if gather_lists is not None else "table"}
+    d = {"rows": 0, "exact": 0, "near_tie_rows": 0, "near_tie_diff": 0, "violations": 0,
+         "max_logit_rel": 0.0}
+    for c, ((gi, gl), h) in enumerate(zip(g_drafts, hiddens)):
+        ref, pick = draft_check(c, h)
+        r = rows(gi, gl, ref, pick)
+        for key in ("rows", "exact", "near_tie_rows", "near_tie_diff", "violations"):
+            d[key] += r[key]
+        d["max_logit_rel"] = max(d["max_logit_rel"], r["max_logit_rel"])
+    out["draft"] = d
     ref = {key: np.asarray(v).reshape(-1) for key, v in orc["verify"].items()
            if key in ("id", "exact", "runner_exact")}
     out["verify"] = rows(g_verify["argmax"].reshape(-1), g_verify["logit"].reshape(-1), ref,
-                         hv, head, None)
+                         lambda m, g: float(oracle.pair_logits(hv, head, np.array([m]),
+                                                               np.array([g]))[0])
+                         if 0 <= g < wk.V else None)
     exp = oracle.accept(np.asarray(drafts, np.int32).reshape(wk.B, wk.k),
                         g_verify["argmax"].reshape(wk.B, wk.k + 1))
     out["accept_equal"] = bool(np.array_equal(g_verify["accept"].reshape(-1), exp["accept"]) and
                                np.array_equal(g_verify["tokens"].reshape(wk.B, wk.k + 1),
                                               exp["tokens"]))
     out["ok"] = bool(out["accept_equal"] and out["verify"]["violations"] == 0 and
-                     (out["draft"] is None or out["draft"]["violations"] == 0))
+                     out["draft"]["violations"] == 0)
     return out
 
 

@@ -74,10 +74,42 @@ def test_parity_summary_flags_wrong_picks_logits_and_acceptance():
     g_verify["accept"][0] = (int(g_verify["accept"][0]) + 1) % (wk.k + 1)
     p = bench.oracle_parity(wk, head, ids, hiddens, hv, drafts, orc, g_drafts, g_verify)
     assert not p["ok"] and not p["accept_equal"]
-    # quantised or gathered drafts: no draft comparison
-    g_drafts, g_verify = _as_gpu(wk, orc, drafts)
-    p = bench.oracle_parity(wk, head, ids, hiddens, hv, drafts, orc, None, g_verify)
-    assert p["ok"] and p["draft"] is None
+
+
+def test_parity_summary_on_quantised_and_gathered_drafts():
+    """fp8 and MXFP4 tables, and gathered lists, are checked against the
+    oracle's own quantisation and candidate sets: the oracle's outputs pass,
+    and a pick that is not in the call's candidate set is a violation."""
+    import oracle
+    wk, head, ids, hiddens, hv, drafts, base, orc = _tiny()
+    _, g_verify = _as_gpu(wk, orc, drafts)
+    q8, e8 = oracle.quantize_fp8(head, ids)
+    q4, s4 = oracle.quantize_mxfp4(head, ids)
+    cases = {
+        "fp8": [oracle.draft_fp8(h, q8, e8, ids) for h in hiddens],
+        "mxfp4": [oracle.draft_mxfp4(h, q4, s4, ids) for h in hiddens],
+    }
+    for table, refs in cases.items():
+        g = [(r["id"].copy(), r["logit"].copy()) for r in refs]
+        p = bench.oracle_parity(wk, head, ids, hiddens, hv, drafts, orc, g, g_verify, table)
+        assert p["ok"] and p["draft"]["exact"] == p["draft"]["rows"], (table, p)
+    lists = [np.sort(wl.rng(5, c).choice(wk.V, size=300, replace=False)).astype(np.int32)
+             for c in range(wk.draft_calls)]
+    qa8, ea8 = oracle.quantize_fp8(head)
+    qa4, sa4 = oracle.quantize_mxfp4(head)
+    gathered = {
+        "bf16": [oracle.draft_gather(h, head, lst) for h, lst in zip(hiddens, lists)],
+        "fp8": [oracle.draft_fp8_gather(h, qa8, ea8, lst) for h, lst in zip(hiddens, lists)],
+        "mxfp4": [oracle.draft_mxfp4_gather(h, qa4, sa4, lst) for h, lst in zip(hiddens, lists)],
+    }
+    for table, refs in gathered.items():
+        g = [(r["id"].copy(), r["logit"].copy()) for r in refs]
+        p = bench.oracle_parity(wk, head, ids, hiddens, hv, drafts, orc, g, g_verify, table, lists)
+        assert p["ok"] and p["draft_source"] == "gather", (table, p)
+        outside = next(i for i in range(wk.V) if i not in set(lists[0].tolist()))
+        g[0][0][0] = outside
+        p = bench.oracle_parity(wk, head, ids, hiddens, hv, drafts, orc, g, g_verify, table, lists)
+        assert not p["ok"] and p["draft"]["violations"] == 1, (table, p)
 
 
 def bench_logit(h, head, token):
