@@ -190,3 +190,105 @@ def test_graph_api_argument_errors(torch, mtp):
     assert mtp.lib.mtp_graph_end(None, ctypes.byref(h)) == mtp.MTP_ERR_INVALID_ARG
     assert not h
     mtp.lib.mtp_graph_destroy(None)
+
+
+@pytest.mark.parametrize("kind", ["fp8", "mxfp4", "gather_bf16", "gather_fp8", "gather_mxfp4"])
+def test_graph_replays_quantised_and_gathered_drafts(torch, mtp, kind):
+    """Three draft calls on an fp8 or MXFP4 table, or through per-call id
+    lists (bf16, fp8 or MXFP4 head), captured into one graph. Each replay
+    runs with new hidden rows and, for gathered drafts, new id lists written
+    into the captured list buffers; it must equal the same calls made
+    eagerly bit for bit, and the first replay meets the oracle's rule."""
+    from tests.parity import check_fp8_rows, check_mxfp4_rows
+    head = wl.head_weights(V, H, 9202)
+    ids = wl.candidate_ids(V, C, 9202)
+    head_d, ids_d = dev_bf16(head), dev_i32(ids)
+    fmt = kind.split("_")[-1]
+    gather = kind.startswith("gather")
+    rows = V if gather else C
+    sel = None if gather else ids_d
+    u8, i16, i32, f32 = torch.uint8, torch.int16, torch.int32, torch.float32
+    q = s8 = None
+    if fmt == "fp8":
+        q = torch.empty((rows, H), dtype=u8, device="cuda")
+        s8 = torch.empty(rows, dtype=f32, device="cuda")
+        mtp.mtp_pack_candidates_fp8(head_d, sel, q, s8, C=rows)
+    elif fmt == "mxfp4":
+        q = torch.empty((rows, H // 2), dtype=u8, device="cuda")
+        s8 = torch.empty((rows, H // 32), dtype=u8, device="cuda")
+        mtp.mtp_pack_candidates_mxfp4(head_d, sel, q, s8, C=rows)
+    h = [torch.zeros((1, H), dtype=i16, device="cuda") for _ in range(DRAFTS)]
+    lists = [torch.zeros(C, dtype=i32, device="cuda") for _ in range(DRAFTS)] if gather else None
+    ws = mtp.alloc_workspace(mtp.mtp_draft_workspace_bytes(1, C, H))
+
+    def outputs():
+        return {"ids": [torch.full((1,), -7, dtype=i32, device="cuda") for _ in range(DRAFTS)],
+                "dlogit": [torch.full((1,), -1.0, dtype=f32, device="cuda")
+                           for _ in range(DRAFTS)]}
+
+    def calls(o):
+        for i in range(DRAFTS):
+            a = (o["ids"][i], o["dlogit"][i])
+            if kind == "fp8":
+                mtp.mtp_draft_argmax_fp8(h[i], q, s8, ids_d, *a, ws=ws)
+            elif kind == "mxfp4":
+                mtp.mtp_draft_argmax_mxfp4(h[i], q, s8, ids_d, *a, ws=ws)
+            elif kind == "gather_bf16":
+                mtp.mtp_draft_argmax_gather(h[i], head_d, lists[i], *a, ws=ws)
+            elif kind == "gather_fp8":
+                mtp.mtp_draft_argmax_fp8_gather(h[i], q, s8, lists[i], *a, ws=ws)
+            else:
+                mtp.mtp_draft_argmax_mxfp4_gather(h[i], q, s8, lists[i], *a, ws=ws)
+
+    def set_inputs(seed):
+        hs = [wl.hidden_states(1, H, seed, 10 + i) for i in range(DRAFTS)]
+        ls = []
+        for i in range(DRAFTS):
+            h[i].copy_(dev_bf16(hs[i]))
+            if gather:
+                lst = wl.candidate_ids(V, C, seed * 10 + i)
+                wl.rng(seed, 40 + i).shuffle(lst)
+                lists[i].copy_(dev_i32(lst))
+                ls.append(lst)
+        return hs, ls
+
+    outs = outputs()
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    g = mtp.Graph()
+    with torch.cuda.stream(s):
+        set_inputs(1)
+        s.synchronize()
+        g.begin()
+        calls(outs)
+        g.end()
+        eager = outputs()
+        for rep, seed in enumerate((21, 22, 23)):
+            hs, ls = set_inputs(seed)
+            g.launch()
+            s.synchronize()
+            got = Step.snapshot(outs)
+            calls(eager)
+            s.synchronize()
+            _equal(got, Step.snapshot(eager))
+            if rep == 0:
+                if fmt != "bf16":
+                    quant = oracle.quantize_fp8 if fmt == "fp8" else oracle.quantize_mxfp4
+                    qr, sr = quant(head, None if gather else ids)
+                for i in range(DRAFTS):
+                    gi, gl = got["ids"][i], got["dlogit"][i]
+                    srt = np.unique(ls[i]).astype(np.int32) if gather else ids
+                    if fmt == "bf16":
+                        w = oracle.pack(head, srt)
+                        check_rows(gi, gl, oracle.draft(hs[i], w, srt), hs[i], w, srt)
+                        continue
+                    qs, ss = (qr[srt], sr[srt]) if gather else (qr, sr)
+                    if fmt == "fp8":
+                        check_fp8_rows(gi, gl, oracle.draft_fp8(hs[i], qs, ss, srt), hs[i], qs,
+                                       ss, srt)
+                    else:
+                        check_mxfp4_rows(gi, gl, oracle.draft_mxfp4(hs[i], qs, ss, srt), hs[i],
+                                         qs, ss, srt)
+            x = torch.randn(1 << 16, device="cuda")
+            _ = float((x * 2).sum())
+    g.destroy()
