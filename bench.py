@@ -398,7 +398,8 @@ def main() -> int:
     # draft over each table, plus the pages' per-rank shard shape as context.
     draft_tables = None
     if wk.tables:
-        draft_tables = draft_table_ablation(wk, mtp, wl, head_d, dev, up, sink, stream)
+        draft_tables = draft_table_ablation(wk, mtp, wl, head_d, dev, up, sink, stream,
+                                            fmt=args.table)
 
     # Acceptance of the last timed verify call (the GPU's own outputs): the
     # share of drafts accepted, and tokens emitted per verify (accepted drafts
@@ -553,7 +554,8 @@ def main() -> int:
     return 0
 
 
-def draft_table_ablation(wk, mtp, wl, head_d, dev, up, sink, stream, reps=200, copies=3):
+def draft_table_ablation(wk, mtp, wl, head_d, dev, up, sink, stream, reps=200, copies=3,
+                         fmt="bf16"):
     """M = 1 draft calls over each table size of the ablation: the full head
     (identity ids), the 65,536-row subset and the nested 32,768-row subset,
     all at the workload's width, plus 32,768 rows x 2,560 (the pages' per-rank
@@ -563,7 +565,9 @@ def draft_table_ablation(wk, mtp, wl, head_d, dev, up, sink, stream, reps=200, c
     so no call is served from the Infinity Cache its predecessor filled. One
     event pair brackets ``reps`` back-to-back calls, so the time per call
     includes the gaps between launches. The streaming-read probe over the same
-    bytes gives the practical read ceiling for each size.
+    bytes gives the practical read ceiling for each size. fmt "fp8" / "mxfp4":
+    the same tables quantised by the library's pack, drafted by the fp8 /
+    MXFP4 kernel.
     """
     import torch
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -574,39 +578,68 @@ def draft_table_ablation(wk, mtp, wl, head_d, dev, up, sink, stream, reps=200, c
             ids = (np.arange(wk.V, dtype=np.int32) if n == wk.V
                    else wl.candidate_ids(wk.V, n, wk.seed))
             ids_d = up(ids, np.int32)
-            tabs = []
-            for _ in range(copies):
-                t = torch.empty((n, H), dtype=torch.int16, device=dev)
-                mtp.mtp_pack_candidates(head_d, ids_d, t)
-                tabs.append(t)
+            src, src_ids = head_d, ids_d
         else:
             ids_d = up(wl.candidate_ids(wk.V, n, wk.seed), np.int32)
-            rows = up(wl.head_weights(n, H, wk.seed + 1))
-            tabs = [rows] + [rows.clone() for _ in range(copies - 1)]
+            src, src_ids = up(wl.head_weights(n, H, wk.seed + 1)), None
+        tabs = []
+        for _ in range(copies):
+            if fmt == "fp8":
+                t = (torch.empty((n, H), dtype=torch.uint8, device=dev),
+                     torch.empty(n, dtype=torch.float32, device=dev))
+                mtp.mtp_pack_candidates_fp8(src, src_ids, t[0], t[1], C=n)
+            elif fmt == "mxfp4":
+                t = (torch.empty((n, H // 2), dtype=torch.uint8, device=dev),
+                     torch.empty((n, H // 32), dtype=torch.uint8, device=dev))
+                mtp.mtp_pack_candidates_mxfp4(src, src_ids, t[0], t[1], C=n)
+            elif src_ids is None:
+                t = src.clone()
+            else:
+                t = torch.empty((n, H), dtype=torch.int16, device=dev)
+                mtp.mtp_pack_candidates(src, src_ids, t)
+            tabs.append(t)
         h = up(wl.hidden_states(1, H, wk.seed, block=0))
         oid = torch.empty(1, dtype=torch.int32, device=dev)
         olog = torch.empty(1, dtype=torch.float32, device=dev)
         ws = mtp.alloc_workspace(mtp.mtp_draft_workspace_bytes(1, n, H), dev)
+        def call(i):
+            t = tabs[i % copies]
+            if fmt == "fp8":
+                mtp.mtp_draft_argmax_fp8(h, t[0], t[1], ids_d, oid, olog, ws=ws)
+            elif fmt == "mxfp4":
+                mtp.mtp_draft_argmax_mxfp4(h, t[0], t[1], ids_d, oid, olog, ws=ws)
+            else:
+                mtp.mtp_draft_argmax(h, t, ids_d, oid, olog, ws=ws)
+
         for i in range(20):
-            mtp.mtp_draft_argmax(h, tabs[i % copies], ids_d, oid, olog, ws=ws)
+            call(i)
         e0.record(stream)
         for i in range(reps):
-            mtp.mtp_draft_argmax(h, tabs[i % copies], ids_d, oid, olog, ws=ws)
+            call(i)
         e1.record(stream)
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1000.0 / reps
-        nbytes = n * H * 2 + H * 2 + 12
-        tab_bytes = n * H * 2
+        if fmt == "fp8":
+            tab_bytes = n * H + n * 4
+        elif fmt == "mxfp4":
+            tab_bytes = n * H // 2 + n * H // 32
+        else:
+            tab_bytes = n * H * 2
+        nbytes = tab_bytes + H * 2 + 12
+        # the streaming-read probe over the codes (the larger buffer)
+        rbufs = [t[0] if isinstance(t, tuple) else t for t in tabs]
+        rbytes = rbufs[0].numel() * rbufs[0].element_size()
         for i in range(reps):
-            mtp.mtp_stream_read(tabs[i % copies], sink, tab_bytes)
+            mtp.mtp_stream_read(rbufs[i % copies], sink, rbytes)
         e0.record(stream)
         for i in range(reps):
-            mtp.mtp_stream_read(tabs[i % copies], sink, tab_bytes)
+            mtp.mtp_stream_read(rbufs[i % copies], sink, rbytes)
         e1.record(stream)
         torch.cuda.synchronize()
-        sr_gbps = tab_bytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        sr_gbps = rbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
         gbps = nbytes / us / 1e3
-        out.append({"rows": n, "H": H, "bytes": int(nbytes), "us_per_call": round(us, 2),
+        out.append({"rows": n, "H": H, "table": fmt, "bytes": int(nbytes),
+                    "us_per_call": round(us, 2),
                     "calls_per_s": round(1e6 / us, 1), "GBps": round(gbps, 1),
                     "frac_peak": round(gbps / HBM_PEAK_GBPS, 4),
                     "stream_read_GBps": round(sr_gbps, 1),
