@@ -376,15 +376,36 @@ __global__ void __launch_bounds__(kFp4Threads)
   finish_rows(sink, f_val, f_row, m0, min(MR, M - m0));
 }
 
-// Rows per iteration: about 8 KiB of codes in flight per wave, except for
-// one block per lane (H up to 2,048), where 4 rows per iteration, and 2 once
-// a pass holds 4 or more hidden rows, were faster (sweep on MI355X at
-// 65,536 x 2,048: 18.6 against 19.4 us at M = 1, 32.0 against 35.0 us at
-// M = 4).
-template <int MR, int NCL>
+// Rows per iteration: about 8 KiB of codes in flight per wave. A packed
+// table with one block per lane (H up to 2,048) runs 4 rows per iteration,
+// and 2 once a pass holds 4 or more hidden rows (sweep on MI355X at
+// 65,536 x 2,048: 18.6 against 19.3 us at M = 1, 31.9 against 35.1 us at
+// M = 4). Gathered rows keep 8: each row waits on its id first, and 4 rows
+// per iteration were slower there (22.2 against 21.2 us at M = 1).
+template <int MR, int NCL, bool GATHER>
 constexpr int fp4_rb() {
-  if (NCL == 1) return MR >= 4 ? 2 : 4;
+  if (NCL == 1 && !GATHER) return MR >= 4 ? 2 : 4;
   return NCL >= 8 ? 1 : 8 / NCL;
+}
+
+template <int MR, int NCL, bool GATHER>
+static hipError_t launch_fp4_shape(const Fp4Launch &L) {
+  constexpr int RB = fp4_rb<MR, NCL, GATHER>();
+  const int64_t row_blocks = (L.N + RB - 1) / RB;
+  const int64_t want = (row_blocks + kFp4Waves - 1) / kFp4Waves;
+  const int gx = (int)(want < L.max_blocks_x ? want : L.max_blocks_x);
+  const int gy = (L.M + MR - 1) / MR;
+  const dim3 grid(gx, gy), block(kFp4Threads);
+  const uint4 *X = (const uint4 *)L.X, *Q = (const uint4 *)L.Q;
+  const int32_t *gids = GATHER ? L.gather_ids : nullptr;
+  const int64_t gV = GATHER ? L.gather_V : 0;
+  if (L.nblk == NCL * kWave)
+    hipLaunchKernelGGL((gemv_argmax_mxfp4<MR, NCL, RB, true, GATHER>), grid, block, 0, L.stream,
+                       X, Q, L.scales, L.M, L.N, L.nblk, gids, gV, L.sink);
+  else
+    hipLaunchKernelGGL((gemv_argmax_mxfp4<MR, NCL, RB, false, GATHER>), grid, block, 0, L.stream,
+                       X, Q, L.scales, L.M, L.N, L.nblk, gids, gV, L.sink);
+  return hipGetLastError();
 }
 
 template <int MR, int NCL>
@@ -393,30 +414,8 @@ static hipError_t launch_fp4_cfg(const Fp4Launch &L) {
   if constexpr (MR * NCL > 8) {
     return hipErrorInvalidValue;
   } else {
-    constexpr int RB = fp4_rb<MR, NCL>();
-    const int64_t row_blocks = (L.N + RB - 1) / RB;
-    const int64_t want = (row_blocks + kFp4Waves - 1) / kFp4Waves;
-    const int gx = (int)(want < L.max_blocks_x ? want : L.max_blocks_x);
-    const int gy = (L.M + MR - 1) / MR;
-    const bool exact = L.nblk == NCL * kWave;
-    const dim3 grid(gx, gy), block(kFp4Threads);
-    const uint4 *X = (const uint4 *)L.X, *Q = (const uint4 *)L.Q;
-    if (L.gather_ids) {
-      if (exact)
-        hipLaunchKernelGGL((gemv_argmax_mxfp4<MR, NCL, RB, true, true>), grid, block, 0, L.stream,
-                           X, Q, L.scales, L.M, L.N, L.nblk, L.gather_ids, L.gather_V, L.sink);
-      else
-        hipLaunchKernelGGL((gemv_argmax_mxfp4<MR, NCL, RB, false, true>), grid, block, 0,
-                           L.stream, X, Q, L.scales, L.M, L.N, L.nblk, L.gather_ids, L.gather_V,
-                           L.sink);
-    } else if (exact) {
-      hipLaunchKernelGGL((gemv_argmax_mxfp4<MR, NCL, RB, true, false>), grid, block, 0, L.stream,
-                         X, Q, L.scales, L.M, L.N, L.nblk, nullptr, (int64_t)0, L.sink);
-    } else {
-      hipLaunchKernelGGL((gemv_argmax_mxfp4<MR, NCL, RB, false, false>), grid, block, 0, L.stream,
-                         X, Q, L.scales, L.M, L.N, L.nblk, nullptr, (int64_t)0, L.sink);
-    }
-    return hipGetLastError();
+    return L.gather_ids ? launch_fp4_shape<MR, NCL, true>(L)
+                        : launch_fp4_shape<MR, NCL, false>(L);
   }
 }
 

@@ -379,14 +379,35 @@ __global__ void __launch_bounds__(kFp8Threads)
   finish_rows(sink, f_val, f_row, m0, min(MR, M - m0));
 }
 
-// Rows per iteration: about 8 KiB of codes in flight per wave, except for
-// two chunks per lane (H up to 2,048) once a pass holds 4 or more hidden
-// rows, where 2 rows per iteration were faster (sweep on MI355X at
-// 65,536 x 2,048: 32.9 against 34.9 us at M = 4; at M = 1, 4 rows stay best).
-template <int MR, int NCL>
+// Rows per iteration: about 8 KiB of codes in flight per wave. A packed
+// table with two chunks per lane (H up to 2,048) runs 2 rows per iteration
+// once a pass holds 4 or more hidden rows (sweep on MI355X at
+// 65,536 x 2,048: 32.9 against 34.9 us at M = 4; at M = 1, 4 rows stay
+// best). Gathered rows keep the general rule (each row waits on its id).
+template <int MR, int NCL, bool GATHER>
 constexpr int fp8_rb() {
-  if (NCL == 2 && MR >= 4) return 2;
+  if (NCL == 2 && MR >= 4 && !GATHER) return 2;
   return NCL >= 8 ? 1 : (8 / NCL > 4 ? 4 : 8 / NCL);
+}
+
+template <int MR, int NCL, bool GATHER>
+static hipError_t launch_fp8_shape(const Fp8Launch &L) {
+  constexpr int RB = fp8_rb<MR, NCL, GATHER>();
+  const int64_t row_blocks = (L.N + RB - 1) / RB;
+  const int64_t want = (row_blocks + kFp8Waves - 1) / kFp8Waves;
+  const int gx = (int)(want < L.max_blocks_x ? want : L.max_blocks_x);
+  const int gy = (L.M + MR - 1) / MR;
+  const dim3 grid(gx, gy), block(kFp8Threads);
+  const uint4 *X = (const uint4 *)L.X, *Q = (const uint4 *)L.Q;
+  const int32_t *gids = GATHER ? L.gather_ids : nullptr;
+  const int64_t gV = GATHER ? L.gather_V : 0;
+  if (L.ncq == NCL * kWave)
+    hipLaunchKernelGGL((gemv_argmax_fp8<MR, NCL, RB, true, GATHER>), grid, block, 0, L.stream, X,
+                       Q, L.scales, L.M, L.N, L.ncq, gids, gV, L.sink);
+  else
+    hipLaunchKernelGGL((gemv_argmax_fp8<MR, NCL, RB, false, GATHER>), grid, block, 0, L.stream, X,
+                       Q, L.scales, L.M, L.N, L.ncq, gids, gV, L.sink);
+  return hipGetLastError();
 }
 
 template <int MR, int NCL>
@@ -395,29 +416,8 @@ static hipError_t launch_fp8_cfg(const Fp8Launch &L) {
   if constexpr (MR * NCL > 16) {
     return hipErrorInvalidValue;
   } else {
-  constexpr int RB = fp8_rb<MR, NCL>();
-  const int64_t row_blocks = (L.N + RB - 1) / RB;
-  const int64_t want = (row_blocks + kFp8Waves - 1) / kFp8Waves;
-  const int gx = (int)(want < L.max_blocks_x ? want : L.max_blocks_x);
-  const int gy = (L.M + MR - 1) / MR;
-  const bool exact = L.ncq == NCL * kWave;
-  const dim3 grid(gx, gy), block(kFp8Threads);
-  const uint4 *X = (const uint4 *)L.X, *Q = (const uint4 *)L.Q;
-  if (L.gather_ids) {
-    if (exact)
-      hipLaunchKernelGGL((gemv_argmax_fp8<MR, NCL, RB, true, true>), grid, block, 0, L.stream, X,
-                         Q, L.scales, L.M, L.N, L.ncq, L.gather_ids, L.gather_V, L.sink);
-    else
-      hipLaunchKernelGGL((gemv_argmax_fp8<MR, NCL, RB, false, true>), grid, block, 0, L.stream, X,
-                         Q, L.scales, L.M, L.N, L.ncq, L.gather_ids, L.gather_V, L.sink);
-  } else if (exact) {
-    hipLaunchKernelGGL((gemv_argmax_fp8<MR, NCL, RB, true, false>), grid, block, 0, L.stream, X,
-                       Q, L.scales, L.M, L.N, L.ncq, nullptr, (int64_t)0, L.sink);
-  } else {
-    hipLaunchKernelGGL((gemv_argmax_fp8<MR, NCL, RB, false, false>), grid, block, 0, L.stream, X,
-                       Q, L.scales, L.M, L.N, L.ncq, nullptr, (int64_t)0, L.sink);
-  }
-  return hipGetLastError();
+    return L.gather_ids ? launch_fp8_shape<MR, NCL, true>(L)
+                        : launch_fp8_shape<MR, NCL, false>(L);
   }
 }
 
