@@ -587,6 +587,38 @@ def pin_worked_accept(oracle):
     assert Fraction(total_acc, total_prop) == Fraction(ex["value_num"], ex["value_den"])
 
 
+def pin_worked_verify(oracle):
+    """Hand-worked verify steps of tests/golden/verify_worked.json: the rows
+    of a [B*(k+1)][H] hidden block are read sequence-major (row b*(k+1)+p is
+    position p of sequence b), each takes its full-head argmax (lowest id on
+    ties), and acceptance runs on that [B][k+1] target. One case has B = k+1,
+    so a position-major reading keeps the shape but fails the values."""
+    g = _golden("verify_worked.json")
+    perm = g["perm"]
+    V = H = len(perm)
+    head_f = np.zeros((V, H), np.float32)
+    for v, col in enumerate(perm):
+        head_f[v, col] = 1.0
+    hidden_f = np.asarray(g["hidden"], np.float32)
+    head, hidden = bits_of(head_f), bits_of(hidden_f)
+    # the fixture's values are exact in bfloat16
+    assert np.array_equal(wl.bf16_bits_to_f32(hidden), hidden_f)
+    # the fixture's own arithmetic: the logit of id v is hidden[perm[v]]
+    for r, row in enumerate(g["hidden"]):
+        z = [row[perm[v]] for v in range(V)]
+        assert _first_max(z) == g["row_argmax"][r] and max(z) == g["row_max_logit"][r]
+    for c in g["cases"]:
+        B, k = c["B"], c["k"]
+        x = hidden[c["rows"]]
+        out = oracle.verify(x, head, B, k, np.asarray(c["draft"], np.int32))
+        assert out["id"].shape == (B, k + 1), out["id"].shape
+        assert out["id"].tolist() == c["target"], (c["_note"], out["id"].tolist())
+        want_logit = np.asarray(g["row_max_logit"], np.float32)[c["rows"]].reshape(B, k + 1)
+        assert np.array_equal(out["logit"], want_logit), out["logit"]
+        assert out["accept"].tolist() == c["accept"], out["accept"]
+        assert out["tokens"].tolist() == c["tokens"], out["tokens"]
+
+
 def pin_accept_invariants(oracle, seed=3):
     """0 <= n <= k; tokens[:n] == drafts[:n]; tokens[n] == target[n];
     if n < k the draft at n disagrees; slots after n are -1; p=1 accepts all,
@@ -666,6 +698,7 @@ ALL_PINS = [
     pin_mxfp4_gathered_candidates,
     pin_pack,
     pin_worked_accept,
+    pin_worked_verify,
     pin_accept_invariants,
     pin_acceptance_law,
     pin_pages_layout,

@@ -1,9 +1,11 @@
 """Pin strength: oracle builds with one planted mistake each must fail at
 least one pin. The mistakes are planted in a temporary copy of the oracle's
-C source, compiled on the CPU; the real oracle is untouched."""
+C source, compiled on the CPU; the real oracle is untouched. The verify composition
+(Python) gets planted mistakes through a patched function."""
 
 import os
 
+import numpy as np
 import pytest
 
 from tests import oracle_pins
@@ -61,3 +63,42 @@ def test_mutant_fails_a_pin(oracle_mod, tmp_path, name, old, new):
                 failed.append(pin.__name__)
                 break
     assert failed, f"mutant {name} passed every pin"
+
+
+def _verify_position_major(oracle_mod):
+    """oracle.verify with the rows read position-major (a transposed reshape)."""
+    def verify(hv, head, B, k, draft_ids=None):
+        r = oracle_mod.argmax(hv, head, None)
+        out = {key: v.reshape(k + 1, B).T.copy() for key, v in r.items()}
+        if draft_ids is not None:
+            out.update(oracle_mod.accept(draft_ids, out["id"]))
+        return out
+    return verify
+
+
+def _verify_shifted_target(oracle_mod):
+    """oracle.verify comparing draft p with the target of position p + 1."""
+    def verify(hv, head, B, k, draft_ids=None):
+        r = oracle_mod.argmax(hv, head, None)
+        out = {key: v.reshape(B, k + 1) for key, v in r.items()}
+        if draft_ids is not None:
+            shifted = np.concatenate([out["id"][:, 1:], out["id"][:, -1:]], axis=1)
+            out.update(oracle_mod.accept(draft_ids, shifted))
+        return out
+    return verify
+
+
+@pytest.mark.parametrize("make", [_verify_position_major, _verify_shifted_target],
+                         ids=["verify_position_major", "verify_shifted_target"])
+def test_verify_mutant_fails_a_pin(oracle_mod, monkeypatch, make):
+    """The verify composition (reshape to [B][k+1], acceptance on it) is
+    Python; its planted mistakes must fail a pin too."""
+    monkeypatch.setattr(oracle_mod, "verify", make(oracle_mod))
+    failed = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(oracle_mod)
+        except (AssertionError, oracle_mod.OracleError, ValueError, IndexError):
+            failed.append(pin.__name__)
+            break
+    assert failed, "planted verify mistake passed every pin"
