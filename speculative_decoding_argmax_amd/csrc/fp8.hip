@@ -5,9 +5,12 @@
 // mantissa bits, subnormals m * 2^-9, no infinities, S.1111.111 NaN, largest
 // magnitude 448). Each row has one scale 2^e, the smallest power of two with
 // max|w| <= 448 * 2^e (e = 0 for an all-zero row); element j is the E4M3
-// code nearest to w[j] * 2^-e, ties to the even code. The pack does this in
-// double precision, where every step is exact except the one rounding, so the
-// codes are the format's definition applied to the bf16 values.
+// code nearest to w[j] * 2^-e, ties to the even code. The pack works on the
+// integer fields of the bf16 encoding only: a bf16 value is an 8-bit
+// significand times a power of two, the scale shifts that power, and the
+// E4M3 code is the significand shifted right to 3 fraction bits (or to the
+// 2^-9 subnormal step) with round-half-to-even on the dropped bits, the carry
+// running into the exponent field. No floating-point arithmetic is involved.
 //
 // The draft kernel streams 16 codes (16 bytes) per lane and load, converts
 // them to bf16 pairs with v_cvt_scalef32_pk_bf16_fp8 (exact: every E4M3
@@ -26,30 +29,73 @@ typedef unsigned u32x4_fp8_t __attribute__((ext_vector_type(4)));
 
 // ---- quantising pack ------------------------------------------------------
 
-// Nearest E4M3 code of x (ties to even, magnitudes >= 448 saturate to 448,
-// NaN gives 0x7F).
-__device__ uint8_t e4m3_code(double x) {
-  if (isnan(x)) return 0x7F;
-  const uint8_t sign = signbit(x) ? 0x80 : 0x00;
-  const double a = fabs(x);
-  if (a >= 448.0) return sign | 0x7E;
-  if (a < 0.015625) {  // below 2^-6: subnormal steps of 2^-9
-    return sign | (uint8_t)rint(ldexp(a, 9));
+// A finite nonzero bf16 magnitude (15 bits, sign dropped) as sig * 2^ex with
+// an 8-bit significand sig in [128, 255]; subnormal bf16 values are shifted
+// up to that form. Zero gives sig = 0.
+__device__ __forceinline__ void bf16_sig_exp(uint32_t mag, int &sig, int &ex) {
+  const int E = (int)(mag >> 7);
+  const int f = (int)(mag & 0x7Fu);
+  if (E != 0) {
+    sig = 128 | f;
+    ex = E - 134;
+  } else if (f != 0) {
+    const int sh = __clz(f) - 24;  // moves the highest set bit to bit 7
+    sig = f << sh;
+    ex = -133 - sh;
+  } else {
+    sig = 0;
+    ex = 0;
   }
-  int E;
-  frexp(a, &E);  // a = f * 2^E, f in [0.5, 1)
-  int ue = E - 1;
-  double r = rint(ldexp(a, 3 - ue));  // 8 .. 16 eighths
-  if (r == 16.0) {
-    r = 8.0;
-    ue += 1;
-  }
-  if (ue > 8 || (ue == 8 && r > 14.0)) return sign | 0x7E;
-  return sign | (uint8_t)(((ue + 7) << 3) | ((int)r - 8));
 }
 
-__device__ __forceinline__ double bf16_value(uint32_t bits16) {
-  return (double)__uint_as_float(bits16 << 16);
+// x >> sh rounded to nearest, ties to even (x < 2^16, sh >= 1).
+__device__ __forceinline__ uint32_t shr_round_even(uint32_t x, int sh) {
+  if (sh > 20) return 0u;  // x / 2^sh < 1/2
+  const uint32_t q = x >> sh;
+  const uint32_t rem = x & ((1u << sh) - 1u);
+  const uint32_t half = 1u << (sh - 1);
+  return q + ((rem > half || (rem == half && (q & 1u))) ? 1u : 0u);
+}
+
+// Row scale exponent from the row's largest bf16 magnitude: the smallest e
+// with sig * 2^ex <= 448 * 2^e = 7 * 2^(6 + e). With sig in [128, 255] the
+// bound 7 * 2^d first covers sig at d = 5 (224) when sig <= 224, else at
+// d = 6 (448), and e = ex + d - 6. A zero row keeps e = 0.
+__device__ __forceinline__ int fp8_row_exp(uint32_t max_mag) {
+  int sig, ex;
+  bf16_sig_exp(max_mag, sig, ex);
+  if (sig == 0) return 0;
+  return sig <= 224 ? ex - 1 : ex;
+}
+
+// 2^e as an fp32 bit pattern (e in [-149, 127]; the pack's range is
+// [-141, 120]).
+__device__ __forceinline__ float pow2_f32(int e) {
+  return __uint_as_float(e >= -126 ? (uint32_t)(e + 127) << 23 : 1u << (e + 149));
+}
+
+// E4M3 code of the bf16 value `bits` times 2^-e: nearest code, ties to the
+// even code, magnitudes past 448 saturating to 448 (code 0x7E), the sign bit
+// kept also when the magnitude rounds to zero.
+__device__ __forceinline__ uint32_t e4m3_of_bf16(uint32_t bits, int e) {
+  const uint32_t sign = (bits >> 8) & 0x80u;
+  int sig, ex;
+  bf16_sig_exp(bits & 0x7FFFu, sig, ex);
+  if (sig == 0) return sign;
+  // y = sig * 2^(ex - e) lies in [2^u, 2^(u+1)) with u = ex - e + 7; its
+  // E4M3 exponent field would be be = u + 7
+  const int be = ex - e + 14;
+  uint32_t c;
+  if (be >= 1) {
+    // normal code: exponent field and the 7 fraction bits of sig, rounded
+    // to 3 fraction bits; a carry out of the fraction bumps the exponent
+    c = shr_round_even(((uint32_t)be << 7) | (uint32_t)(sig & 0x7F), 4);
+  } else {
+    // subnormal code: y in steps of 2^-9 is sig * 2^(be - 5); a count of 8
+    // is code 0x08, the smallest normal value 2^-6
+    c = shr_round_even((uint32_t)sig, 5 - be);
+  }
+  return sign | (c > 0x7Eu ? 0x7Eu : c);
 }
 
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
@@ -86,15 +132,8 @@ __global__ void __launch_bounds__(256)
       }
     }
     mx = valid ? wave_max_u32(mx) : 0u;
-    int e = 0;
-    // (a row holding Inf or NaN is outside the contract: it keeps e = 0, so
-    // the search below always ends)
-    if (mx != 0 && mx < 0x7F80u) {
-      const double amax = bf16_value(mx);
-      e = ilogb(amax) - 8;
-      while (ldexp(448.0, e) < amax) ++e;
-      while (ldexp(448.0, e - 1) >= amax) --e;
-    }
+    // a row holding Inf or NaN is outside the contract: it keeps e = 0
+    const int e = mx < 0x7F80u ? fp8_row_exp(mx) : 0;
     uint2 *dst = q + row * (int64_t)(H / 8);
     for (int c = lane; c < nch; c += kWave) {
       uint32_t b[2] = {0u, 0u};
@@ -104,13 +143,13 @@ __global__ void __launch_bounds__(256)
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
           const uint32_t bits = (k & 1) ? (w[k >> 1] >> 16) : (w[k >> 1] & 0xFFFFu);
-          const uint32_t code = e4m3_code(ldexp(bf16_value(bits), -e));
+          const uint32_t code = e4m3_of_bf16(bits, e);
           b[k >> 2] |= code << (8 * (k & 3));
         }
       }
       dst[c] = make_uint2(b[0], b[1]);
     }
-    if (lane == 0) scales[row] = valid ? (float)ldexp(1.0, e) : 1.0f;
+    if (lane == 0) scales[row] = valid ? pow2_f32(e) : 1.0f;
   }
 }
 
@@ -159,13 +198,7 @@ __global__ void __launch_bounds__(256)
       }
     }
     mx = wave_max_u32(mx);
-    int e = 0;
-    if (mx != 0 && mx < 0x7F80u) {
-      const double amax = bf16_value(mx);
-      e = ilogb(amax) - 8;
-      while (ldexp(448.0, e) < amax) ++e;
-      while (ldexp(448.0, e - 1) >= amax) --e;
-    }
+    const int e = mx < 0x7F80u ? fp8_row_exp(mx) : 0;
     const int64_t t = row / 64;
     const int rb = (int)(row % 64) / 16;
     const int jj = (int)(row % 16);
@@ -177,7 +210,7 @@ __global__ void __launch_bounds__(256)
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
           const uint32_t bits = (k & 1) ? (w[k >> 1] >> 16) : (w[k >> 1] & 0xFFFFu);
-          const uint32_t code = e4m3_code(ldexp(bf16_value(bits), -e));
+          const uint32_t code = e4m3_of_bf16(bits, e);
           b[k >> 2] |= code << (8 * (k & 3));
         }
       }
@@ -185,7 +218,7 @@ __global__ void __launch_bounds__(256)
       const int64_t off = ((((t * SP + s / 2) * 4 + rb) * kWave + jj + 16 * g) * 16) + (s & 1) * 8;
       *reinterpret_cast<uint2 *>(tiled + off) = make_uint2(b[0], b[1]);
     }
-    if (lane == 0 && row < C) scales[row] = valid ? (float)ldexp(1.0, e) : 1.0f;
+    if (lane == 0 && row < C) scales[row] = valid ? pow2_f32(e) : 1.0f;
   }
 }
 
