@@ -209,10 +209,20 @@ def mtp_verify_workspace_bytes(B: int, k: int, V: int, H: int) -> int:
 
 
 def alloc_workspace(nbytes: int, device=None, stream=None):
-    """Allocate (torch) and zero (mtp_workspace_init) a workspace of nbytes."""
+    """Allocate (torch) and zero (mtp_workspace_init) a workspace of nbytes.
+
+    With ``stream`` given, the block is allocated on that stream: torch's
+    caching allocator then hands it out again only to later work on the same
+    stream, so a workspace that the caller drops right after an asynchronous
+    call on a side stream is never reused while that call still runs.
+    """
     torch = _torch()
     n = max(8, (int(nbytes) + 7) // 8 * 8)
-    ws = torch.empty(n // 8, dtype=torch.int64, device=device or "cuda")
+    if stream is None:
+        ws = torch.empty(n // 8, dtype=torch.int64, device=device or "cuda")
+    else:
+        with torch.cuda.stream(stream):
+            ws = torch.empty(n // 8, dtype=torch.int64, device=device or "cuda")
     mtp_workspace_init(ws, stream=stream)
     return ws
 

@@ -293,3 +293,32 @@ def test_shard_exchange_equals_unsharded(torch, mtp, G):
                 best_id, best_v = int(pid[m]), pv[m]
         assert best_id == int(full[0][m])
         assert np.float32(best_v).view(np.uint32) == np.float32(full[1][m]).view(np.uint32)
+
+
+def test_side_stream_call_without_workspace(torch, mtp):
+    """A call on a side stream with ws=None: the binding allocates the
+    workspace on that stream, so the caching allocator cannot hand the block
+    to work on the current stream (here a large fill launched right after the
+    call returns) while the draft kernel still uses it. Repeated calls must
+    all give the oracle's pick."""
+    M, N, H = 4, 200_003, 2048
+    x = wl.exact_grid_bf16((M, H), 77, 1)
+    w = wl.exact_grid_bf16((N, H), 77, 2)
+    x_d, w_d = dev_bf16(x), dev_bf16(w)
+    orc = oracle.argmax(x, w, None)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for _ in range(6):
+        oi = torch.full((M,), -7, dtype=torch.int32, device="cuda")
+        ol = torch.full((M,), float("nan"), dtype=torch.float32, device="cuda")
+        side.wait_stream(torch.cuda.current_stream())
+        mtp.mtp_draft_argmax(x_d, w_d, None, oi, ol, stream=side)
+        # freed workspace block: work on the current stream must not get it
+        junk = torch.full((1 << 16,), -1, dtype=torch.int64, device="cuda")
+        del junk
+        outs.append((oi, ol))
+    torch.cuda.synchronize()
+    for oi, ol in outs:
+        assert np.array_equal(oi.cpu().numpy(), orc["id"])
+        assert np.array_equal(ol.cpu().numpy(), orc["logit"])
