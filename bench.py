@@ -15,7 +15,9 @@ draft calls of one step read three different copies of the candidate table, so
 no call is served from the 256 MB Infinity Cache by its predecessor; the
 verify head (>= 1 GB) cannot stay cached between steps. Kernel durations come
 from HIP events recorded on the launch stream around the draft block and the
-verify launch of every fifth timed step (--event-every). Prints one JSON line.
+verify launch of the timed steps (every step when fewer than 50 are timed, else
+every fifth; --event-every), after a warm-up of at least --warmup-seconds.
+Prints one JSON line.
 
 --workload draft_ablation adds context.draft_tables: the M = 1 draft timed over
 the full head, the 65,536-row and the nested 32,768-row tables (and the pages'
@@ -75,8 +77,13 @@ def parse_args():
     ap.add_argument("--graph", action="store_true",
                     help="time the steps as replays of a captured HIP graph (mtp_graph_*); "
                          "per-call durations still come from event-bracketed eager launches")
-    ap.add_argument("--event-every", type=int, default=5,
-                    help="record the per-call HIP events on every n-th timed step")
+    ap.add_argument("--event-every", type=int, default=None,
+                    help="record the per-call HIP events on every n-th timed step (default: "
+                         "every step when fewer than 50 steps are timed, else every 5th)")
+    ap.add_argument("--warmup-seconds", type=float, default=1.0,
+                    help="after the --warmup steps, keep running untimed steps until the warm-up "
+                         "has lasted this long, so that the timed steps start with the GPU's "
+                         "clocks and queues already in their steady state")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall-clock budget of the CPU oracle sample")
@@ -279,9 +286,11 @@ def main() -> int:
 
     n_tab = len(tables)
 
-    def step(i: int, ev=None):
-        # ev: (before drafts, after drafts = before verify, after verify)
-        if ev is not None:
+    def step(i: int, ev=None, record_start: bool = True):
+        # ev: (before drafts, after drafts = before verify, after verify);
+        # record_start False: ev[0] is the previous step's end event, already
+        # recorded
+        if ev is not None and record_start:
             ev[0].record(stream)
         for c in range(wk.draft_calls):
             draft_call(c, tables[(i * wk.draft_calls + c) % n_tab])
@@ -291,9 +300,22 @@ def main() -> int:
         if ev is not None:
             ev[2].record(stream)
 
+    # Warm-up: the --warmup steps, then more untimed steps until the warm-up
+    # has lasted --warmup-seconds. A short timed region started right after
+    # set-up (host uploads, packing, one synchronising verify call) otherwise
+    # runs while the GPU is still raising its clocks.
+    t_w = time.perf_counter()
+    n_warm = 0
     for i in range(args.warmup):
         step(i)
+        n_warm += 1
     torch.cuda.synchronize()
+    while time.perf_counter() - t_w < args.warmup_seconds:
+        for _ in range(20):
+            step(n_warm)
+            n_warm += 1
+        torch.cuda.synchronize()
+    warmup_s = time.perf_counter() - t_w
 
     K = args.steps
     graphs = []
@@ -310,26 +332,37 @@ def main() -> int:
             graphs[i % n_tab].launch()
         torch.cuda.synchronize()
 
-    # Per-call events go on every n-th timed step only: each recorded event
-    # costs the stream a few microseconds, which on every step would slow the
-    # whole job by about 4%.
-    every = max(1, args.event_every)
+    # Per-call events: each recorded event costs the stream a few
+    # microseconds, which on every step slows the whole job by about 4%, so
+    # long runs record them on every 5th step; short runs record them on every
+    # step, so that the per-call figures rest on enough samples.
+    every = max(1, args.event_every) if args.event_every is not None else (1 if K < 50 else 5)
 
     def timed_steps(with_events: bool, use_graph: bool):
-        evs = {i: tuple(torch.cuda.Event(enable_timing=True) for _ in range(3))
-               for i in range(0, K, every)} if with_events else {}
+        # with events on every step, consecutive steps share their boundary
+        # event (the end of step i is the start of step i + 1), so each step
+        # records two events instead of three
+        chained = with_events and every == 1
+        if chained:
+            bounds = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+            mids = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+            evs = {i: (bounds[i], mids[i], bounds[i + 1]) for i in range(K)}
+        else:
+            evs = {i: tuple(torch.cuda.Event(enable_timing=True) for _ in range(3))
+                   for i in range(0, K, every)} if with_events else {}
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(K):
             ev = evs.get(i)
+            first = not chained or i == 0
             if use_graph:
-                if ev:
+                if ev and first:
                     ev[0].record(stream)
                 graphs[i % n_tab].launch()
                 if ev:
                     ev[2].record(stream)
             else:
-                step(i, ev)
+                step(i, ev, record_start=first)
         torch.cuda.synchronize()
         return time.perf_counter() - t0, list(evs.values())
 
@@ -528,6 +561,8 @@ def main() -> int:
         "context": {
             "ms_per_step_without_kernel_events": round(t_noev * 1000.0 / K, 4),
             "kernel_event_steps": f"1 in {every} timed steps ({len(evs)} of {K})",
+            "warmup_steps_run": n_warm,
+            "warmup_s": round(warmup_s, 3),
             "step_mode": "hip_graph" if graphs else "eager",
             "graph_step_us_mean": round(statistics.mean(graph_step_ms) * 1000.0, 2)
             if graph_step_ms else None,
