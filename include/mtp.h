@@ -187,6 +187,34 @@ mtp_status mtp_verify_accept_cfg(const mtp_bf16 *hidden, int B, int k, int H,
                                  hipStream_t stream, const mtp_config *cfg);
 
 /*
+ * Allocation-free verify, for callers that cannot allocate device memory or
+ * hold a workspace: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. Same arguments, kernels and results as
+ * mtp_verify_accept (row-major head), without ws / ws_bytes. The ticket and
+ * the per-row keys live in a static device array of the library, 8,448 bytes
+ * (header + MTP_NOALLOC_MAX_ROWS keys), which every GPU the library runs on
+ * holds from its first such call until the process ends; this array is the
+ * one exception to "the library allocates nothing".
+ *   - B*(k+1) <= MTP_NOALLOC_MAX_ROWS; a larger call returns
+ *     MTP_ERR_WORKSPACE with nothing enqueued. Other argument errors are those
+ *     of mtp_verify_accept.
+ *   - The array keeps what the last call left in it. Each call first clears
+ *     the part it uses (one small kernel on `stream`, no hipMemsetAsync).
+ *   - All calls on one GPU share its array: calls that may overlap (other
+ *     streams, or threads without ordering between them) race and give
+ *     undefined results. Order them on one stream, or use mtp_verify_accept
+ *     with one workspace per stream.
+ *   - No hipMalloc, hipFree or allocating library routine is called. The first
+ *     call on a device looks up the array's device address
+ *     (hipGetSymbolAddress); a failure there returns MTP_ERR_HIP.
+ */
+#define MTP_NOALLOC_MAX_ROWS 1024
+mtp_status mtp_verify_accept_noalloc(const mtp_bf16 *hidden, int B, int k, int H,
+                                     const mtp_bf16 *head, int64_t V, const int32_t *draft,
+                                     int32_t *out_argmax, float *out_logit, int32_t *out_accept,
+                                     int32_t *out_tokens, hipStream_t stream);
+
+/*
  * Tiled tables (batched rows).
  *
  * When one call scores many hidden rows (a batch of sequences), the table

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <mutex>
 #include <new>
 #include <cstdint>
 #include <cstring>
@@ -201,11 +202,11 @@ mtp::RowSink draft_sink(void *ws, const int32_t *ids, int32_t *out_ids, float *o
   return s;
 }
 
-mtp_status check_verify_args(const mtp_bf16 *hidden, int B, int k, int H, const void *head,
-                             int64_t V, const int32_t *draft, const int32_t *out_argmax,
-                             const float *out_logit, const int32_t *out_accept,
-                             const int32_t *out_tokens, const void *ws, size_t ws_bytes,
-                             const mtp_config *cfg) {
+// Verify arguments other than the workspace.
+mtp_status check_verify_io(const mtp_bf16 *hidden, int B, int k, int H, const void *head,
+                           int64_t V, const int32_t *draft, const int32_t *out_argmax,
+                           const float *out_logit, const int32_t *out_accept,
+                           const int32_t *out_tokens) {
   if (!hidden || !head || !out_argmax || !out_accept || !out_tokens) return MTP_ERR_INVALID_ARG;
   if (B < 1 || k < 0 || k > MTP_MAX_K) return MTP_ERR_INVALID_ARG;
   if (k > 0 && !draft) return MTP_ERR_INVALID_ARG;
@@ -215,7 +216,19 @@ mtp_status check_verify_args(const mtp_bf16 *hidden, int B, int k, int H, const 
       !aligned(out_accept, 4) || !aligned(out_tokens, 4) || (draft && !aligned(draft, 4)) ||
       (out_logit && !aligned(out_logit, 4)))
     return MTP_ERR_INVALID_ARG;
-  mtp_status st = check_cfg(cfg);
+  return MTP_OK;
+}
+
+mtp_status check_verify_args(const mtp_bf16 *hidden, int B, int k, int H, const void *head,
+                             int64_t V, const int32_t *draft, const int32_t *out_argmax,
+                             const float *out_logit, const int32_t *out_accept,
+                             const int32_t *out_tokens, const void *ws, size_t ws_bytes,
+                             const mtp_config *cfg) {
+  mtp_status st = check_verify_io(hidden, B, k, H, head, V, draft, out_argmax, out_logit,
+                                  out_accept, out_tokens);
+  if (st != MTP_OK) return st;
+  const int64_t M = (int64_t)B * (k + 1);
+  st = check_cfg(cfg);
   if (st != MTP_OK) return st;
   if (!ws || !aligned(ws, 8)) return MTP_ERR_WORKSPACE;
   if (ws_bytes < rows_workspace_bytes(M)) return MTP_ERR_WORKSPACE;
@@ -239,6 +252,45 @@ mtp::RowSink verify_sink(void *ws, int B, int k, const int32_t *draft, int32_t *
   s.out_tokens = out_tokens;
   return s;
 }
+
+// ---- Scratch of the allocation-free verify ---------------------------------
+//
+// mtp_verify_accept_noalloc keeps its workspace (ticket header + one 64-bit key
+// per hidden row, the layout mtp_verify_accept uses) in this file-scope device
+// array instead of a caller-provided buffer. Every GPU the library runs on
+// holds its own copy, at its own address, until the process ends. In host code
+// `scratch` names a host-side stand-in, never the device memory: the device
+// address is taken once per device with hipGetSymbolAddress (that device
+// current) and only that address is passed to kernels.
+constexpr size_t kScratchBytes =
+    mtp::kWsHeader + (((size_t)MTP_NOALLOC_MAX_ROWS * 8 + 255) / 256) * 256;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+std::atomic<void *> g_scratch_dev[kMaxDevices];
+
+// Device address of the current device's scratch (looked up on first use).
+hipError_t scratch_address(void **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void *p = g_scratch_dev[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_dev[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (!p) return hipErrorInvalidSymbol;
+      g_scratch_dev[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return hipSuccess;
+}
+
+static_assert(kScratchBytes == 8448, "the size mtp.h states for the scratch array");
 
 }  // namespace
 
@@ -340,6 +392,29 @@ mtp_status mtp_verify_accept(const mtp_bf16 *hidden, int B, int k, int H, const 
                              void *ws, size_t ws_bytes, hipStream_t stream) {
   return mtp_verify_accept_cfg(hidden, B, k, H, head, V, draft, out_argmax, out_logit,
                                out_accept, out_tokens, ws, ws_bytes, stream, nullptr);
+}
+
+mtp_status mtp_verify_accept_noalloc(const mtp_bf16 *hidden, int B, int k, int H,
+                                     const mtp_bf16 *head, int64_t V, const int32_t *draft,
+                                     int32_t *out_argmax, float *out_logit, int32_t *out_accept,
+                                     int32_t *out_tokens, hipStream_t stream) {
+  mtp_status st = check_verify_io(hidden, B, k, H, head, V, draft, out_argmax, out_logit,
+                                  out_accept, out_tokens);
+  if (st != MTP_OK) return st;
+  const int64_t M = (int64_t)B * (k + 1);
+  if (M > MTP_NOALLOC_MAX_ROWS) return MTP_ERR_WORKSPACE;
+  void *ws = nullptr;
+  hipError_t e = scratch_address(&ws);
+  if (e != hipSuccess) return hip_fail(e);
+  // The array keeps whatever the last call on this device left in it: clear
+  // the ticket and this call's keys first (a kernel, stream-ordered before
+  // the verify kernels; no hipMemsetAsync).
+  const size_t used = rows_workspace_bytes(M);
+  e = mtp::launch_fill_zero(ws, used, stream);
+  if (e != hipSuccess) return hip_fail(e);
+  return run_rows(hidden, B * (k + 1), H, head, V,
+                  verify_sink(ws, B, k, draft, out_argmax, out_logit, out_accept, out_tokens),
+                  stream, nullptr);
 }
 
 size_t mtp_tiled_bytes(int64_t rows, int H) { return tiled_bytes_of(rows, H); }

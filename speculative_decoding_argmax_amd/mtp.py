@@ -35,6 +35,7 @@ MTP_PATH_MFMA = 2
 
 MTP_MAX_K = 15
 MTP_MAX_ROWS = 4096
+MTP_NOALLOC_MAX_ROWS = 1024
 MTP_MAX_HIDDEN = 16384
 
 
@@ -79,6 +80,7 @@ def _load() -> ctypes.CDLL:
         "mtp_draft_argmax_cfg": ([P, I, I, P, P, I64, P, P, P, S, P, P], I),
         "mtp_verify_accept": ([P, I, I, I, P, I64, P, P, P, P, P, P, S, P], I),
         "mtp_verify_accept_cfg": ([P, I, I, I, P, I64, P, P, P, P, P, P, S, P, P], I),
+        "mtp_verify_accept_noalloc": ([P, I, I, I, P, I64, P, P, P, P, P, P], I),
         "mtp_tiled_bytes": ([I64, I], S),
         "mtp_pack_tiled": ([P, I64, I, P, I64, P, S, P], I),
         "mtp_draft_argmax_tiled": ([P, I, I, P, P, I64, P, P, P, S, P], I),
@@ -306,6 +308,30 @@ def mtp_verify_accept(hidden, head, draft, B: int, k: int, out_argmax, out_accep
         _ptr(out_tokens, "out_tokens", (torch.int32,)),
         _ptr(ws, "ws", (torch.int64, torch.uint8, torch.int32)), ws.numel() * ws.element_size(),
         _stream(stream), ctypes.byref(cfg)), "mtp_verify_accept")
+
+
+def mtp_verify_accept_noalloc(hidden, head, draft, B: int, k: int, out_argmax, out_accept,
+                              out_tokens, out_logit=None, stream=None) -> None:
+    """mtp_verify_accept without a workspace: the library's static per-device
+    scratch holds the counters (B*(k+1) <= MTP_NOALLOC_MAX_ROWS; calls that
+    overlap on one GPU race, see include/mtp.h). Allocates nothing."""
+    torch = _torch()
+    Mv, H = hidden.shape
+    V, H2 = head.shape
+    if H != H2 or Mv != B * (k + 1):
+        raise ValueError("hidden must be [B*(k+1)][H] with the head's H")
+    if out_argmax.numel() != Mv or out_tokens.numel() != Mv or out_accept.numel() != B:
+        raise ValueError("output sizes do not match B and k")
+    if draft is not None and draft.numel() != B * k:
+        raise ValueError("draft must be [B][k]")
+    _check(lib.mtp_verify_accept_noalloc(
+        _ptr(hidden, "hidden", _bf16_types()), B, k, H, _ptr(head, "head", _bf16_types()), V,
+        _ptr(draft, "draft", (torch.int32,), allow_none=(k == 0)),
+        _ptr(out_argmax, "out_argmax", (torch.int32,)),
+        _ptr(out_logit, "out_logit", (torch.float32,), allow_none=True),
+        _ptr(out_accept, "out_accept", (torch.int32,)),
+        _ptr(out_tokens, "out_tokens", (torch.int32,)), _stream(stream)),
+        "mtp_verify_accept_noalloc")
 
 
 # --- tiled tables -------------------------------------------------------------

@@ -115,6 +115,34 @@ def test_verify_workspace_errors():
     assert _verify(B=64, k=3, ws_bytes=2048) == mtp.MTP_ERR_WORKSPACE
 
 
+def _verify_noalloc(hidden=FAKE, B=1, k=3, H=64, head=FAKE, V=100, draft=FAKE, out_argmax=FAKE,
+                    out_logit=None, out_accept=FAKE, out_tokens=FAKE):
+    return mtp.lib.mtp_verify_accept_noalloc(hidden, B, k, H, head, V, draft, out_argmax,
+                                             out_logit, out_accept, out_tokens, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(hidden=None), dict(head=None), dict(out_argmax=None), dict(out_accept=None),
+    dict(out_tokens=None), dict(B=0), dict(k=-1), dict(k=16), dict(draft=None),
+    dict(B=1025, k=3), dict(V=0), dict(H=20), dict(head=FAKE_ODD), dict(out_tokens=P(0x10001)),
+])
+def test_verify_noalloc_rejects_bad_arguments(kw):
+    """The allocation-free verify checks its arguments as mtp_verify_accept
+    does, before it looks up its scratch or enqueues anything."""
+    assert _verify_noalloc(**kw) == INVALID
+
+
+def test_verify_noalloc_rejects_calls_beyond_its_scratch():
+    """More than MTP_NOALLOC_MAX_ROWS verify rows do not fit the static
+    scratch: MTP_ERR_WORKSPACE, nothing enqueued (no GPU needed)."""
+    assert mtp.MTP_NOALLOC_MAX_ROWS == 1024
+    assert _verify_noalloc(B=257, k=3) == mtp.MTP_ERR_WORKSPACE    # 1,028 rows
+    assert _verify_noalloc(B=65, k=15) == mtp.MTP_ERR_WORKSPACE    # 1,040 rows
+    assert _verify_noalloc(B=1025, k=0) == mtp.MTP_ERR_WORKSPACE
+    header = open(mtp.HEADER).read()
+    assert "#define MTP_NOALLOC_MAX_ROWS 1024" in header
+
+
 def test_pack_and_init_reject_bad_arguments():
     f = mtp.lib.mtp_pack_candidates
     assert f(None, 10, 8, FAKE, 2, FAKE, None) == INVALID
