@@ -123,7 +123,7 @@ def _drafts_and_verify(torch, mtp, wk, W, draft_rows=None, verify_seqs=None, str
           f"{sum(r.near_tie_rows for r in reports)}, near-tie picks differing "
           f"{sum(r.near_tie_diff for r in reports)}, max logit rel err "
           f"{max(r.max_logit_rel for r in reports):.2e}; accepted {acc.tolist()}", flush=True)
-    return g
+    return g, sum(r.rows for r in reports)
 
 
 @pytest.mark.timeout(600)
@@ -215,5 +215,6 @@ def test_mtp4_large_with_exact_ties(torch, mtp, layout):
     assert np.array_equal(chk["exact"], chk["runner_exact"])
     assert list(chk["id"]) == [min(p) for p in pairs[:len(vt.rows)]]
     strict_draft = [(0, int(r)) for r in dt.rows]
-    _drafts_and_verify(torch, mtp, wk, W, strict_draft=strict_draft,
-                       strict_verify=[int(r) for r in vt.rows], layout=layout)
+    _, checked = _drafts_and_verify(torch, mtp, wk, W, strict_draft=strict_draft,
+                                    strict_verify=[int(r) for r in vt.rows], layout=layout)
+    assert checked == wk.draft_calls * wk.Md + wk.Mv == 288
