@@ -86,7 +86,8 @@ mtp_status check_cfg(const mtp_config *cfg) {
 
 // Score M hidden rows against N table rows and finish through `sink`.
 // Path: the vector-ALU kernel while one pass keeps every hidden row's slice in
-// registers (few rows), the matrix-core kernel beyond.
+// registers (few rows), the matrix cores beyond: fed by LDS DMA from the rows
+// when H % 64 == 0, else by the register-staged kernel.
 // Gathered candidates (gather_ids != nullptr: candidate i is head row
 // gather_ids[i]) run on the vector-ALU kernel only.
 mtp_status run_rows(const mtp_bf16 *X, int M, int H, const mtp_bf16 *W, int64_t N,
@@ -123,7 +124,25 @@ mtp_status run_rows(const mtp_bf16 *X, int M, int H, const mtp_bf16 *W, int64_t 
     L.gather_ids = gather_ids;
     L.gather_V = gather_V;
     e = mtp::launch_valu(L, mtp::valu_rows_for(M, ncl), ncl);
+  } else if (mtp::dma_rm_ok(H)) {
+    // matrix cores fed by LDS DMA straight from the row-major rows
+    const int per_cu = (cfg && cfg->blocks_per_cu > 0) ? cfg->blocks_per_cu : 1;
+    mtp::DmaLaunch L;
+    L.X = X;
+    L.WT = W;
+    L.M = M;
+    L.N = N;
+    L.nch = nch;
+    L.S = H / 32;
+    L.max_blocks_x = per_cu * cus;
+    L.sink = sink;
+    L.stream = stream;
+    // rows a multiple of 4 KiB apart: stagger the workgroups over 8 chunk
+    // phases (the arithmetic of every logit is the same either way)
+    L.nphase = ((int64_t)H * 2) % 4096 == 0 ? 8 : 1;
+    e = mtp::launch_dma_rm(L, mtp::dma_nb_for(M));
   } else {
+    // widths that are not a multiple of 64: register-staged matrix-core kernel
     const int per_cu = (cfg && cfg->blocks_per_cu > 0) ? cfg->blocks_per_cu : 2;
     mtp::MfmaLaunch L;
     L.X = X;

@@ -68,6 +68,19 @@ __device__ __forceinline__ void barrier_no_fence() {
   asm volatile("" ::: "memory");
 }
 
+// Piece swizzle of row-major weight chunks in LDS (RW16 16-byte pieces per
+// row, rows stored one after another). An MFMA read has lanes j = 0..15 (and
+// g) on rows 16 b + j at one piece index q; the row's piece q sits at
+// position q ^ rm_swizzle(row). With 8 pieces per row (128-byte rows) the
+// value (j + j / 8) mod 8 puts every 8 consecutive lanes, and every 16, on
+// distinct 16-byte bank groups; with 16 or more pieces j itself does.
+template <int RW16>
+__device__ __forceinline__ int rm_swizzle(int trow) {
+  const int j = trow & 15;
+  if constexpr (RW16 == 8) return (j + (j >> 3)) & 7;
+  else return j & (RW16 - 1);
+}
+
 // s_waitcnt with vmcnt(n) and no wait on the other counters (gfx9 encoding).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -88,12 +101,18 @@ __device__ __forceinline__ void wait_vmcnt() {
 // and `scales` points at its scale groups (256 bytes per 64 rows and four
 // steps); each step's codes are converted with their block's scale into the
 // bf16 operand (exact), so no scale touches the logit.
-template <int NB, int RW, int KS, int NBUF, int WV, int CP, bool FP8 = false, bool FP4 = false>
+template <int NB, int RW, int KS, int NBUF, int WV, int CP, bool FP8 = false, bool FP4 = false,
+          bool RM = false, int PS = 1>
 __global__ void __launch_bounds__(WV * 64)
     gemm_argmax_dma(const uint4 *__restrict__ X, const uint4 *__restrict__ WT, int M, int N,
-                    int nch, int S, RowSink sink, const float *__restrict__ scales) {
+                    int nch, int S, RowSink sink, const float *__restrict__ scales, int nphase) {
   constexpr int RBT = WV * RW;                 // 16-row blocks per workgroup tile
   constexpr int TV = RBT * 16;                 // table rows per workgroup tile
+  // row-major weights: 16-byte pieces per row per chunk, rows per copy
+  constexpr int RW16 = 4 * KS;
+  constexpr int RPC = 64 / RW16;
+  static_assert(!RM || (KS == 2 && !FP8 && !FP4),
+                "row-major chunks: two steps, i.e. whole 128-byte lines of bf16 rows");
   static_assert(!FP8 || KS % 2 == 0, "fp8 chunks hold whole step pairs");
   static_assert(!FP4 || KS % 4 == 0, "fp4 chunks hold whole step groups");
   static_assert(!(FP8 && FP4), "one table format");
@@ -167,6 +186,40 @@ __global__ void __launch_bounds__(WV * 64)
     else return scale3;
   };
 
+  // row-major weights: lane offsets of a copy within its RPC row segments,
+  // one for copies whose rows start at an even multiple of 8 (f even) and
+  // one for odd ones (the swizzle depends on the row modulo 16)
+  const int rowbytes = nch * 16;
+  int rm_voff[2] = {0, 0};
+  if constexpr (RM) {
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+      const int trow = par * RPC + lane / RW16;
+      rm_voff[par] = (lane / RW16) * rowbytes + 16 * ((lane % RW16) ^ rm_swizzle<RW16>(trow));
+    }
+  }
+
+  // Row-major chunk order. With a row pitch that is a multiple of 4 KiB, every
+  // workgroup reading chunk c of its tile at the same moment puts all
+  // concurrent reads on the same low address bits, and the HBM channels they
+  // map to limit the stream (5.0-5.5 TB/s on MI355X against 6.7-7.0 with an
+  // unaligned pitch or with workgroups at different column offsets). With PS
+  // > 1 the columns of a row form PS contiguous segments of nchunks / PS
+  // chunks, and workgroup b starts every tile at segment
+  // p = (b / 8) % PS (so that every XCD holds every phase) and wraps around:
+  // segments p, p + 1, ..., PS - 1, 0, ..., p - 1. Each segment is summed on
+  // its own, its chunks in ascending order from zero; at the end of a tile the
+  // segment sums are put back in segment order and added in one fixed order.
+  // Every logit is thus the same sum of the same segment sums whatever the
+  // workgroup's phase, and duplicated rows still score bit-identically.
+  static_assert(PS == 1 || (RM && (PS == 2 || PS == 4 || PS == 8)), "segments: row-major, 2/4/8");
+  const int seglen = nchunks / PS;
+  int rot = 0;  // the workgroup's phase p
+  if constexpr (PS > 1) rot = (bx >> 3) % PS;
+  const int c0 = rot * seglen;
+  // next chunk to copy: tile and position within the tile's rotated order
+  int rm_iss_t = bx, rm_iss_pos = 0;
+
   // Copy the next chunk (tile iss_t, K chunk iss_c) into a slot, then step
   // the position. Fragment f < AF: weights, step f / RBT of the chunk,
   // 16-row block f % RBT of the tile; f >= AF: hidden fragment for step
@@ -175,17 +228,45 @@ __global__ void __launch_bounds__(WV * 64)
   int iss_t = bx, iss_c = 0;
   auto issue = [&](auto tag) {
     uint4 *base = slot(tag);
-    const int tile = iss_t;
-    const int c = iss_c;
-    if (++iss_c == nchunks) {
-      iss_c = 0;
-      iss_t += gdx;
+    int tile, c;
+    if constexpr (RM) {
+      tile = rm_iss_t;
+      c = rm_iss_pos + c0;
+      c = c < nchunks ? c : c - nchunks;
+      if (++rm_iss_pos == nchunks) {
+        rm_iss_pos = 0;
+        rm_iss_t += gdx;
+      }
+    } else {
+      tile = iss_t;
+      c = iss_c;
+      if (++iss_c == nchunks) {
+        iss_c = 0;
+        iss_t += gdx;
+      }
     }
 #pragma unroll
     for (int q = 0; q < PER_WAVE; ++q) {
       int f = wave + WV * q;
       f = f < FR ? f : FR - 1;
-      if (f < AF) {
+      if (f < AF && RM) {
+        // row-major weights: copy f holds RPC whole row segments of the chunk
+        // (RW16 pieces of 16 bytes each, at least one 128-byte line per row);
+        // the piece at LDS position (row, q) is the row's piece
+        // q ^ rm_swizzle(row), so the MFMA-order reads below hit distinct
+        // banks. A buffer load from a per-copy descriptor (scalar: the copy's
+        // first row and chunk) plus a loop-invariant lane offset keeps no
+        // per-copy address register alive; rows past the table fall outside
+        // the descriptor's range and read zeros (never reported).
+        const int64_t row0 = (int64_t)tile * TV + f * RPC;
+        const int64_t left = ((int64_t)N - row0) * rowbytes;
+        const int nrec = left <= 0 ? 0 : left > 0x7FFFFFFF ? 0x7FFFFFFF : (int)left;
+        __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(reinterpret_cast<const char *>(WT) + row0 * rowbytes + c * (RW16 * 16)),
+            (short)0, nrec, 0x00020000);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, MTP_LDS(base + f * kWave), 16,
+                                                 rm_voff[f & 1], 0, 0, CP);
+      } else if (f < AF) {
         const int s = f / RBT;  // step (bf16), step pair (fp8) or step group (fp4) of the chunk
         int rb = tile * RBT + f % RBT;
         rb = rb < nrb ? rb : nrb - 1;          // past the table: valid, never reported
@@ -250,6 +331,11 @@ __global__ void __launch_bounds__(WV * 64)
     if (2 < total) issue(std::integral_constant<int, 2>{});
   }
   int cur_t = bx, cur_c = 0;  // position of the chunk being multiplied
+  // row-major: position of the chunk being multiplied within its tile's
+  // rotated order, and the sums of the tile's finished segments, newest first
+  int rm_pos = 0;
+  constexpr int SPS = PS > 1 ? PS : 1, SRW = PS > 1 ? RW : 1, SNB = PS > 1 ? NB : 1;
+  f32x4_dma_t seg[SPS][SRW][SNB];
 
   auto body = [&](auto tag, int it) {
     constexpr int SL = decltype(tag)::value;
@@ -297,6 +383,10 @@ __global__ void __launch_bounds__(WV * 64)
               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w0, 1.0f, true)),
               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w1, 1.0f, false)),
               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w1, 1.0f, true)));
+        } else if constexpr (RM) {
+          // row j of 16-row block blk, piece 4s + g of the chunk
+          const int trow = (wave * RW + rw) * 16 + j;
+          a[rw] = A[trow * RW16 + ((4 * s + g) ^ rm_swizzle<RW16>(trow))];
         } else {
           a[rw] = A[(s * RBT + wave * RW + rw) * kWave + lane];
         }
@@ -308,10 +398,67 @@ __global__ void __launch_bounds__(WV * 64)
         for (int rw = 0; rw < RW; ++rw) acc[rw][nb] = mfma16_dma(a[rw], b, acc[rw][nb]);
       }
     }
-    if (++cur_c == nchunks) {
-      const int tile = cur_t;
-      cur_c = 0;
-      cur_t += gdx;
+    bool tile_done;
+    int tile;
+    if constexpr (RM) {
+      tile = cur_t;
+      ++rm_pos;
+      if constexpr (PS > 1) {
+        if (rm_pos % seglen == 0) {
+          // segment done: shift it into the finished sums, start the next
+#pragma unroll
+          for (int rw = 0; rw < RW; ++rw)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+              for (int q = PS - 1; q > 0; --q) seg[q][rw][nb] = seg[q - 1][rw][nb];
+              seg[0][rw][nb] = acc[rw][nb];
+              acc[rw][nb] = f32x4_dma_t{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+      }
+      tile_done = rm_pos == nchunks;
+      if (tile_done) {
+        rm_pos = 0;
+        cur_t += gdx;
+        if constexpr (PS > 1) {
+          // seg[PS - 1 - q] holds the segment finished q-th, i.e. segment
+          // (q + rot) % PS: reverse, then rotate right by rot, which leaves
+          // segment s at index s; then add them in a fixed pairwise order
+#pragma unroll
+          for (int rw = 0; rw < RW; ++rw)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+              f32x4_dma_t r[PS];
+#pragma unroll
+              for (int q = 0; q < PS; ++q) r[q] = seg[PS - 1 - q][rw][nb];
+#pragma unroll
+              for (int bit = 1; bit < PS; bit <<= 1) {
+                if (rot & bit) {
+                  f32x4_dma_t t2[PS];
+#pragma unroll
+                  for (int q = 0; q < PS; ++q) t2[q] = r[(q - bit + PS) % PS];
+#pragma unroll
+                  for (int q = 0; q < PS; ++q) r[q] = t2[q];
+                }
+              }
+#pragma unroll
+              for (int w = 1; w < PS; w <<= 1)
+#pragma unroll
+                for (int q = 0; q < PS; q += 2 * w) r[q] = r[q] + r[q + w];
+              acc[rw][nb] = r[0];
+            }
+        }
+      }
+    } else {
+      tile = cur_t;
+      tile_done = ++cur_c == nchunks;
+      if (tile_done) {
+        cur_c = 0;
+        cur_t += gdx;
+      }
+    }
+    if (tile_done) {
       const int vbase = tile * TV + wave * RW * 16 + 4 * g;
 #pragma unroll
       for (int rw = 0; rw < RW; ++rw) {
@@ -622,15 +769,16 @@ __global__ void __launch_bounds__(WV * 64)
 int64_t tiled_rows(int64_t rows) { return (rows + 63) / 64 * 64; }
 int tiled_cols(int H) { return (H + 127) / 128 * 128; }
 
-template <int NB, int RW, int KS, int NBUF, int WV, int CP, bool FP8 = false, bool FP4 = false>
+template <int NB, int RW, int KS, int NBUF, int WV, int CP, bool FP8 = false, bool FP4 = false,
+          bool RM = false, int PS = 1>
 static hipError_t launch_dma_cfg(const DmaLaunch &L) {
   constexpr int TV = WV * RW * 16;
   const int64_t ntiles = (L.N + TV - 1) / TV;
   const int gx = (int)(ntiles < L.max_blocks_x ? ntiles : L.max_blocks_x);
   const int gy = (L.M + NB * 16 - 1) / (NB * 16);
-  hipLaunchKernelGGL((gemm_argmax_dma<NB, RW, KS, NBUF, WV, CP, FP8, FP4>), dim3(gx, gy),
+  hipLaunchKernelGGL((gemm_argmax_dma<NB, RW, KS, NBUF, WV, CP, FP8, FP4, RM, PS>), dim3(gx, gy),
                      dim3(WV * 64), 0, L.stream, (const uint4 *)L.X, (const uint4 *)L.WT, L.M,
-                     (int)L.N, L.nch, L.S, L.sink, L.scales);
+                     (int)L.N, L.nch, L.S, L.sink, L.scales, L.nphase);
   return hipGetLastError();
 }
 
@@ -687,6 +835,38 @@ hipError_t launch_dma(const DmaLaunch &L, int nb) {
     case 6: return launch_dma_cfg<6, 4, 1, 3, 8, NT>(L);
     case 8: return launch_dma_cfg<8, 4, 1, 3, 8, NT>(L);
     case 10: return launch_dma_cfg<10, 4, 1, 3, 8, NT>(L);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// Row-major tables and heads (H % 64 == 0): the same kernel with each weight
+// copy holding 8 whole 128-byte row segments (two 32-column steps per chunk).
+// A row-major copy of 16 rows x 64 bytes, the MFMA operand's own shape, streams
+// at half the rate on MI355X (3.8 against 7.1 TB/s for copy-only loops over
+// 248,320 x 5,120), so every shape takes two-step chunks; 96 to 160 hidden rows
+// use 256-row tiles to fit their two-step chunks in three LDS slots.
+bool dma_rm_ok(int H) { return H % 64 == 0; }
+
+// PSMAX: column segments (workgroup phases) this pass takes on rows a multiple
+// of 4 KiB apart; the segment sums cost RW * NB * 4 registers each.
+template <int NB, int RW, int NBUF, int PSMAX>
+static hipError_t launch_rm(const DmaLaunch &L) {
+  constexpr int NT = 2;
+  if constexpr (PSMAX > 1) {
+    if (L.nphase > 1) return launch_dma_cfg<NB, RW, 2, NBUF, 8, NT, false, false, true, PSMAX>(L);
+  }
+  return launch_dma_cfg<NB, RW, 2, NBUF, 8, NT, false, false, true, 1>(L);
+}
+
+hipError_t launch_dma_rm(const DmaLaunch &L, int nb) {
+  switch (nb) {
+    case 1: return launch_rm<1, 1, 3, 8>(L);
+    case 2: return launch_rm<2, 2, 4, 4>(L);
+    case 3: return launch_rm<3, 2, 3, 4>(L);
+    case 4: return launch_rm<4, 2, 3, 2>(L);
+    case 6: return launch_rm<6, 2, 3, 2>(L);
+    case 8: return launch_rm<8, 2, 3, 1>(L);
+    case 10: return launch_rm<10, 2, 3, 1>(L);
     default: return hipErrorInvalidValue;
   }
 }

@@ -49,16 +49,17 @@ hipError_t launch_mfma(const MfmaLaunch &L, int nb);
 
 struct DmaLaunch {
   const void *X;     // hidden [M][H] bf16, row-major
-  const void *WT;    // table in the 64-row tiled layout
+  const void *WT;    // table in the 64-row tiled layout (row-major for launch_dma_rm)
   int M;
   int64_t N;         // table rows (before padding)
   int nch;           // H / 8
-  int S;             // 32-column steps per padded row (tiled_cols(H) / 32)
+  int S;             // 32-column steps per padded row (tiled_cols(H) / 32; H / 32 row-major)
   int max_blocks_x;
   RowSink sink;
   hipStream_t stream;
   const float *scales = nullptr;  // fp8 tables: row scales [N]
   void *stage = nullptr;          // wide passes: packed hidden block (ring_stage_bytes)
+  int nphase = 1;                 // row-major: workgroup chunk phases (1: none)
 };
 
 int64_t tiled_rows(int64_t rows);
@@ -66,6 +67,9 @@ int tiled_cols(int H);
 int dma_nb_for(int M);
 hipError_t launch_dma(const DmaLaunch &L, int nb);
 size_t ring_stage_bytes(int M, int H);
+// Row-major tables and heads through the same kernel (H % 64 == 0).
+bool dma_rm_ok(int H);
+hipError_t launch_dma_rm(const DmaLaunch &L, int nb);
 int dma_nb_for_fp8(int M);
 hipError_t launch_dma_fp8(const DmaLaunch &L, int nb);
 int dma_nb_for_fp4(int M);

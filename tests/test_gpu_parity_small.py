@@ -52,7 +52,8 @@ EXACT_SHAPES = [  # (M, N, H)
     (1, 1, 8), (1, 1000, 8), (3, 4097, 256), (1, 70001, 2048), (4, 12345, 2560),
     (8, 3001, 4096), (2, 999, 5120), (1, 257, 16384), (9, 2000, 512), (32, 5000, 1024),
     (5, 777, 3000), (1, 65, 24), (16, 1025, 640), (17, 333, 1032), (48, 2049, 4096),
-    (160, 1111, 5120), (161, 300, 256), (64, 4000, 2048),
+    (160, 1111, 5120), (161, 300, 256), (64, 4000, 2048), (90, 3333, 1024),
+    (120, 2500, 2048), (33, 257, 64),
     (4096, 3001, 256),  # the most hidden rows one call takes (MTP_MAX_ROWS)
 ]
 
@@ -115,7 +116,8 @@ def test_verify_special_drafts(torch, mtp):
     assert np.array_equal(g["tokens"][:, 0], t[:, 0]) and np.all(g["tokens"][:, 1:] == -1)
 
 
-@pytest.mark.parametrize("path,M", [("auto", 3), ("mfma", 3), ("mfma", 40)])
+@pytest.mark.parametrize("path,M", [("auto", 3), ("mfma", 3), ("mfma", 20), ("mfma", 40), ("mfma", 60),
+                                    ("mfma", 90)])
 def test_duplicate_rows_tie_to_lowest_id(torch, mtp, path, M):
     """Random N(0,0.02) head with the winner's row copied below and above it:
     the copies score bit-identically on the GPU and the lowest id wins."""
@@ -123,13 +125,21 @@ def test_duplicate_rows_tie_to_lowest_id(torch, mtp, path, M):
     W = wl.head_weights(V, H, 42)
     h = wl.hidden_states(M, H, 42)
     win = oracle.argmax(h, W)["id"]
+    used = {int(x) for x in win}   # never overwrite a row's winner or a partner
+
+    def free(j, step):
+        while j in used:
+            j = (j + step) % V
+        return j
+
     for m in range(M):
         j1 = int(win[m])
-        lo = (j1 * 7919 + 13) % max(j1, 1) if j1 > 0 else None
-        hi = j1 + 1 + (j1 * 104729) % (V - j1 - 1) if j1 < V - 1 else None
+        lo = free((j1 * 7919 + 13) % max(j1, 1), -1) if j1 > 0 else None
+        hi = free(j1 + 1 + (j1 * 104729) % (V - j1 - 1), 1) if j1 < V - 1 else None
         for j2 in (lo, hi):
             if j2 is not None and j2 != j1:
                 W[j2] = W[j1]
+                used.add(j2)
     orc = oracle.argmax(h, W)
     for m in range(M):
         assert orc["runner_exact"][m] == orc["exact"][m]      # the tie holds
@@ -141,7 +151,8 @@ def test_duplicate_rows_tie_to_lowest_id(torch, mtp, path, M):
         assert list(g["argmax"].ravel()[:3]) == list(orc["id"])
 
 
-@pytest.mark.parametrize("path,M", [("auto", 4), ("mfma", 4), ("mfma", 33)])
+@pytest.mark.parametrize("path,M", [("auto", 4), ("mfma", 4), ("mfma", 20), ("mfma", 33),
+                                    ("mfma", 60)])
 def test_determinism_across_launch_shapes(torch, mtp, path, M):
     """Bit-identical outputs for repeated calls and any grid size."""
     V, H = 50000, 2048
