@@ -13,10 +13,11 @@ Inputs are seeded synthetic data (N(0,0.02) bf16 head, N(0,1) bf16 hidden
 states, seeded sorted candidate subset), resident in HBM before timing. The
 draft calls of one step read three different copies of the candidate table, so
 no call is served from the 256 MB Infinity Cache by its predecessor; the
-verify head (>= 1 GB) cannot stay cached between steps. Kernel durations come
-from HIP events recorded on the launch stream around the draft block and the
-verify launch of the timed steps (every step when fewer than 50 are timed, else
-every fifth; --event-every), after a warm-up of at least --warmup-seconds.
+verify head (>= 1 GB) cannot stay cached between steps. Per-call durations
+come from one HIP event per call of every timed step, stamped by the library
+with the end of the call's last kernel on the launch stream
+(mtp_time_next_call): a call's time is the span from the previous call's end to
+its own end. A warm-up of at least --warmup-seconds precedes the timed steps.
 Prints one JSON line.
 
 --workload draft_ablation adds context.draft_tables: the M = 1 draft timed over
@@ -49,7 +50,27 @@ KERNEL_SOURCES = {
     "valu": ("common.hpp", "gemv_valu.hip"),
     "mfma": ("common.hpp", "gemm_mfma.hip"),
     "dma": ("common.hpp", "gemm_dma.hip"),
+    "fp8": ("common.hpp", "fp8.hip"),
+    "fp4": ("common.hpp", "fp4.hip"),
+    "pack": ("pack.hip",),
+    "probe": ("probe.hip",),
 }
+
+
+def rows_path(M: int, H: int) -> str:
+    """Kernel family a row-major bf16 call of M hidden rows at width H runs on
+    (the selection rule of the C ABI): the vector-ALU kernel while one pass
+    keeps every hidden row's slice in registers (16-byte chunks per lane
+    rounded up to an instantiated count, at most 32 chunk slices), the LDS-DMA
+    matrix-core kernel for H % 64 == 0, else the register-staged one."""
+    need = -(-(H // 8) // 64)
+    ncl = next((n for n in (1, 2, 3, 4, 5, 6, 8, 10, 12, 16, 20, 24, 32) if n >= need), 0)
+    mr = 1
+    while ncl and mr < 8 and mr < M and 2 * mr * ncl <= 32:
+        mr *= 2
+    if ncl and mr >= M:
+        return "valu"
+    return "dma" if H % 64 == 0 else "mfma"
 
 
 def parse_args():
@@ -77,9 +98,6 @@ def parse_args():
     ap.add_argument("--graph", action="store_true",
                     help="time the steps as replays of a captured HIP graph (mtp_graph_*); "
                          "per-call durations still come from event-bracketed eager launches")
-    ap.add_argument("--event-every", type=int, default=None,
-                    help="record the per-call HIP events on every n-th timed step (default: "
-                         "every step when fewer than 50 steps are timed, else every 5th)")
     ap.add_argument("--warmup-seconds", type=float, default=1.0,
                     help="after the --warmup steps, keep running untimed steps until the warm-up "
                          "has lasted this long, so that the timed steps start with the GPU's "
@@ -101,11 +119,11 @@ def kernel_source_hash(path: str) -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel: str, workload: str, path: str):
+def measured_traffic(kernel: str, profile: str, path: str):
     """HBM bytes per launch of the verify or draft call, from the committed
-    rocprofv3 counter summary of the workload, if it was taken from the
-    current sources."""
-    p = os.path.join(ROOT, "profiles", f"verify_{workload}_pmc.txt")
+    rocprofv3 counter summary of the workload (profiles/verify_<profile>_pmc.txt),
+    if it was taken from the current sources."""
+    p = os.path.join(ROOT, "profiles", f"verify_{profile}_pmc.txt")
     if not os.path.exists(p):
         return None
     text = open(p).read()
@@ -286,19 +304,17 @@ def main() -> int:
 
     n_tab = len(tables)
 
-    def step(i: int, ev=None, record_start: bool = True):
-        # ev: (before drafts, after drafts = before verify, after verify);
-        # record_start False: ev[0] is the previous step's end event, already
-        # recorded
-        if ev is not None and record_start:
-            ev[0].record(stream)
+    def step(i: int, ev=None):
+        # ev: one event per call, the draft calls' then the verify's, which the
+        # library stamps with the end of the call's last kernel
+        # (mtp_time_next_call with a stop event only)
         for c in range(wk.draft_calls):
+            if ev is not None:
+                mtp.mtp_time_next_call(None, ev[c])
             draft_call(c, tables[(i * wk.draft_calls + c) % n_tab])
         if ev is not None:
-            ev[1].record(stream)
+            mtp.mtp_time_next_call(None, ev[-1])
         verify_call(drafts_d)
-        if ev is not None:
-            ev[2].record(stream)
 
     # Warm-up: the --warmup steps, then more untimed steps until the warm-up
     # has lasted --warmup-seconds. A short timed region started right after
@@ -332,52 +348,58 @@ def main() -> int:
             graphs[i % n_tab].launch()
         torch.cuda.synchronize()
 
-    # Per-call events: each recorded event costs the stream a few
-    # microseconds, which on every step slows the whole job by about 4%, so
-    # long runs record them on every 5th step; short runs record them on every
-    # step, so that the per-call figures rest on enough samples.
-    every = max(1, args.event_every) if args.event_every is not None else (1 if K < 50 else 5)
+    # Per-call timing: the library launches each call's last kernel with a stop
+    # event (hipExtLaunchKernel), which takes that dispatch's own end time; a
+    # call's time is the span from the previous call's end to its own end (its
+    # kernels plus the bubble before them). Stop stamps cost the stream about
+    # 0.6 us per call, against about 5 us for a start stamp or 7 us for a
+    # marker event, so every timed step carries them.
+    every = 1
 
     def timed_steps(with_events: bool, use_graph: bool):
-        # with events on every step, consecutive steps share their boundary
-        # event (the end of step i is the start of step i + 1), so each step
-        # records two events instead of three
-        chained = with_events and every == 1
-        if chained:
-            bounds = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
-            mids = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-            evs = {i: (bounds[i], mids[i], bounds[i + 1]) for i in range(K)}
+        E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+        if use_graph:
+            # graph replays: one event pair around each replay
+            evs = {i: (E(), E()) for i in range(0, K, every)} if with_events else {}
         else:
-            evs = {i: tuple(torch.cuda.Event(enable_timing=True) for _ in range(3))
-                   for i in range(0, K, every)} if with_events else {}
+            steps_ev = list(range(K)) if with_events else []
+            pool = iter(mtp.timing_events((wk.draft_calls + 1) * len(steps_ev), stream))
+            evs = {i: [next(pool) for _ in range(wk.draft_calls + 1)] for i in steps_ev}
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(K):
             ev = evs.get(i)
-            first = not chained or i == 0
             if use_graph:
-                if ev and first:
+                if ev:
                     ev[0].record(stream)
                 graphs[i % n_tab].launch()
                 if ev:
-                    ev[2].record(stream)
+                    ev[1].record(stream)
             else:
-                step(i, ev, record_start=first)
+                step(i, ev)
         torch.cuda.synchronize()
         return time.perf_counter() - t0, list(evs.values())
 
     t_total, evs = timed_steps(True, bool(graphs))
     graph_step_ms = None
     if graphs:
-        graph_step_ms = [e[0].elapsed_time(e[2]) for e in evs]
-        # per-call durations: the same kernels launched eagerly, each block
-        # bracketed by events
+        graph_step_ms = [e[0].elapsed_time(e[1]) for e in evs]
+        # per-call durations: the same calls launched eagerly, each timed by
+        # its own event pair
         _, evs = timed_steps(True, False)
 
-    # per-call durations: the draft block's span over its calls (inter-kernel
-    # gaps included), the verify launch's own span
-    draft_ms = [e[0].elapsed_time(e[1]) / wk.draft_calls for e in evs]
-    verify_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    # per-call durations: from the previous call's end to the call's end (the
+    # very first call of the timed steps has no previous stamp); the draft
+    # figure of a step is the mean of its draft calls
+    stops = [ev for e in evs for ev in e]
+    span = [None] + [mtp.elapsed_ms(stops[j - 1], stops[j]) for j in range(1, len(stops))]
+    n_call = wk.draft_calls + 1
+    draft_ms, verify_ms = [], []
+    for i in range(len(evs)):
+        d = [span[i * n_call + c] for c in range(wk.draft_calls) if span[i * n_call + c] is not None]
+        if d:
+            draft_ms.append(statistics.mean(d))
+        verify_ms.append(span[i * n_call + wk.draft_calls])
 
     # Untimed context: the same steps without per-launch events, and the
     # draft call re-reading one table (Infinity Cache may serve part of it).
@@ -521,12 +543,18 @@ def main() -> int:
     # row-major calls with few rows run on the vector-ALU kernel; tiled ones
     # on the DMA-fed matrix-core kernel
     dom_rows = wk.Mv if dom_name == "verify" else wk.Md
-    path = "dma" if layout == "tiled" else ("valu" if dom_rows <= 8 else "mfma")
-    traffic = measured_traffic(dom_name, wk.name, path)
+    path = "dma" if layout == "tiled" else rows_path(dom_rows, wk.H)
+    # counter summaries: one per workload in its default layout, plus the
+    # row-major runs of the batched workloads
+    default_layout = "rows" if max(wk.Md, wk.Mv) <= 8 else "tiled"
+    profile = wk.name if layout == default_layout else f"{wk.name}_{layout}"
+    traffic = measured_traffic(dom_name, profile, path) if args.table == "bf16" and \
+        args.draft_source == "table" else None
     achieved = dom_bytes / dom_us / 1e3
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                "traffic": traffic, "kernel": dom_name,
+                "traffic": traffic, "kernel": dom_name, "kernel_family": path,
+                "kernel_source_hash": kernel_source_hash(path),
                 "algorithmic_bytes_per_launch": int(dom_bytes)}
 
     dom_stream = stream_read["head_GBps"] if dom_name == "verify" else \
@@ -560,7 +588,9 @@ def main() -> int:
         "calls": {"draft": draft_stats, "verify": verify_stats},
         "context": {
             "ms_per_step_without_kernel_events": round(t_noev * 1000.0 / K, 4),
-            "kernel_event_steps": f"1 in {every} timed steps ({len(evs)} of {K})",
+            "kernel_event_steps": f"every timed step ({len(evs)} of {K}); one stop event per "
+                                  "call, stamped with the end of the call's last kernel; a call's "
+                                  "time runs from the previous call's end to its own",
             "warmup_steps_run": n_warm,
             "warmup_s": round(warmup_s, 3),
             "step_mode": "hip_graph" if graphs else "eager",

@@ -89,6 +89,19 @@ typedef struct {
 /* Human-readable name of a status code (static storage). */
 const char *mtp_status_string(mtp_status status);
 
+/*
+ * Measurement aid, not a step of the method: time the next draft or verify
+ * call made by this thread. Its first kernel is launched with `start` and its
+ * last with `stop` (hipExtLaunchKernel), so hipEventElapsedTime(start, stop)
+ * gives the call's time on the GPU from the first dispatch's start to the last
+ * one's end, with no marker packets between the calls of a stream. Either
+ * event may be NULL. The request stays pending until a call launches (calls
+ * that fail their argument checks launch nothing) and applies to one call.
+ * Events must be created with timing enabled on the call's device; not for
+ * use inside a graph capture.
+ */
+void mtp_time_next_call(hipEvent_t start, hipEvent_t stop);
+
 /* hipError_t of the calling thread's last MTP_ERR_HIP (0 if none). */
 int mtp_last_hip_error(void);
 

@@ -15,6 +15,7 @@
 namespace {
 
 thread_local int g_last_hip_error = 0;
+thread_local mtp::CallTiming g_call_timing;
 
 mtp_status hip_fail(hipError_t e) {
   g_last_hip_error = (int)e;
@@ -313,6 +314,8 @@ static_assert(kScratchBytes == 8448, "the size mtp.h states for the scratch arra
 
 }  // namespace
 
+mtp::CallTiming &mtp::call_timing() { return g_call_timing; }
+
 extern "C" {
 
 const char *mtp_status_string(mtp_status status) {
@@ -328,6 +331,11 @@ const char *mtp_status_string(mtp_status status) {
 }
 
 int mtp_last_hip_error(void) { return g_last_hip_error; }
+
+void mtp_time_next_call(hipEvent_t start, hipEvent_t stop) {
+  g_call_timing.start = start;
+  g_call_timing.stop = stop;
+}
 
 int mtp_version(void) { return 100; }
 

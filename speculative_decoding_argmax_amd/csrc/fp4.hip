@@ -400,12 +400,12 @@ static hipError_t launch_fp4_shape(const Fp4Launch &L) {
   const int32_t *gids = GATHER ? L.gather_ids : nullptr;
   const int64_t gV = GATHER ? L.gather_V : 0;
   if (L.nblk == NCL * kWave)
-    hipLaunchKernelGGL((gemv_argmax_mxfp4<MR, NCL, RB, true, GATHER>), grid, block, 0, L.stream,
-                       X, Q, L.scales, L.M, L.N, L.nblk, gids, gV, L.sink);
-  else
-    hipLaunchKernelGGL((gemv_argmax_mxfp4<MR, NCL, RB, false, GATHER>), grid, block, 0, L.stream,
-                       X, Q, L.scales, L.M, L.N, L.nblk, gids, gV, L.sink);
-  return hipGetLastError();
+    return launch_call_kernel((gemv_argmax_mxfp4<MR, NCL, RB, true, GATHER>), grid, block,
+                              L.stream, true, true, X, Q, L.scales, L.M, L.N, L.nblk, gids, gV,
+                              L.sink);
+  return launch_call_kernel((gemv_argmax_mxfp4<MR, NCL, RB, false, GATHER>), grid, block,
+                            L.stream, true, true, X, Q, L.scales, L.M, L.N, L.nblk, gids, gV,
+                            L.sink);
 }
 
 template <int MR, int NCL>

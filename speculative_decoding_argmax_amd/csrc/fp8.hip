@@ -435,12 +435,11 @@ static hipError_t launch_fp8_shape(const Fp8Launch &L) {
   const int32_t *gids = GATHER ? L.gather_ids : nullptr;
   const int64_t gV = GATHER ? L.gather_V : 0;
   if (L.ncq == NCL * kWave)
-    hipLaunchKernelGGL((gemv_argmax_fp8<MR, NCL, RB, true, GATHER>), grid, block, 0, L.stream, X,
-                       Q, L.scales, L.M, L.N, L.ncq, gids, gV, L.sink);
-  else
-    hipLaunchKernelGGL((gemv_argmax_fp8<MR, NCL, RB, false, GATHER>), grid, block, 0, L.stream, X,
-                       Q, L.scales, L.M, L.N, L.ncq, gids, gV, L.sink);
-  return hipGetLastError();
+    return launch_call_kernel((gemv_argmax_fp8<MR, NCL, RB, true, GATHER>), grid, block,
+                              L.stream, true, true, X, Q, L.scales, L.M, L.N, L.ncq, gids, gV,
+                              L.sink);
+  return launch_call_kernel((gemv_argmax_fp8<MR, NCL, RB, false, GATHER>), grid, block, L.stream,
+                            true, true, X, Q, L.scales, L.M, L.N, L.ncq, gids, gV, L.sink);
 }
 
 template <int MR, int NCL>

@@ -776,10 +776,10 @@ static hipError_t launch_dma_cfg(const DmaLaunch &L) {
   const int64_t ntiles = (L.N + TV - 1) / TV;
   const int gx = (int)(ntiles < L.max_blocks_x ? ntiles : L.max_blocks_x);
   const int gy = (L.M + NB * 16 - 1) / (NB * 16);
-  hipLaunchKernelGGL((gemm_argmax_dma<NB, RW, KS, NBUF, WV, CP, FP8, FP4, RM, PS>), dim3(gx, gy),
-                     dim3(WV * 64), 0, L.stream, (const uint4 *)L.X, (const uint4 *)L.WT, L.M,
-                     (int)L.N, L.nch, L.S, L.sink, L.scales, L.nphase);
-  return hipGetLastError();
+  return launch_call_kernel((gemm_argmax_dma<NB, RW, KS, NBUF, WV, CP, FP8, FP4, RM, PS>),
+                            dim3(gx, gy), dim3(WV * 64), L.stream, true, true,
+                            (const uint4 *)L.X, (const uint4 *)L.WT, L.M, (int)L.N, L.nch, L.S,
+                            L.sink, L.scales, L.nphase);
 }
 
 // Hidden-row blocks per pass: M rounds up to an instantiated count (at most
@@ -805,14 +805,13 @@ static hipError_t launch_ring_cfg(const DmaLaunch &L) {
   const int nbt = gy * NB;
   const int64_t elems = (int64_t)L.S * nbt * kWave;
   const int pblocks = (int)(elems / 256 + 1 < 1024 ? elems / 256 + 1 : 1024);
-  hipLaunchKernelGGL(pack_hidden_frags, dim3(pblocks), dim3(256), 0, L.stream,
-                     (const uint4 *)L.X, L.M, L.nch, L.S, nbt, (uint4 *)L.stage);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launch_call_kernel(pack_hidden_frags, dim3(pblocks), dim3(256), L.stream, true,
+                                    false, (const uint4 *)L.X, L.M, L.nch, L.S, nbt,
+                                    (uint4 *)L.stage);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((gemm_argmax_ring<NB, RW, KS, D, WV, CP>), dim3(gx, gy), dim3(WV * 64), 0,
-                     L.stream, (const uint4 *)L.stage, (const uint4 *)L.WT, L.M, (int)L.N, L.S,
-                     nbt, L.sink);
-  return hipGetLastError();
+  return launch_call_kernel((gemm_argmax_ring<NB, RW, KS, D, WV, CP>), dim3(gx, gy),
+                            dim3(WV * 64), L.stream, false, true, (const uint4 *)L.stage,
+                            (const uint4 *)L.WT, L.M, (int)L.N, L.S, nbt, L.sink);
 }
 
 // Staging bytes of the wide passes (the packed hidden block), 0 for M <= 128.

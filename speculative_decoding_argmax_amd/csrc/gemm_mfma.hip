@@ -263,10 +263,9 @@ static hipError_t launch_nb(const MfmaLaunch &L) {
   const int64_t ntiles = (L.N + TILE - 1) / TILE;
   const int gx = (int)(ntiles < L.max_blocks_x ? ntiles : L.max_blocks_x);
   const int gy = (L.M + NB * 16 - 1) / (NB * 16);
-  hipLaunchKernelGGL((gemm_argmax_mfma<NB, RW, KS, PFD>), dim3(gx, gy), dim3(kMfmaThreads), 0,
-                     L.stream, (const uint4 *)L.X, (const uint4 *)L.W, L.M, (int)L.N, L.nch,
-                     L.sink);
-  return hipGetLastError();
+  return launch_call_kernel((gemm_argmax_mfma<NB, RW, KS, PFD>), dim3(gx, gy),
+                            dim3(kMfmaThreads), L.stream, true, true, (const uint4 *)L.X,
+                            (const uint4 *)L.W, L.M, (int)L.N, L.nch, L.sink);
 }
 
 // Instantiated shapes (measured on MI355X; none spills registers).

@@ -225,25 +225,26 @@ static hipError_t launch_variant(const ValuLaunch &L) {
   const int gy = (L.M + MR - 1) / MR;
   const RowSource src{L.gather_ids, L.gather_V};
   const bool exact = L.nch == NCL * kWave;
+  hipError_t e;
   if (L.gather_ids) {
     if (exact)
-      hipLaunchKernelGGL((gemv_argmax_valu<MR, NCL, RB, PF, true, true>), dim3(gx, gy),
-                         dim3(kValuThreads), 0, L.stream, (const uint4 *)L.X, (const uint4 *)L.W,
+      e = launch_call_kernel((gemv_argmax_valu<MR, NCL, RB, PF, true, true>), dim3(gx, gy),
+                             dim3(kValuThreads), L.stream, true, true, (const uint4 *)L.X, (const uint4 *)L.W,
                          L.M, L.N, L.nch, src, L.sink);
     else
-      hipLaunchKernelGGL((gemv_argmax_valu<MR, NCL, RB, PF, false, true>), dim3(gx, gy),
-                         dim3(kValuThreads), 0, L.stream, (const uint4 *)L.X, (const uint4 *)L.W,
+      e = launch_call_kernel((gemv_argmax_valu<MR, NCL, RB, PF, false, true>), dim3(gx, gy),
+                             dim3(kValuThreads), L.stream, true, true, (const uint4 *)L.X, (const uint4 *)L.W,
                          L.M, L.N, L.nch, src, L.sink);
   } else if (exact) {
-    hipLaunchKernelGGL((gemv_argmax_valu<MR, NCL, RB, PF, true, false>), dim3(gx, gy),
-                       dim3(kValuThreads), 0, L.stream, (const uint4 *)L.X, (const uint4 *)L.W,
+    e = launch_call_kernel((gemv_argmax_valu<MR, NCL, RB, PF, true, false>), dim3(gx, gy),
+                           dim3(kValuThreads), L.stream, true, true, (const uint4 *)L.X, (const uint4 *)L.W,
                        L.M, L.N, L.nch, src, L.sink);
   } else {
-    hipLaunchKernelGGL((gemv_argmax_valu<MR, NCL, RB, PF, false, false>), dim3(gx, gy),
-                       dim3(kValuThreads), 0, L.stream, (const uint4 *)L.X, (const uint4 *)L.W,
+    e = launch_call_kernel((gemv_argmax_valu<MR, NCL, RB, PF, false, false>), dim3(gx, gy),
+                           dim3(kValuThreads), L.stream, true, true, (const uint4 *)L.X, (const uint4 *)L.W,
                        L.M, L.N, L.nch, src, L.sink);
   }
-  return hipGetLastError();
+  return e;
 }
 
 template <int MR, int NCL>

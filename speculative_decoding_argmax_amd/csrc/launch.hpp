@@ -1,12 +1,40 @@
 // Internal launchers of the HIP kernels (host side). Not part of the C ABI.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "common.hpp"
 
 namespace mtp {
+
+// Timing of one call (a measurement aid, mtp_time_next_call): when set, the
+// next draft or verify call of this thread launches its first kernel with
+// `start` and its last with `stop` through hipExtLaunchKernel, which stamps
+// the events with the dispatches' own start and end times (no marker packets
+// in the stream). The request is cleared by the launch that takes `stop`.
+struct CallTiming {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+CallTiming &call_timing();
+
+// Launch a draft / verify kernel; `first` / `last`: the call's first / last
+// kernel (for the timing request above).
+template <typename K, typename... Args>
+hipError_t launch_call_kernel(K kernel, dim3 grid, dim3 block, hipStream_t stream, bool first,
+                              bool last, Args... args) {
+  CallTiming &t = call_timing();
+  if (t.start || t.stop) {
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, first ? t.start : nullptr,
+                          last ? t.stop : nullptr, 0, args...);
+    if (last) t = CallTiming{};
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, 0, stream, args...);
+  }
+  return hipGetLastError();
+}
 
 struct ValuLaunch {
   const void *X;     // hidden [M][H] bf16

@@ -70,6 +70,7 @@ def _load() -> ctypes.CDLL:
     sig = {
         "mtp_status_string": ([I], ctypes.c_char_p),
         "mtp_last_hip_error": ([], I),
+        "mtp_time_next_call": ([P, P], None),
         "mtp_version": ([], I),
         "mtp_validate_ids": ([P, I64, I64], I),
         "mtp_draft_workspace_bytes": ([I, I64, I], S),
@@ -123,6 +124,10 @@ def _load() -> ctypes.CDLL:
         f = getattr(lib, name)
         f.argtypes = args
         f.restype = res
+    # the HIP runtime the library is bound to (torch's): event timing of the
+    # calls timed with mtp_time_next_call, whose events torch did not record
+    lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), P, P]
+    lib.hipEventElapsedTime.restype = I
     return lib
 
 
@@ -141,6 +146,45 @@ def status_string(status: int) -> str:
 
 def last_hip_error() -> int:
     return int(lib.mtp_last_hip_error())
+
+
+def timing_events(n: int, stream=None):
+    """n torch.cuda.Event(enable_timing=True) events backed by HIP events
+    (torch creates the HIP event on an event's first record, so each is
+    recorded once here, then the stream is synchronised): the events that
+    mtp_time_next_call takes. Create them outside any timed region."""
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    for e in evs:
+        e.record(s)
+    s.synchronize()
+    return evs
+
+
+def mtp_time_next_call(start=None, stop=None) -> None:
+    """Time the next draft / verify call of this thread between two events of
+    timing_events() (a measurement aid; see include/mtp.h): the events take
+    the call's own kernel start and end; read them with elapsed_ms()."""
+    def handle(ev):
+        if ev is None:
+            return None
+        if not ev.cuda_event:
+            raise ValueError("event has no HIP event yet: create it with timing_events()")
+        return ctypes.c_void_p(ev.cuda_event)
+    lib.mtp_time_next_call(handle(start), handle(stop))
+
+
+def elapsed_ms(start, stop) -> float:
+    """Milliseconds between two events stamped by a call timed with
+    mtp_time_next_call (hipEventElapsedTime; torch's own elapsed_time only
+    accepts events that torch recorded)."""
+    ms = ctypes.c_float(0.0)
+    rc = lib.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(start.cuda_event),
+                                 ctypes.c_void_p(stop.cuda_event))
+    if rc != 0:
+        raise RuntimeError(f"hipEventElapsedTime failed (hipError {rc})")
+    return float(ms.value)
 
 
 def _check(status: int, what: str) -> None:

@@ -333,3 +333,42 @@ def test_side_stream_call_without_workspace(torch, mtp):
     for oi, ol in outs:
         assert np.array_equal(oi.cpu().numpy(), orc["id"])
         assert np.array_equal(ol.cpu().numpy(), orc["logit"])
+
+
+def test_time_next_call_brackets_one_call(torch, mtp):
+    """mtp_time_next_call: the events take the timed call's kernel start and
+    end (a positive span, within the host-measured time of the call), the
+    outputs are those of an untimed call, and the request covers one call only
+    (a second call leaves the events as the first one stamped them). Covered
+    for a one-kernel draft and a two-kernel call (the tiled 160-row verify)."""
+    M, N, H = 4, 100_003, 2048
+    x = wl.exact_grid_bf16((M, H), 31, 1)
+    w = wl.exact_grid_bf16((N, H), 31, 2)
+    x_d, w_d = dev_bf16(x), dev_bf16(w)
+    ref = gpu_draft(x_d, w_d, None)
+    e0, e1 = mtp.timing_events(2)
+    with pytest.raises(ValueError):   # an event torch has not created yet
+        mtp.mtp_time_next_call(torch.cuda.Event(enable_timing=True), e1)
+    mtp.mtp_time_next_call(e0, e1)
+    got = gpu_draft(x_d, w_d, None)
+    span = mtp.elapsed_ms(e0, e1)
+    assert np.array_equal(got[0], ref[0]) and np.array_equal(got[1], ref[1])
+    assert 0.0 < span < 50.0, span                  # ms
+    gpu_draft(x_d, w_d, None)                       # not timed: the events keep their stamps
+    assert mtp.elapsed_ms(e0, e1) == span
+    # two kernels (hidden pack + register-ring kernel): start on the first, stop on the last
+    B, k, V, H2 = 32, 4, 20_000, 512
+    hv = wl.exact_grid_bf16((B * (k + 1), H2), 32, 1)
+    wv = wl.exact_grid_bf16((V, H2), 32, 2)
+    head_t = mtp.alloc_tiled(V, H2)
+    mtp.mtp_pack_tiled(dev_bf16(wv), None, head_t, C=V)
+    a = torch.full((B, k + 1), -7, dtype=torch.int32, device="cuda")
+    acc = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    tok = torch.full((B, k + 1), -7, dtype=torch.int32, device="cuda")
+    d = torch.zeros((B, k), dtype=torch.int32, device="cuda")
+    f0, f1 = mtp.timing_events(2)
+    mtp.mtp_time_next_call(f0, f1)
+    mtp.mtp_verify_accept_tiled(dev_bf16(hv), head_t, V, d, B, k, a, acc, tok)
+    torch.cuda.synchronize()
+    assert 0.0 < mtp.elapsed_ms(f0, f1) < 50.0
+    assert np.array_equal(a.cpu().numpy().ravel(), oracle.argmax(hv, wv)["id"])
