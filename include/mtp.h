@@ -115,10 +115,14 @@ mtp_status mtp_validate_ids(const int32_t *ids_host, int64_t C, int64_t V);
 
 /* Bytes of workspace needed by mtp_draft_argmax for M hidden rows, and by
  * mtp_verify_accept for B sequences with k drafts each (the same sizes serve
- * every variant of these calls; with M or B*(k+1) above 128 they include the
- * tiled calls' staging area of about M*H*2 bytes, placed past 33 KiB of
- * counters). 0 for arguments out of range. A tiled call with more than 128 hidden rows returns
- * MTP_ERR_WORKSPACE when given less. */
+ * every variant of these calls; with M or B*(k+1) above 128 they include a
+ * staging area of about M*H*2 bytes for the packed hidden block, placed past
+ * 33 KiB of counters). 0 for arguments out of range. A tiled call with more
+ * than 128 hidden rows returns MTP_ERR_WORKSPACE when given less. A row-major
+ * call needs only the counters (256 + 8*M bytes, rounded up to 256): given
+ * the full size, its passes of more than 128 rows (H % 64 == 0) run the
+ * register-ring matrix-core kernel, given less the LDS-fed one; both sum
+ * every logit in the same order, so the results are the same bits. */
 size_t mtp_draft_workspace_bytes(int M, int64_t C, int H);
 size_t mtp_verify_workspace_bytes(int B, int k, int64_t V, int H);
 

@@ -71,6 +71,15 @@ void *stage_ptr(void *ws) {
   return (void *)((p + 255) & ~(uintptr_t)255);
 }
 
+// Row-major calls with more than 128 hidden rows use the staging area when
+// the workspace holds it (the size queries include it), and otherwise run
+// without it on the LDS-fed kernel.
+void *rows_stage(void *ws, size_t ws_bytes, int64_t M, int H) {
+  if (mtp::ring_stage_bytes((int)M, H) == 0 || ws_bytes < call_workspace_bytes(M, H))
+    return nullptr;
+  return stage_ptr(ws);
+}
+
 bool shape_ok(int64_t M, int64_t N, int64_t H) {
   return M >= 1 && M <= MTP_MAX_ROWS && N >= 1 && N <= INT32_MAX && H >= 8 &&
          H <= MTP_MAX_HIDDEN && H % 8 == 0;
@@ -92,7 +101,7 @@ mtp_status check_cfg(const mtp_config *cfg) {
 // Gathered candidates (gather_ids != nullptr: candidate i is head row
 // gather_ids[i]) run on the vector-ALU kernel only.
 mtp_status run_rows(const mtp_bf16 *X, int M, int H, const mtp_bf16 *W, int64_t N,
-                    mtp::RowSink sink, hipStream_t stream, const mtp_config *cfg,
+                    mtp::RowSink sink, hipStream_t stream, const mtp_config *cfg, void *stage,
                     const int32_t *gather_ids = nullptr, int64_t gather_V = 0) {
   const int nch = H / 8;
   const int ncl = mtp::valu_ncl_for(nch);
@@ -138,6 +147,7 @@ mtp_status run_rows(const mtp_bf16 *X, int M, int H, const mtp_bf16 *W, int64_t 
     L.max_blocks_x = per_cu * cus;
     L.sink = sink;
     L.stream = stream;
+    L.stage = stage;
     // rows a multiple of 4 KiB apart: stagger the workgroups over 8 chunk
     // phases (the arithmetic of every logit is the same either way)
     L.nphase = ((int64_t)H * 2) % 4096 == 0 ? 8 : 1;
@@ -390,7 +400,7 @@ mtp_status mtp_draft_argmax_cfg(const mtp_bf16 *hidden, int M, int H, const mtp_
       check_draft_args(hidden, M, H, table, ids, C, out_ids, out_logit, ws, ws_bytes, cfg);
   if (st != MTP_OK) return st;
   return run_rows(hidden, M, H, table, C, draft_sink(ws, ids, out_ids, out_logit, M), stream,
-                  cfg);
+                  cfg, rows_stage(ws, ws_bytes, M, H));
 }
 
 mtp_status mtp_draft_argmax(const mtp_bf16 *hidden, int M, int H, const mtp_bf16 *table,
@@ -410,7 +420,7 @@ mtp_status mtp_verify_accept_cfg(const mtp_bf16 *hidden, int B, int k, int H,
   if (st != MTP_OK) return st;
   return run_rows(hidden, B * (k + 1), H, head, V,
                   verify_sink(ws, B, k, draft, out_argmax, out_logit, out_accept, out_tokens),
-                  stream, cfg);
+                  stream, cfg, rows_stage(ws, ws_bytes, (int64_t)B * (k + 1), H));
 }
 
 mtp_status mtp_verify_accept(const mtp_bf16 *hidden, int B, int k, int H, const mtp_bf16 *head,
@@ -441,7 +451,7 @@ mtp_status mtp_verify_accept_noalloc(const mtp_bf16 *hidden, int B, int k, int H
   if (e != hipSuccess) return hip_fail(e);
   return run_rows(hidden, B * (k + 1), H, head, V,
                   verify_sink(ws, B, k, draft, out_argmax, out_logit, out_accept, out_tokens),
-                  stream, nullptr);
+                  stream, nullptr, nullptr);
 }
 
 size_t mtp_tiled_bytes(int64_t rows, int H) { return tiled_bytes_of(rows, H); }
@@ -521,7 +531,7 @@ mtp_status mtp_draft_argmax_gather_cfg(const mtp_bf16 *hidden, int M, int H,
   if (st != MTP_OK) return st;
   // the key of a gathered candidate is its id, so the finish needs no id map
   return run_rows(hidden, M, H, head, C, draft_sink(ws, nullptr, out_ids, out_logit, M), stream,
-                  cfg, ids, V);
+                  cfg, nullptr, ids, V);
 }
 
 mtp_status mtp_draft_argmax_gather(const mtp_bf16 *hidden, int M, int H, const mtp_bf16 *head,

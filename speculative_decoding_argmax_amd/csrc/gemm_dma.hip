@@ -551,6 +551,22 @@ __global__ void __launch_bounds__(WV * 64)
 // the up to D - 1 chunks past the end are multiplied into a tile that is
 // never evaluated. Summation order per logit is that of the kernel above
 // (steps ascending, MFMA in-step order), so results are bit-identical to it.
+//
+// Row-major heads (RM, H % 64 == 0): a chunk is two steps, i.e. one 128-byte
+// segment of every row. A 16-row block of it takes two buffer loads, each
+// covering 8 whole row segments (a load shaped like the MFMA operand, 16 rows
+// x 64 bytes, streams at about half the rate): in load h, lane l holds row
+// 8h + (l mod 8) of the block, 16-byte piece l / 16 + 4 ((l / 8) mod 2) of the
+// segment. The operands of the chunk's two steps are then one DPP exchange of
+// half rows away: lanes 8..15 of each 16-lane row of load 0 swap with lanes
+// 0..7 of load 1 (row_ror:8 with a bank mask, one v_mov_b32_dpp per dword),
+// after which load 0 holds step 0 (lane j + 16g: row j, piece g) and load 1
+// step 1 (row j, piece 4 + g), exactly the tiled fragments. Rows past the
+// table fall outside the load's descriptor range and read zeros. Two chunks
+// of registers (D = 2) keep as many weight bytes in flight per wave as three
+// one-step chunks do, and the running best of each lane lives in the LDS
+// reduction arrays (read and written only when a tile ends), so the wave
+// stays within the 256 registers of two waves per SIMD.
 
 // hidden [M][nch] (16-byte chunks) -> fragments (st, b), 1 KiB each, ordered
 // st * nbt + b: lane j + 16 g holds hidden row 16 b + j, chunk 4 st + g.
@@ -570,20 +586,20 @@ __global__ void __launch_bounds__(256)
   }
 }
 
-template <int NB, int RW, int KS, int D, int WV, int CP>
+template <int NB, int RW, int KS, int D, int WV, int CP, bool RM = false>
 __global__ void __launch_bounds__(WV * 64)
     gemm_argmax_ring(const uint4 *__restrict__ XP, const uint4 *WT, int M, int N, int S,
-                     int nbt, RowSink sink) {
+                     int nbt, int nch, RowSink sink) {
   constexpr int RBT = WV * RW;
   constexpr int TV = RBT * 16;
   constexpr int BF = KS * NB;                   // hidden fragments per chunk
   constexpr int PWB = (BF + WV - 1) / WV;       // hidden copies per wave per chunk
   constexpr int AL = RW * KS;                   // weight loads per wave per chunk
-  static_assert(D >= 3 && D <= 4, "ring depth");
+  static_assert(RM ? (KS == 2 && D >= 2 && D <= 4) : (D >= 3 && D <= 4), "ring depth");
   static_assert(RBT % 4 == 0, "whole 64-row tiles");
   __shared__ uint4 bs0[BF * 64];
   __shared__ uint4 bs1[BF * 64];
-  __shared__ uint4 bs2[BF * 64];
+  __shared__ uint4 bs2[D > 2 ? BF * 64 : 1];
   __shared__ uint4 bs3[D > 3 ? BF * 64 : 1];
   __shared__ float red_v[WV * NB * 64];
   __shared__ int red_i[WV * NB * 64];
@@ -614,10 +630,61 @@ __global__ void __launch_bounds__(WV * 64)
 
   uint4 ar[D][KS][RW];
   int a_t = bx, a_c = 0;
+  // row-major: one descriptor per tile (rows past the table lie outside its
+  // range and read zeros), the chunk's column offset as the scalar offset,
+  // and per load the lane's offset within the tile: row 8h + (l mod 8) of
+  // the wave's block rw, piece l / 16 + 4 ((l / 8) mod 2) of the segment.
+  // These stay in registers for the whole kernel, so a chunk's loads cost
+  // no per-load address arithmetic.
+  const int64_t rowbytes = (int64_t)nch * 16;
+  int rm_voff[2][RM ? RW : 1];
+  if constexpr (RM) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int rw = 0; rw < RW; ++rw)
+        rm_voff[h][rw] = (int)(((wave * RW + rw) * 16 + 8 * h + (lane & 7)) * rowbytes) +
+                         16 * ((lane >> 4) + 4 * ((lane >> 3) & 1));
+  }
+  auto rm_rsrc = [&](int tile) __attribute__((always_inline)) {
+    const int64_t row0 = (int64_t)tile * TV;
+    const int64_t left = ((int64_t)N - row0) * rowbytes;
+    const int nrec = left <= 0 ? 0 : left > 0x7FFFFFFF ? 0x7FFFFFFF : (int)left;
+    return __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(reinterpret_cast<const char *>(WT) + row0 * rowbytes), (short)0, nrec,
+        0x00020000);
+  };
+  __amdgpu_buffer_rsrc_t a_rs = rm_rsrc(bx);
+  // keep `own` in lanes 0..7 (swap_hi) or 8..15 (swap_lo) of each 16-lane
+  // row and take the other half from `other` rotated by 8 lanes (row_ror:8)
+  auto swap_hi = [](uint32_t own, uint32_t other) __attribute__((always_inline)) -> uint32_t {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)own, (int)other, 0x128, 0xF, 0xC, false);
+  };
+  auto swap_lo = [](uint32_t own, uint32_t other) __attribute__((always_inline)) -> uint32_t {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)own, (int)other, 0x128, 0xF, 0x3, false);
+  };
   auto issue_a = [&](auto tag) __attribute__((always_inline)) {
     constexpr int SL = decltype(tag)::value;
     const int tile = a_t;
     const int c = a_c;
+    if constexpr (RM) {
+      const __amdgpu_buffer_rsrc_t r = a_rs;
+      if (++a_c == nchunks) {
+        a_c = 0;
+        a_t += gdx;
+        a_rs = rm_rsrc(a_t);
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int rw = 0; rw < RW; ++rw) {
+          const u32x4_ring_t v = __builtin_amdgcn_raw_buffer_load_b128(r, rm_voff[h][rw], c * 128, CP);
+          ar[SL][h][rw] = make_uint4(v.x, v.y, v.z, v.w);
+        }
+      }
+      (void)tile;
+      return;
+    }
     if (++a_c == nchunks) {
       a_c = 0;
       a_t += gdx;
@@ -635,22 +702,23 @@ __global__ void __launch_bounds__(WV * 64)
       }
     }
   };
+  // hidden copies: one descriptor per chunk (its first fragment of this
+  // pass), and per copy a scalar offset to fragment (s, nb) of the chunk,
+  // which depends only on the wave (computed outside the loop)
   int b_c = 0;
   auto issue_b = [&](auto tag) __attribute__((always_inline)) {
     uint4 *base = bslot(tag);
     const int c = b_c;
     if (++b_c == nchunks) b_c = 0;
+    const uint4 *fr = XP + ((int64_t)c * KS * nbt + by * NB) * kWave;
+    __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc((void *)fr, (short)0, 0x7FFFFFFF, 0x00020000);
 #pragma unroll
     for (int q = 0; q < PWB; ++q) {
       int f = wave + WV * q;
       f = f < BF ? f : BF - 1;                   // surplus copies repeat the last fragment
-      const int s = f / NB;
-      const int nb = f - s * NB;
-      const uint4 *fr = XP + ((int64_t)(c * KS + s) * nbt + by * NB + nb) * kWave;
-      __amdgpu_buffer_rsrc_t r =
-          __builtin_amdgcn_make_buffer_rsrc((void *)fr, (short)0, 1024, 0x00020000);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, MTP_LDS(base + f * kWave), 16, lane * 16, 0, 0,
-                                               0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, MTP_LDS(base + f * kWave), 16, lane * 16,
+                                               ((f / NB) * nbt + f % NB) * 1024, 0, 0);
     }
   };
 
@@ -659,12 +727,22 @@ __global__ void __launch_bounds__(WV * 64)
   for (int rw = 0; rw < RW; ++rw)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[rw][nb] = f32x4_dma_t{0.f, 0.f, 0.f, 0.f};
-  float bv[NB];
-  int bi[NB];
+  // running best (logit, row) of each lane's hidden row: registers, or for
+  // row-major heads this lane's entries of the reduction arrays
+  constexpr int NBR = RM ? 1 : NB;
+  float bv[NBR];
+  int bi[NBR];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
+  for (int nb = 0; nb < NBR; ++nb) {
     bv[nb] = 0.f;
     bi[nb] = -1;
+  }
+  if constexpr (RM) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      red_v[(wave * NB + nb) * kWave + lane] = 0.f;
+      red_i[(wave * NB + nb) * kWave + lane] = -1;
+    }
   }
 
   // prologue: chunks 0 .. D - 2, in the order A B A B ...
@@ -672,10 +750,12 @@ __global__ void __launch_bounds__(WV * 64)
   asm volatile("" ::: "memory");
   issue_b(std::integral_constant<int, 0>{});
   asm volatile("" ::: "memory");
-  issue_a(std::integral_constant<int, 1>{});
-  asm volatile("" ::: "memory");
-  issue_b(std::integral_constant<int, 1>{});
-  asm volatile("" ::: "memory");
+  if constexpr (D > 2) {
+    issue_a(std::integral_constant<int, 1>{});
+    asm volatile("" ::: "memory");
+    issue_b(std::integral_constant<int, 1>{});
+    asm volatile("" ::: "memory");
+  }
   if constexpr (D > 3) {
     issue_a(std::integral_constant<int, 2>{});
     asm volatile("" ::: "memory");
@@ -688,20 +768,48 @@ __global__ void __launch_bounds__(WV * 64)
     constexpr int SL = decltype(tag)::value;
     constexpr int NX = (SL + D - 1) % D;
     issue_a(std::integral_constant<int, NX>{});
+    asm volatile("" ::: "memory");
     // younger than chunk it's hidden copies: D - 2 whole chunks, then this
     // body's weight loads (the weights of chunk it are older still)
     wait_vmcnt<(D - 2) * (AL + PWB) + AL>();
     barrier_no_fence();
     issue_b(std::integral_constant<int, NX>{});
     asm volatile("" ::: "memory");
+    if constexpr (RM) {
+      // half-row exchange: loads 0 and 1 of each block become the operands
+      // of steps 0 and 1 (row_ror:8 is its own inverse; the bank mask keeps
+      // the other half of each 16-lane row)
+#pragma unroll
+      for (int rw = 0; rw < RW; ++rw) {
+        const uint4 l0 = ar[SL][0][rw], l1 = ar[SL][1][rw];
+        ar[SL][0][rw] = make_uint4(swap_hi(l0.x, l1.x), swap_hi(l0.y, l1.y),
+                                   swap_hi(l0.z, l1.z), swap_hi(l0.w, l1.w));
+        ar[SL][1][rw] = make_uint4(swap_lo(l1.x, l0.x), swap_lo(l1.y, l0.y),
+                                   swap_lo(l1.z, l0.z), swap_lo(l1.w, l0.w));
+      }
+    }
     const uint4 *Bf = bslot(tag);
+    if constexpr (RM) {
+      // operand B one fragment ahead: the LDS read of fragment f + 1 is in
+      // flight while the MFMAs of fragment f run
+      uint4 bnext = Bf[lane];
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
+      for (int f = 0; f < KS * NB; ++f) {
+        const uint4 b = bnext;
+        if (f + 1 < KS * NB) bnext = Bf[(f + 1) * kWave + lane];
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const uint4 b = Bf[(s * NB + nb) * kWave + lane];
+        for (int rw = 0; rw < RW; ++rw)
+          acc[rw][f % NB] = mfma16_dma(ar[SL][f / NB][rw], b, acc[rw][f % NB]);
+      }
+    } else {
 #pragma unroll
-        for (int rw = 0; rw < RW; ++rw) acc[rw][nb] = mfma16_dma(ar[SL][s][rw], b, acc[rw][nb]);
+      for (int s = 0; s < KS; ++s) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const uint4 b = Bf[(s * NB + nb) * kWave + lane];
+#pragma unroll
+          for (int rw = 0; rw < RW; ++rw) acc[rw][nb] = mfma16_dma(ar[SL][s][rw], b, acc[rw][nb]);
+        }
       }
     }
     if (++cur_c == nchunks) {
@@ -709,20 +817,43 @@ __global__ void __launch_bounds__(WV * 64)
       cur_c = 0;
       cur_t += gdx;
       const int vbase = tile * TV + wave * RW * 16 + 4 * g;
-#pragma unroll
-      for (int rw = 0; rw < RW; ++rw) {
+      if constexpr (RM) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
+          float cv = red_v[(wave * NB + nb) * kWave + lane];
+          int ci = red_i[(wave * NB + nb) * kWave + lane];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int v = vbase + rw * 16 + r;
-            const float z = acc[rw][nb][r];
-            if (v < N && better_row(z, v, bv[nb], bi[nb])) {
-              bv[nb] = z;
-              bi[nb] = v;
+          for (int rw = 0; rw < RW; ++rw) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int v = vbase + rw * 16 + r;
+              const float z = acc[rw][nb][r];
+              if (v < N && better_row(z, v, cv, ci)) {
+                cv = z;
+                ci = v;
+              }
             }
+            acc[rw][nb] = f32x4_dma_t{0.f, 0.f, 0.f, 0.f};
           }
-          acc[rw][nb] = f32x4_dma_t{0.f, 0.f, 0.f, 0.f};
+          red_v[(wave * NB + nb) * kWave + lane] = cv;
+          red_i[(wave * NB + nb) * kWave + lane] = ci;
+        }
+      } else {
+#pragma unroll
+        for (int rw = 0; rw < RW; ++rw) {
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int v = vbase + rw * 16 + r;
+              const float z = acc[rw][nb][r];
+              if (v < N && better_row(z, v, bv[nb], bi[nb])) {
+                bv[nb] = z;
+                bi[nb] = v;
+              }
+            }
+            acc[rw][nb] = f32x4_dma_t{0.f, 0.f, 0.f, 0.f};
+          }
         }
       }
     }
@@ -731,16 +862,18 @@ __global__ void __launch_bounds__(WV * 64)
   for (int it = 0; it < total; it += D) {
     body(std::integral_constant<int, 0>{});
     body(std::integral_constant<int, 1>{});
-    body(std::integral_constant<int, 2>{});
+    if constexpr (D > 2) body(std::integral_constant<int, 2>{});
     if constexpr (D > 3) body(std::integral_constant<int, 3>{});
   }
   wait_vmcnt<0>();
   __syncthreads();
 
+  if constexpr (!RM) {
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    red_v[(wave * NB + nb) * kWave + lane] = bv[nb];
-    red_i[(wave * NB + nb) * kWave + lane] = bi[nb];
+    for (int nb = 0; nb < NB; ++nb) {
+      red_v[(wave * NB + nb) * kWave + lane] = bv[nb];
+      red_i[(wave * NB + nb) * kWave + lane] = bi[nb];
+    }
   }
   __syncthreads();
   if (tid < NB * 16) {
@@ -796,7 +929,7 @@ int dma_nb_for(int M) {
 // Instantiated shapes (measured on MI355X at the workload shapes; none spills
 // registers, every one fits the 160 KiB LDS). Non-temporal weight copies
 // (CP = 2) stream 6.7 TB/s where default-policy copies reach 6.0 TB/s.
-template <int NB, int RW, int KS, int D, int WV, int CP>
+template <int NB, int RW, int KS, int D, int WV, int CP, bool RM = false>
 static hipError_t launch_ring_cfg(const DmaLaunch &L) {
   constexpr int TV = WV * RW * 16;
   const int64_t ntiles = (L.N + TV - 1) / TV;
@@ -809,9 +942,9 @@ static hipError_t launch_ring_cfg(const DmaLaunch &L) {
                                     false, (const uint4 *)L.X, L.M, L.nch, L.S, nbt,
                                     (uint4 *)L.stage);
   if (e != hipSuccess) return e;
-  return launch_call_kernel((gemm_argmax_ring<NB, RW, KS, D, WV, CP>), dim3(gx, gy),
+  return launch_call_kernel((gemm_argmax_ring<NB, RW, KS, D, WV, CP, RM>), dim3(gx, gy),
                             dim3(WV * 64), L.stream, false, true, (const uint4 *)L.stage,
-                            (const uint4 *)L.WT, L.M, (int)L.N, L.S, nbt, L.sink);
+                            (const uint4 *)L.WT, L.M, (int)L.N, L.S, nbt, L.nch, L.sink);
 }
 
 // Staging bytes of the wide passes (the packed hidden block), 0 for M <= 128.
@@ -858,6 +991,8 @@ static hipError_t launch_rm(const DmaLaunch &L) {
 }
 
 hipError_t launch_dma_rm(const DmaLaunch &L, int nb) {
+  // wide passes with staging: the register ring on row-major rows
+  if (nb == 10 && L.stage) return launch_ring_cfg<10, 4, 2, 2, 8, 2, true>(L);
   switch (nb) {
     case 1: return launch_rm<1, 1, 3, 8>(L);
     case 2: return launch_rm<2, 2, 4, 4>(L);

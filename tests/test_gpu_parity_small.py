@@ -116,8 +116,61 @@ def test_verify_special_drafts(torch, mtp):
     assert np.array_equal(g["tokens"][:, 0], t[:, 0]) and np.all(g["tokens"][:, 1:] == -1)
 
 
+def rows_workspace(torch, mtp, M):
+    """The smallest workspace a row-major call accepts: the 256-byte header
+    and one 8-byte key per hidden row (no staging area)."""
+    return mtp.alloc_workspace(256 + -(-M * 8 // 256) * 256)
+
+
+@pytest.mark.parametrize("M,N,H", [(160, 1111, 5120), (161, 300, 256), (200, 2999, 1024),
+                                   (144, 5000, 2048), (130, 777, 64), (320, 4100, 4096)])
+def test_rows_wide_pass_with_and_without_staging(torch, mtp, M, N, H):
+    """More than 128 hidden rows on a row-major table. Given the staging area
+    (a workspace from the size query) the call runs the register-ring kernel,
+    given only the counters the LDS-fed kernel: on q/16-grid inputs both equal
+    the oracle bit for bit, and on N(0, 0.02) rows both return the same bits,
+    since both sum every logit in the same order."""
+    seed = 500 + M + N + H
+    x = wl.exact_grid_bf16((M, H), seed, 1)
+    w = wl.exact_grid_bf16((N, H), seed, 2)
+    x_d, w_d = dev_bf16(x), dev_bf16(w)
+    staged = gpu_draft(x_d, w_d, None)
+    plain = gpu_draft(x_d, w_d, None, ws=rows_workspace(torch, mtp, M))
+    exact_logit_match(*staged, x, w, None)
+    exact_logit_match(*plain, x, w, None)
+
+    W = wl.head_weights(N, H, seed)
+    h = wl.hidden_states(M, H, seed)
+    W_d, h_d = dev_bf16(W), dev_bf16(h)
+    staged = gpu_draft(h_d, W_d, None)
+    plain = gpu_draft(h_d, W_d, None, ws=rows_workspace(torch, mtp, M))
+    assert np.array_equal(staged[0], plain[0])
+    assert np.array_equal(staged[1].view(np.uint32), plain[1].view(np.uint32))
+    check_rows(staged[0], staged[1], oracle.argmax(h, W), h, W, None)
+
+
+def test_rows_wide_verify_with_and_without_staging(torch, mtp):
+    """The 160-row verify (B = 32, k = 4) on a row-major head, with and
+    without the staging area: identical bits, the oracle's ids, and the
+    oracle's acceptance of those ids."""
+    B, k, V, H = 32, 4, 7000, 5120
+    W = wl.head_weights(V, H, 71)
+    hv = wl.hidden_states(B * (k + 1), H, 71)
+    orc = oracle.argmax(hv, W)
+    t = orc["id"].reshape(B, k + 1)
+    drafts = wl.select_drafts(t, wl.agreement_draws(B, k, 0.5, V, 71), np.arange(V, dtype=np.int32))
+    W_d, hv_d = dev_bf16(W), dev_bf16(hv)
+    staged = gpu_verify(hv_d, W_d, drafts, B, k)
+    plain = gpu_verify(hv_d, W_d, drafts, B, k, ws=rows_workspace(torch, mtp, B * (k + 1)))
+    for key in ("argmax", "accept", "tokens"):
+        assert np.array_equal(staged[key], plain[key])
+    assert np.array_equal(staged["logit"].view(np.uint32), plain["logit"].view(np.uint32))
+    check_rows(staged["argmax"].ravel(), staged["logit"].ravel(), orc, hv, W, None)
+    check_accept(staged, drafts, B, k)
+
+
 @pytest.mark.parametrize("path,M", [("auto", 3), ("mfma", 3), ("mfma", 20), ("mfma", 40), ("mfma", 60),
-                                    ("mfma", 90)])
+                                    ("mfma", 90), ("mfma", 140), ("mfma", 160)])
 def test_duplicate_rows_tie_to_lowest_id(torch, mtp, path, M):
     """Random N(0,0.02) head with the winner's row copied below and above it:
     the copies score bit-identically on the GPU and the lowest id wins."""
@@ -152,7 +205,7 @@ def test_duplicate_rows_tie_to_lowest_id(torch, mtp, path, M):
 
 
 @pytest.mark.parametrize("path,M", [("auto", 4), ("mfma", 4), ("mfma", 20), ("mfma", 33),
-                                    ("mfma", 60)])
+                                    ("mfma", 60), ("mfma", 150)])
 def test_determinism_across_launch_shapes(torch, mtp, path, M):
     """Bit-identical outputs for repeated calls and any grid size."""
     V, H = 50000, 2048
