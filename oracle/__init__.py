@@ -20,9 +20,9 @@ the pages each one follows):
   draft_fp8(h, q, exps, ids)  argmax over the fp8 table, mapped to ids
   draft_fp8_gather(h, q, exps, ids)
                               draft_gather's candidates on an fp8 head
-  e2m1_value(codes), e2m1_round(x), mx_block_exponent(w)
+  e2m1_value(codes), e2m1_round(x), mx_block_exponent(w, rule)
                               the OCP E2M1 element and the MX block scale rule
-  quantize_mxfp4(head, ids)   MXFP4 candidate table: packed E2M1 codes and
+  quantize_mxfp4(head, ids, rule)  MXFP4 candidate table: packed E2M1 codes and
                               E8M0 scales per block of 32
   draft_mxfp4(h, q, scales, ids)
                               argmax over the MXFP4 table, mapped to ids
@@ -88,14 +88,17 @@ class _Lib:
         lib.mtp_oracle_e2m1_round.restype = ctypes.c_uint8
         lib.mtp_oracle_e2m1_round_array.argtypes = [P, I64, P]
         lib.mtp_oracle_mx_block_exponent.argtypes = [P, I64, P]
+        lib.mtp_oracle_mx_block_exponent_fit.argtypes = [P, I64, P]
         lib.mtp_oracle_quantize_mxfp4.argtypes = [P, I64, I64, P, I64, P, P]
+        lib.mtp_oracle_quantize_mxfp4_rule.argtypes = [P, I64, I64, P, I64, P, P, ctypes.c_int]
         lib.mtp_oracle_mxfp4_argmax.argtypes = [P, I64, P, P, P, I64, I64, P, P, P, P, P]
         for f in ("mtp_oracle_logits", "mtp_oracle_pair_logits", "mtp_oracle_argmax",
                   "mtp_oracle_accept", "mtp_oracle_check_ids", "mtp_oracle_pack",
                   "mtp_oracle_e4m3_round_array", "mtp_oracle_fp8_row_exponent",
                   "mtp_oracle_quantize_fp8", "mtp_oracle_fp8_argmax",
                   "mtp_oracle_e2m1_round_array", "mtp_oracle_mx_block_exponent",
-                  "mtp_oracle_quantize_mxfp4", "mtp_oracle_mxfp4_argmax"):
+                  "mtp_oracle_mx_block_exponent_fit", "mtp_oracle_quantize_mxfp4",
+                  "mtp_oracle_quantize_mxfp4_rule", "mtp_oracle_mxfp4_argmax"):
             getattr(lib, f).restype = ctypes.c_int
         self.lib = lib
         self.path = path
@@ -380,18 +383,25 @@ def e2m1_round(x) -> np.ndarray:
     return out
 
 
-def mx_block_exponent(w_block: np.ndarray) -> int:
-    """Scale exponent of one block of bf16 values (OCP MX rule)."""
+MX_SCALE_RULES = {"ocp": 0, "fit": 1}
+
+
+def mx_block_exponent(w_block: np.ndarray, rule: str = "ocp") -> int:
+    """Scale exponent of one block of bf16 values: the OCP MX rule
+    floor(log2 max|w|) - 2, or the fit rule, the smallest e with
+    max|w| <= 6 * 2^e (both clamped to [-127, 127], -127 for a zero block)."""
     w = _bf16(np.atleast_1d(w_block))
     e = np.zeros(1, np.int32)
-    _check(_load().mtp_oracle_mx_block_exponent(_p(w), w.size, _p(e)), "mx_block_exponent")
+    fn = {"ocp": _load().mtp_oracle_mx_block_exponent,
+          "fit": _load().mtp_oracle_mx_block_exponent_fit}[rule]
+    _check(fn(_p(w), w.size, _p(e)), "mx_block_exponent")
     return int(e[0])
 
 
-def quantize_mxfp4(head: np.ndarray, ids: Optional[np.ndarray] = None):
+def quantize_mxfp4(head: np.ndarray, ids: Optional[np.ndarray] = None, rule: str = "ocp"):
     """The MXFP4 candidate table of head rows ids (None: every row): packed
     E2M1 codes [C][H/2] (element 2i in the low nibble) and E8M0 block scales
-    [C][H/32] (code e + 127)."""
+    [C][H/32] (code e + 127), block scales by the OCP rule or the fit rule."""
     head = _bf16(head)
     V, H = head.shape
     if ids is not None:
@@ -399,7 +409,8 @@ def quantize_mxfp4(head: np.ndarray, ids: Optional[np.ndarray] = None):
     C = V if ids is None else len(ids)
     q = np.empty((C, H // 2), dtype=np.uint8)
     scales = np.empty((C, H // 32), dtype=np.uint8)
-    _check(_load().mtp_oracle_quantize_mxfp4(_p(head), V, H, _p(ids), C, _p(q), _p(scales)),
+    _check(_load().mtp_oracle_quantize_mxfp4_rule(_p(head), V, H, _p(ids), C, _p(q), _p(scales),
+                                                  MX_SCALE_RULES[rule]),
            "quantize_mxfp4")
     return q, scales
 

@@ -58,6 +58,11 @@
  * to 6; a negative value keeps its sign bit even when it rounds to zero).
  * Two codes share a byte, element 2i in the low nibble. A row's logit is
  * sum_j x[j] * 2^e(j / 32) * value(q[j]), summed as above in double.
+ * A second scale reading (the "fit" rule) is offered beside the OCP one: the
+ * smallest e with max |w| <= 6 * 2^e, so that no element of the block
+ * saturates; same clamp, same zero block, same elements otherwise. It
+ * differs from the OCP rule only in blocks whose largest magnitude lies
+ * above 6 * 2^(floor(log2 max) - 2), where it takes e one larger.
  *
  * Build: gcc -O2 -fopenmp -ffp-contract=off -shared -fPIC (no fast-math).
  */
@@ -380,11 +385,37 @@ int mtp_oracle_mx_block_exponent(const uint16_t *w, int64_t n, int32_t *e_out) {
   return ORC_OK;
 }
 
+/* A block's scale exponent under the fit rule: the smallest e with
+ * max |w| <= 6 * 2^e, clamped to [-127, 127]; -127 for an all-zero block.
+ * 6 * 2^(ilogb(max) - 3) < 2^ilogb(max) <= max, so the search starts below
+ * the answer and steps up to it. */
+int mtp_oracle_mx_block_exponent_fit(const uint16_t *w, int64_t n, int32_t *e_out) {
+  if (!w || !e_out || n <= 0) return ORC_BAD_ARG;
+  double amax = 0.0;
+  for (int64_t j = 0; j < n; ++j) {
+    const double v = fabs(bf16_to_double(w[j]));
+    if (!isfinite(v)) return ORC_NOT_FINITE;
+    if (v > amax) amax = v;
+  }
+  int e = -127;
+  if (amax != 0.0) {
+    e = ilogb(amax) - 3;
+    while (ldexp(6.0, e) < amax) ++e;
+  }
+  if (e < -127) e = -127;
+  if (e > 127) e = 127;
+  *e_out = e;
+  return ORC_OK;
+}
+
 /* Quantise the candidate rows head[ids[i]] (ids NULL: rows 0..C-1) to MXFP4:
  * q[i][j / 2] holds the codes of elements j (low nibble, j even) and j + 1;
- * scales[i][b] = e + 127 of block b (elements 32b .. 32b + 31). H % 32 == 0. */
-int mtp_oracle_quantize_mxfp4(const uint16_t *head, int64_t V, int64_t H, const int32_t *ids,
-                              int64_t C, uint8_t *q, uint8_t *scales) {
+ * scales[i][b] = e + 127 of block b (elements 32b .. 32b + 31). H % 32 == 0.
+ * rule 0: the OCP scale rule; rule 1: the fit rule. */
+int mtp_oracle_quantize_mxfp4_rule(const uint16_t *head, int64_t V, int64_t H,
+                                   const int32_t *ids, int64_t C, uint8_t *q, uint8_t *scales,
+                                   int rule) {
+  if (rule != 0 && rule != 1) return ORC_BAD_ARG;
   if (!head || !q || !scales || V <= 0 || H <= 0 || H % 32 != 0 || C <= 0) return ORC_BAD_ARG;
   if (ids && mtp_oracle_check_ids(ids, C, V) != ORC_OK) return ORC_BAD_IDS;
   if (!ids && C > V) return ORC_BAD_ARG;
@@ -393,7 +424,8 @@ int mtp_oracle_quantize_mxfp4(const uint16_t *head, int64_t V, int64_t H, const 
     const uint16_t *w = head + (int64_t)(ids ? ids[i] : i) * H;
     for (int64_t b = 0; b < nb; ++b) {
       int32_t e = 0;
-      const int r = mtp_oracle_mx_block_exponent(w + 32 * b, 32, &e);
+      const int r = rule == 0 ? mtp_oracle_mx_block_exponent(w + 32 * b, 32, &e)
+                              : mtp_oracle_mx_block_exponent_fit(w + 32 * b, 32, &e);
       if (r != ORC_OK) return r;
       scales[i * nb + b] = (uint8_t)(e + 127);
       for (int64_t j = 32 * b; j < 32 * b + 32; j += 2) {
@@ -404,6 +436,11 @@ int mtp_oracle_quantize_mxfp4(const uint16_t *head, int64_t V, int64_t H, const 
     }
   }
   return ORC_OK;
+}
+
+int mtp_oracle_quantize_mxfp4(const uint16_t *head, int64_t V, int64_t H, const int32_t *ids,
+                              int64_t C, uint8_t *q, uint8_t *scales) {
+  return mtp_oracle_quantize_mxfp4_rule(head, V, H, ids, C, q, scales, 0);
 }
 
 /* One MXFP4 row's logit: sum over j of x[j] * 2^e(j / 32) * value(q[j]), in

@@ -472,6 +472,66 @@ def pin_mxfp4_quantize(oracle, seed=59):
     assert np.array_equal(qi, q[ids]) and np.array_equal(si, sc[ids])
 
 
+def pin_mxfp4_fit_quantize(oracle, seed=67):
+    """The fit scale rule: the smallest e with max|w| <= 6 * 2^e, i.e.
+    6 * 2^(e-1) < max|w| <= 6 * 2^e (clamped to [-127, 127]; -127 for an
+    all-zero block), so no element saturates and every code is the
+    nearest-even E2M1 code of w * 2^-e. It equals the OCP rule's exponent
+    where the OCP scale covers the block (max|w| <= 6 * 2^e_ocp) and is one
+    larger where the OCP scale would saturate. Blocks at exactly 6 * 2^k and
+    one bf16 step above it, at 7 * 2^k (saturating under the OCP rule), at
+    both bf16 extremes and all-zero fix the boundaries; rule "ocp" is the
+    default table."""
+    V, H = 24, 128
+    W = wl.normal_bf16_rows(V, H, 0.02, seed, 1)
+    W[2] = 0
+    W[3, 32:64] = 0                                      # one zero block
+    W[4, :32] = 0x0001                                   # smallest subnormal: clamp at -127
+    W[4, 32:64] = 0x7F7F                                 # largest finite bf16: e = 126
+    six = wl.f32_to_bf16_bits(np.array([6.0 * 2.0 ** -7], np.float32))[0]
+    W[5, :32] = 0
+    W[5, 7] = six                                        # max exactly 6 * 2^-7: e = -7
+    W[5, 32:64] = 0
+    W[5, 40] = six + 1                                   # one bf16 step above: e = -6
+    W[5, 64:96] = 0
+    W[5, 70] = wl.f32_to_bf16_bits(np.array([-7.0 * 2.0 ** -9], np.float32))[0]  # 7 * 2^-9
+    q, sc = oracle.quantize_mxfp4(W, rule="fit")
+    q0, sc0 = oracle.quantize_mxfp4(W, rule="ocp")
+    qd, scd = oracle.quantize_mxfp4(W)
+    assert np.array_equal(q0, qd) and np.array_equal(sc0, scd)
+    wf = wl.bf16_bits_to_f32(W).astype(np.float64)
+    mags = _minifloat_magnitudes(2, 1, 1)
+    raised = 0
+    for i in range(V):
+        for b in range(H // 32):
+            blk = wf[i, 32 * b:32 * b + 32]
+            e = int(sc[i, b]) - 127
+            e0 = int(sc0[i, b]) - 127
+            amax = np.abs(blk).max()
+            assert e == oracle.mx_block_exponent(W[i, 32 * b:32 * b + 32], "fit")
+            if amax == 0:
+                assert e == -127
+                continue
+            if 2.0 ** -125 <= amax < 2.0 ** 127:
+                assert 6.0 * 2.0 ** (e - 1) < amax <= 6.0 * 2.0 ** e, (i, b, e, amax)
+                assert e == (e0 if amax <= 6.0 * 2.0 ** e0 else e0 + 1), (i, b, e, e0)
+                raised += e != e0
+            for j in range(32 * b, 32 * b + 32):
+                x = float(wf[i, j] * 2.0 ** -e)
+                if e > -127:
+                    assert abs(x) <= 6.0
+                byte = int(q[i, j // 2])
+                code = byte & 15 if j % 2 == 0 else byte >> 4
+                assert code == _nearest_even_code(x, mags, 8), (i, j)
+    assert raised > 0
+    assert sc[4, 0] == 0 and sc[4, 1] == 126 + 127 and sc0[4, 1] == 125 + 127
+    assert sc[5, 0] == -7 + 127 and sc[5, 1] == -6 + 127
+    assert sc[5, 2] == -8 + 127 and sc0[5, 2] == -9 + 127
+    ids = np.array([0, 4, 5, 23], np.int32)
+    qi, si = oracle.quantize_mxfp4(W, ids, rule="fit")
+    assert np.array_equal(qi, q[ids]) and np.array_equal(si, sc[ids])
+
+
 def pin_mxfp4_draft(oracle, seed=61):
     """Rows built on the scaled E2M1 grid (every block's max 6 * 2^e, so the
     scale rule returns e) quantise exactly; with hidden rows on the q/16 grid
@@ -694,6 +754,7 @@ ALL_PINS = [
     pin_fp8_gathered_candidates,
     pin_e2m1_format,
     pin_mxfp4_quantize,
+    pin_mxfp4_fit_quantize,
     pin_mxfp4_draft,
     pin_mxfp4_gathered_candidates,
     pin_pack,

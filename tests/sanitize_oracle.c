@@ -42,6 +42,10 @@ int mtp_oracle_e2m1_round_array(const double *x, int64_t n, uint8_t *out);
 int mtp_oracle_mx_block_exponent(const uint16_t *w, int64_t n, int32_t *e_out);
 int mtp_oracle_quantize_mxfp4(const uint16_t *head, int64_t V, int64_t H, const int32_t *ids,
                               int64_t C, uint8_t *q, uint8_t *scales);
+int mtp_oracle_mx_block_exponent_fit(const uint16_t *w, int64_t n, int32_t *e_out);
+int mtp_oracle_quantize_mxfp4_rule(const uint16_t *head, int64_t V, int64_t H,
+                                   const int32_t *ids, int64_t C, uint8_t *q, uint8_t *scales,
+                                   int rule);
 int mtp_oracle_mxfp4_argmax(const uint16_t *x, int64_t M, const uint8_t *q,
                             const uint8_t *scales, const int32_t *ids, int64_t N, int64_t H,
                             int32_t *top_id, float *top_logit, double *top_exact,
@@ -112,6 +116,7 @@ static void run_shape(int64_t M, int64_t V, int64_t C, int64_t H) {
     uint8_t *s4 = malloc((size_t)(C * H / 32));
     EXPECT(mtp_oracle_quantize_mxfp4(head, V, H, ids, C, q4, s4) == 0);
     EXPECT(mtp_oracle_quantize_mxfp4(head, V, H, NULL, C, q4, s4) == 0);
+    EXPECT(mtp_oracle_quantize_mxfp4_rule(head, V, H, ids, C, q4, s4, 1) == 0);
     EXPECT(mtp_oracle_mxfp4_argmax(x, M, q4, s4, NULL, C, H, top, topf, tope, run, rune) == 0);
     free(q4);
     free(s4);
@@ -160,12 +165,15 @@ int main(void) {
     memset(w, 0, sizeof w);
     EXPECT(mtp_oracle_fp8_row_exponent(w, 64, &e) == 0 && e == 0);
     EXPECT(mtp_oracle_mx_block_exponent(w, 32, &e) == 0 && e == -127);
+    EXPECT(mtp_oracle_mx_block_exponent_fit(w, 32, &e) == 0 && e == -127);
     w[5] = 0x7F7F;  /* largest finite bfloat16 */
     EXPECT(mtp_oracle_fp8_row_exponent(w, 64, &e) == 0);
     EXPECT(mtp_oracle_mx_block_exponent(w, 32, &e) == 0 && e == 125);
+    EXPECT(mtp_oracle_mx_block_exponent_fit(w, 32, &e) == 0 && e == 126);
     w[6] = 0x0001;  /* smallest subnormal bfloat16 */
     w[5] = 0;
     EXPECT(mtp_oracle_mx_block_exponent(w, 32, &e) == 0 && e == -127);
+    EXPECT(mtp_oracle_mx_block_exponent_fit(w, 32, &e) == 0 && e == -127);
     w[7] = 0x7F80;  /* +inf: outside the contract, reported */
     EXPECT(mtp_oracle_fp8_row_exponent(w, 64, &e) == 7);
   }
@@ -180,6 +188,7 @@ int main(void) {
     EXPECT(mtp_oracle_argmax(h, 1, h, NULL, 0, 8, NULL, NULL, NULL, NULL, NULL) == 1);
     EXPECT(mtp_oracle_accept(NULL, NULL, 1, 1, NULL, NULL) == 1);
     EXPECT(mtp_oracle_quantize_mxfp4(h, 1, 8, NULL, 1, (uint8_t *)t, (uint8_t *)t) == 1);
+    EXPECT(mtp_oracle_quantize_mxfp4_rule(h, 1, 32, NULL, 1, (uint8_t *)t, (uint8_t *)t, 2) == 1);
   }
   if (failures) {
     fprintf(stderr, "%d check(s) failed\n", failures);

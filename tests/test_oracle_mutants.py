@@ -39,11 +39,16 @@ MUTATIONS = [
     ("e2m1_sign_lost", "const uint8_t s = x < 0.0 ? 8 : 0;", "const uint8_t s = 0;"),
     ("mx_scale_one_too_high", "ilogb(amax) - 2", "ilogb(amax) - 1"),
     ("mx_zero_block_scale", "amax == 0.0 ? -127", "amax == 0.0 ? 0"),
-    ("mx_no_low_clamp", "if (e < -127) e = -127;", ""),
+    ("mx_no_low_clamp", "ilogb(amax) - 2;\n  if (e < -127) e = -127;", "ilogb(amax) - 2;\n"),
+    ("mx_fit_no_low_clamp", "++e;\n  }\n  if (e < -127) e = -127;", "++e;\n  }\n"),
     ("mx_nibbles_swapped", "(uint8_t)(lo | (hi << 4))", "(uint8_t)(hi | (lo << 4))"),
     ("mx_logit_scale_stride_16", "const int e = (int)scales[j / 32] - 127;", "const int e = (int)scales[j / 16] - 127;"),
     ("mx_logit_ignores_scale", "s += bf16_to_double(x[j]) * ldexp(mtp_oracle_e2m1_value(code), e);", "s += bf16_to_double(x[j]) * mtp_oracle_e2m1_value(code);"),
     ("mx_logit_nibble_order", "(j & 1) ? (q[j / 2] >> 4) : (q[j / 2] & 15)", "(j & 1) ? (q[j / 2] & 15) : (q[j / 2] >> 4)"),
+    ("mx_fit_not_minimal_at_equality", "while (ldexp(6.0, e) < amax) ++e;", "while (ldexp(6.0, e) <= amax) ++e;"),
+    ("mx_fit_search_starts_high", "e = ilogb(amax) - 3;", "e = ilogb(amax) - 1;"),
+    ("mx_fit_bound_4", "while (ldexp(6.0, e) < amax) ++e;", "while (ldexp(4.0, e) < amax) ++e;"),
+    ("mx_fit_rule_ignored", "const int r = rule == 0 ? mtp_oracle_mx_block_exponent(w + 32 * b, 32, &e)", "const int r = 1 ? mtp_oracle_mx_block_exponent(w + 32 * b, 32, &e)"),
 ]
 
 
