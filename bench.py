@@ -90,6 +90,13 @@ def parse_args():
                          "one E8M0 scale per 32 elements; mtp_pack_candidates_mxfp4, or "
                          "mtp_pack_tiled_mxfp4 with --layout tiled); the verify always reads "
                          "the bf16 head")
+    ap.add_argument("--mx-scale", choices=("ocp", "fit"), default="ocp",
+                    help="block scale rule of the MXFP4 packs: the OCP MX rule "
+                         "floor(log2 max|w|) - 2 (default), or the smallest e with "
+                         "max|w| <= 6 * 2^e (no element saturates)")
+    ap.add_argument("--agree-rows", type=int, default=512,
+                    help="hidden rows of the untimed check of how often a quantised draft "
+                         "picks the bf16 draft's token")
     ap.add_argument("--draft-source", choices=("table", "gather"), default="table",
                     help="draft calls read a packed candidate table (default), or head rows "
                          "through a per-call id list (mtp_draft_argmax_gather; with --table "
@@ -169,6 +176,7 @@ def main() -> int:
 
     layout = args.layout
     fp4 = args.table == "mxfp4"
+    mx_rule = mtp.MX_SCALE_RULES[args.mx_scale]
     if layout == "auto":
         layout = "rows" if max(wk.Md, wk.Mv) <= 8 else "tiled"
     gather = args.draft_source == "gather"
@@ -192,18 +200,18 @@ def main() -> int:
             # every head row quantised once; each call gathers its own rows
             tq = torch.empty((wk.V, wk.H // 2), dtype=torch.uint8, device=dev)
             ts = torch.empty((wk.V, wk.H // 32), dtype=torch.uint8, device=dev)
-            mtp.mtp_pack_candidates_mxfp4(head_d, None, tq, ts, C=wk.V)
+            mtp.mtp_pack_candidates_mxfp4(head_d, None, tq, ts, C=wk.V, rule=mx_rule)
             tables.append((tq, ts))
             continue
         if fp4 and layout == "tiled":
             tq, ts = mtp.alloc_tiled_mxfp4(wk.C, wk.H, dev)
-            mtp.mtp_pack_tiled_mxfp4(head_d, ids_d, tq, ts)
+            mtp.mtp_pack_tiled_mxfp4(head_d, ids_d, tq, ts, rule=mx_rule)
             tables.append((tq, ts))
             continue
         if fp4:
             tq = torch.empty((wk.C, wk.H // 2), dtype=torch.uint8, device=dev)
             ts = torch.empty((wk.C, wk.H // 32), dtype=torch.uint8, device=dev)
-            mtp.mtp_pack_candidates_mxfp4(head_d, ids_d, tq, ts)
+            mtp.mtp_pack_candidates_mxfp4(head_d, ids_d, tq, ts, rule=mx_rule)
             tables.append((tq, ts))
             continue
         if fp8 and layout == "rows":
@@ -454,7 +462,7 @@ def main() -> int:
     draft_tables = None
     if wk.tables:
         draft_tables = draft_table_ablation(wk, mtp, wl, head_d, dev, up, sink, stream,
-                                            fmt=args.table)
+                                            fmt=args.table, mx_rule=mx_rule)
 
     # Acceptance of the last timed verify call (the GPU's own outputs): the
     # share of drafts accepted, and tokens emitted per verify (accepted drafts
@@ -474,7 +482,7 @@ def main() -> int:
     if fp8 or fp4:
         # how often the quantised draft picks the bf16 draft's token (512
         # hidden rows of the workload's distribution; untimed)
-        n_rows = 512
+        n_rows = max(1, min(args.agree_rows, 4096))
         hx = up(wl.hidden_states(n_rows, wk.H, wk.seed, block=900))
         t16 = torch.empty((wk.C, wk.H), dtype=torch.int16, device=dev)
         mtp.mtp_pack_candidates(head_d, ids_d, t16)
@@ -584,6 +592,7 @@ def main() -> int:
             "step": "hip_graph" if graphs else "eager",
             "draft_source": args.draft_source,
             "draft_table": args.table,
+            "mx_scale": args.mx_scale if fp4 else None,
         },
         "calls": {"draft": draft_stats, "verify": verify_stats},
         "context": {
@@ -601,6 +610,7 @@ def main() -> int:
             "stream_read": stream_read,
             "acceptance": acceptance,
             "quantised_draft_agrees_with_bf16": agreement,
+            "agreement_rows": (max(1, min(args.agree_rows, 4096)) if (fp8 or fp4) else None),
             "draft_tables": draft_tables,
             "setup_s": round(setup_s, 1),
         },
@@ -614,13 +624,13 @@ def main() -> int:
         lists = [wl.candidate_ids(wk.V, wk.C, wk.seed + 1000 * (c + 1))
                  for c in range(wk.draft_calls)] if gather else None
         result["parity"] = oracle_parity(wk, head, ids, hiddens, hv, drafts, orc, g_drafts,
-                                         g_verify, args.table, lists)
+                                         g_verify, args.table, lists, args.mx_scale)
     print(json.dumps(result), flush=True)
     return 0
 
 
 def draft_table_ablation(wk, mtp, wl, head_d, dev, up, sink, stream, reps=200, copies=3,
-                         fmt="bf16"):
+                         fmt="bf16", mx_rule=0):
     """M = 1 draft calls over each table size of the ablation: the full head
     (identity ids), the 65,536-row subset and the nested 32,768-row subset,
     all at the workload's width, plus 32,768 rows x 2,560 (the pages' per-rank
@@ -656,7 +666,7 @@ def draft_table_ablation(wk, mtp, wl, head_d, dev, up, sink, stream, reps=200, c
             elif fmt == "mxfp4":
                 t = (torch.empty((n, H // 2), dtype=torch.uint8, device=dev),
                      torch.empty((n, H // 32), dtype=torch.uint8, device=dev))
-                mtp.mtp_pack_candidates_mxfp4(src, src_ids, t[0], t[1], C=n)
+                mtp.mtp_pack_candidates_mxfp4(src, src_ids, t[0], t[1], C=n, rule=mx_rule)
             elif src_ids is None:
                 t = src.clone()
             else:
@@ -760,7 +770,7 @@ def cpu_baseline(wk, head, ids, hiddens, hv, drafts, budget_s):
 
 
 def oracle_parity(wk, head, ids, hiddens, hv, drafts, orc, g_drafts, g_verify, table="bf16",
-                  gather_lists=None):
+                  gather_lists=None, mx_scale="ocp"):
     """The GPU outputs of the last timed step against the oracle's outputs for
     the same inputs. A pick passes if it equals the oracle's, or if the row is a
     near tie (oracle runner-up within 1e-3 x |max| of the max) and the pick
@@ -842,7 +852,8 @@ def oracle_parity(wk, head, ids, hiddens, hv, drafts, orc, g_drafts, g_verify, t
     if table == "fp8":
         quant["fp8"] = oracle.quantize_fp8(head, None if gather_lists is not None else ids)
     elif table == "mxfp4":
-        quant["mxfp4"] = oracle.quantize_mxfp4(head, None if gather_lists is not None else ids)
+        quant["mxfp4"] = oracle.quantize_mxfp4(head, None if gather_lists is not None else ids,
+                                               rule=mx_scale)
 
     out = {"rule": "ids equal, or a pick within 1e-3 relative of the max in a near-tie row; "
                    "logits within 2e-3 relative; acceptance equal to the oracle's on the "

@@ -436,6 +436,23 @@ size_t mtp_mxfp4_scale_bytes(int64_t C, int H);
 mtp_status mtp_pack_candidates_mxfp4(const mtp_bf16 *head, int64_t V, int H, const int32_t *ids,
                                      int64_t C, uint8_t *table_q, uint8_t *scales,
                                      hipStream_t stream);
+
+/* Block scale readings for the MXFP4 packs. The pages fix no scale format
+ * (same section as above); the OCP rule above is the default. The fit rule
+ * takes the smallest e with max |w| <= 6 * 2^e over the block (same clamp,
+ * -127 for an all-zero block), so no element saturates: e is one larger than
+ * the OCP exponent in blocks whose maximum lies above 6 * 2^(e_ocp), and the
+ * same elsewhere. The stored format is unchanged, so every MXFP4 draft entry
+ * point (packed, gathered, tiled) reads tables of either rule. */
+#define MTP_MX_SCALE_OCP 0
+#define MTP_MX_SCALE_FIT 1
+
+/* mtp_pack_candidates_mxfp4 with the block scale rule `rule`
+ * (MTP_MX_SCALE_OCP or MTP_MX_SCALE_FIT; anything else gives
+ * MTP_ERR_INVALID_ARG before anything is enqueued). */
+mtp_status mtp_pack_candidates_mxfp4_rule(const mtp_bf16 *head, int64_t V, int H,
+                                          const int32_t *ids, int64_t C, uint8_t *table_q,
+                                          uint8_t *scales, int rule, hipStream_t stream);
 mtp_status mtp_draft_argmax_mxfp4(const mtp_bf16 *hidden, int M, int H, const uint8_t *table_q,
                                   const uint8_t *scales, const int32_t *ids, int64_t C,
                                   int32_t *out_ids, float *out_logit, void *ws, size_t ws_bytes,
@@ -504,6 +521,12 @@ size_t mtp_tiled_mxfp4_scale_bytes(int64_t rows, int H);
 mtp_status mtp_pack_tiled_mxfp4(const mtp_bf16 *head, int64_t V, int H, const int32_t *ids,
                                 int64_t C, void *tiled_q, size_t q_bytes, uint8_t *tiled_scales,
                                 size_t scale_bytes, hipStream_t stream);
+/* mtp_pack_tiled_mxfp4 with the block scale rule `rule` (MTP_MX_SCALE_OCP or
+ * MTP_MX_SCALE_FIT; anything else gives MTP_ERR_INVALID_ARG). */
+mtp_status mtp_pack_tiled_mxfp4_rule(const mtp_bf16 *head, int64_t V, int H, const int32_t *ids,
+                                     int64_t C, void *tiled_q, size_t q_bytes,
+                                     uint8_t *tiled_scales, size_t scale_bytes, int rule,
+                                     hipStream_t stream);
 mtp_status mtp_draft_argmax_tiled_mxfp4(const mtp_bf16 *hidden, int M, int H,
                                         const void *table_q, const uint8_t *tiled_scales,
                                         const int32_t *ids, int64_t C, int32_t *out_ids,

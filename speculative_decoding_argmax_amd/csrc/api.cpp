@@ -654,10 +654,11 @@ size_t mtp_mxfp4_scale_bytes(int64_t C, int H) {
   return (size_t)C * (size_t)(H / 32);
 }
 
-mtp_status mtp_pack_candidates_mxfp4(const mtp_bf16 *head, int64_t V, int H, const int32_t *ids,
-                                     int64_t C, uint8_t *table_q, uint8_t *scales,
-                                     hipStream_t stream) {
+mtp_status mtp_pack_candidates_mxfp4_rule(const mtp_bf16 *head, int64_t V, int H,
+                                          const int32_t *ids, int64_t C, uint8_t *table_q,
+                                          uint8_t *scales, int rule, hipStream_t stream) {
   if (!head || !table_q || !scales) return MTP_ERR_INVALID_ARG;
+  if (rule != MTP_MX_SCALE_OCP && rule != MTP_MX_SCALE_FIT) return MTP_ERR_INVALID_ARG;
   if (V < 1 || V > INT32_MAX || mtp_mxfp4_table_bytes(C, H) == 0) return MTP_ERR_INVALID_ARG;
   if (!ids && C > V) return MTP_ERR_INVALID_ARG;
   if (!aligned(head, 16) || !aligned(table_q, 16) || (ids && !aligned(ids, 4)))
@@ -665,9 +666,16 @@ mtp_status mtp_pack_candidates_mxfp4(const mtp_bf16 *head, int64_t V, int H, con
   int cus = 0;
   hipError_t e = current_cus(&cus);
   if (e != hipSuccess) return hip_fail(e);
-  e = mtp::launch_pack_mxfp4(head, V, H, ids, C, table_q, scales, cus, stream);
+  e = mtp::launch_pack_mxfp4(head, V, H, ids, C, table_q, scales, rule, cus, stream);
   if (e != hipSuccess) return hip_fail(e);
   return MTP_OK;
+}
+
+mtp_status mtp_pack_candidates_mxfp4(const mtp_bf16 *head, int64_t V, int H, const int32_t *ids,
+                                     int64_t C, uint8_t *table_q, uint8_t *scales,
+                                     hipStream_t stream) {
+  return mtp_pack_candidates_mxfp4_rule(head, V, H, ids, C, table_q, scales, MTP_MX_SCALE_OCP,
+                                        stream);
 }
 
 // MXFP4 draft over C candidates: table rows 0..C-1, or (gather_ids) head rows
@@ -758,10 +766,12 @@ size_t mtp_tiled_mxfp4_scale_bytes(int64_t rows, int H) {
   return (size_t)mtp::tiled_rows(rows) * (size_t)(mtp::tiled_cols_fp4(H) / 32);
 }
 
-mtp_status mtp_pack_tiled_mxfp4(const mtp_bf16 *head, int64_t V, int H, const int32_t *ids,
-                                int64_t C, void *tiled_q, size_t q_bytes, uint8_t *tiled_scales,
-                                size_t scale_bytes, hipStream_t stream) {
+mtp_status mtp_pack_tiled_mxfp4_rule(const mtp_bf16 *head, int64_t V, int H, const int32_t *ids,
+                                     int64_t C, void *tiled_q, size_t q_bytes,
+                                     uint8_t *tiled_scales, size_t scale_bytes, int rule,
+                                     hipStream_t stream) {
   if (!head || !tiled_q || !tiled_scales) return MTP_ERR_INVALID_ARG;
+  if (rule != MTP_MX_SCALE_OCP && rule != MTP_MX_SCALE_FIT) return MTP_ERR_INVALID_ARG;
   if (V < 1 || V > INT32_MAX || (!ids && C > V)) return MTP_ERR_INVALID_ARG;
   const size_t need = mtp_tiled_mxfp4_bytes(C, H);
   if (need == 0 || q_bytes < need || scale_bytes < mtp_tiled_mxfp4_scale_bytes(C, H))
@@ -772,9 +782,16 @@ mtp_status mtp_pack_tiled_mxfp4(const mtp_bf16 *head, int64_t V, int H, const in
   int cus = 0;
   hipError_t e = current_cus(&cus);
   if (e != hipSuccess) return hip_fail(e);
-  e = mtp::launch_pack_tiled_mxfp4(head, V, H, ids, C, tiled_q, tiled_scales, cus, stream);
+  e = mtp::launch_pack_tiled_mxfp4(head, V, H, ids, C, tiled_q, tiled_scales, rule, cus, stream);
   if (e != hipSuccess) return hip_fail(e);
   return MTP_OK;
+}
+
+mtp_status mtp_pack_tiled_mxfp4(const mtp_bf16 *head, int64_t V, int H, const int32_t *ids,
+                                int64_t C, void *tiled_q, size_t q_bytes, uint8_t *tiled_scales,
+                                size_t scale_bytes, hipStream_t stream) {
+  return mtp_pack_tiled_mxfp4_rule(head, V, H, ids, C, tiled_q, q_bytes, tiled_scales,
+                                   scale_bytes, MTP_MX_SCALE_OCP, stream);
 }
 
 mtp_status mtp_draft_argmax_tiled_mxfp4_cfg(const mtp_bf16 *hidden, int M, int H,

@@ -11,6 +11,11 @@
 // share a byte, element 2i in the low nibble; a row is H/2 code bytes and H/32
 // scale bytes.
 //
+// A second scale reading (fit rule, selected per pack call): the smallest e
+// with max |w| <= 6 * 2^e, so that no element of the block saturates; it is
+// one larger than the OCP exponent in blocks whose maximum exceeds 1.5 times
+// its power of two, and the same elsewhere.
+//
 // The pack computes e from the bf16 bits of the block maximum and the code by
 // counting the rounding midpoints below |w| * 2^-e (the ones whose tie goes
 // up, at 0.75, 1.75 and 3.5, counted with >=), in fp32, where the scaling is
@@ -35,13 +40,17 @@ typedef unsigned u32x4_fp4_t __attribute__((ext_vector_type(4)));
 // ---- quantising pack ------------------------------------------------------
 
 // Scale exponent of a block from the bf16 bits of its largest magnitude
-// (0: all-zero block).
-__device__ __forceinline__ int mx_exponent(uint32_t mx) {
+// (0: all-zero block). With amax = sig * 2^(fl - 7), sig the 8-bit
+// significand in [128, 255]: the OCP rule takes fl - 2; the fit rule takes
+// fl - 2 when 6 * 2^(fl - 2) = 1.5 * 2^fl covers amax (sig <= 192), else fl - 1.
+__device__ __forceinline__ int mx_exponent(uint32_t mx, bool fit) {
   if (mx == 0) return -127;
   const int E = (int)(mx >> 7);
   // normal: 2^(E-127) <= amax; subnormal m * 2^-133: highest set bit of m
-  const int fl = E > 0 ? E - 127 : (31 - __builtin_clz(mx & 0x7Fu)) - 133;
-  int e = fl - 2;
+  const int hb = 31 - __builtin_clz((mx & 0x7Fu) | 1u);
+  const int fl = E > 0 ? E - 127 : hb - 133;
+  const int sig = E > 0 ? (int)(0x80u | (mx & 0x7Fu)) : (int)((mx & 0x7Fu) << (7 - hb));
+  int e = fl - 2 + (fit && sig > 192 ? 1 : 0);
   e = e < -127 ? -127 : e;
   return e > 127 ? 127 : e;
 }
@@ -60,7 +69,7 @@ __device__ __forceinline__ uint32_t e2m1_code(uint32_t bits, int e) {
 // [0, V) is written as zero codes with scale code 0.
 __global__ void __launch_bounds__(256)
     pack_mxfp4(const uint4 *__restrict__ head, int64_t V, int H, const int32_t *__restrict__ ids,
-               int64_t C, uint4 *__restrict__ q, uint8_t *__restrict__ scales) {
+               int64_t C, uint4 *__restrict__ q, uint8_t *__restrict__ scales, int fit) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t waves = (int64_t)gridDim.x * (blockDim.x / kWave);
   const int nblk = H / 32;
@@ -86,7 +95,7 @@ __global__ void __launch_bounds__(256)
         mx = lo > mx ? lo : mx;
         mx = hi > mx ? hi : mx;
       }
-      const int e = valid ? mx_exponent(mx) : -127;
+      const int e = valid ? mx_exponent(mx, fit != 0) : -127;
       uint32_t out[4] = {0u, 0u, 0u, 0u};
       if (valid) {
 #pragma unroll
@@ -103,14 +112,15 @@ __global__ void __launch_bounds__(256)
 }
 
 hipError_t launch_pack_mxfp4(const void *head, int64_t V, int H, const int32_t *ids, int64_t C,
-                             void *q, uint8_t *scales, int num_cus, hipStream_t stream) {
+                             void *q, uint8_t *scales, int rule, int num_cus,
+                             hipStream_t stream) {
   const int64_t waves_per_block = 4;
   int64_t blocks = (C + waves_per_block - 1) / waves_per_block;
   const int64_t cap = (int64_t)num_cus * 8;
   if (blocks > cap) blocks = cap;
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL(pack_mxfp4, dim3((unsigned)blocks), dim3(256), 0, stream,
-                     (const uint4 *)head, V, H, ids, C, (uint4 *)q, scales);
+                     (const uint4 *)head, V, H, ids, C, (uint4 *)q, scales, rule);
   return hipGetLastError();
 }
 
@@ -126,7 +136,7 @@ hipError_t launch_pack_mxfp4(const void *head, int64_t V, int H, const int32_t *
 __global__ void __launch_bounds__(256)
     pack_tiled_mxfp4(const uint4 *__restrict__ head, int64_t V, int H,
                      const int32_t *__restrict__ ids, int64_t C, int64_t Cp, int Hp,
-                     uint8_t *__restrict__ tiled, uint8_t *__restrict__ tscales) {
+                     uint8_t *__restrict__ tiled, uint8_t *__restrict__ tscales, int fit) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t waves = (int64_t)gridDim.x * (blockDim.x / kWave);
   const int nblk = H / 32;
@@ -160,7 +170,7 @@ __global__ void __launch_bounds__(256)
           mx = lo > mx ? lo : mx;
           mx = hi > mx ? hi : mx;
         }
-        e = mx_exponent(mx);
+        e = mx_exponent(mx, fit != 0);
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
           const uint32_t byte = e2m1_code(w[k] & 0xFFFFu, e) | (e2m1_code(w[k] >> 16, e) << 4);
@@ -179,8 +189,8 @@ __global__ void __launch_bounds__(256)
 }
 
 hipError_t launch_pack_tiled_mxfp4(const void *head, int64_t V, int H, const int32_t *ids,
-                                   int64_t C, void *tiled, uint8_t *tscales, int num_cus,
-                                   hipStream_t stream) {
+                                   int64_t C, void *tiled, uint8_t *tscales, int rule,
+                                   int num_cus, hipStream_t stream) {
   const int64_t Cp = (C + 63) / 64 * 64;
   const int Hp = (H + 255) / 256 * 256;
   const int64_t waves_per_block = 4;
@@ -189,7 +199,7 @@ hipError_t launch_pack_tiled_mxfp4(const void *head, int64_t V, int H, const int
   if (blocks > cap) blocks = cap;
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL(pack_tiled_mxfp4, dim3((unsigned)blocks), dim3(256), 0, stream,
-                     (const uint4 *)head, V, H, ids, C, Cp, Hp, (uint8_t *)tiled, tscales);
+                     (const uint4 *)head, V, H, ids, C, Cp, Hp, (uint8_t *)tiled, tscales, rule);
   return hipGetLastError();
 }
 

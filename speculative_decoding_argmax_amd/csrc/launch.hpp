@@ -104,8 +104,8 @@ int dma_nb_for_fp4(int M);
 int tiled_cols_fp4(int H);
 hipError_t launch_dma_fp4(const DmaLaunch &L, int nb);
 hipError_t launch_pack_tiled_mxfp4(const void *head, int64_t V, int H, const int32_t *ids,
-                                   int64_t C, void *tiled, uint8_t *tscales, int num_cus,
-                                   hipStream_t stream);
+                                   int64_t C, void *tiled, uint8_t *tscales, int rule,
+                                   int num_cus, hipStream_t stream);
 hipError_t launch_pack_tiled_fp8(const void *head, int64_t V, int H, const int32_t *ids,
                                  int64_t C, void *tiled, float *scales, int num_cus,
                                  hipStream_t stream);
@@ -160,7 +160,8 @@ int fp4_ncl_for(int nblk);
 int fp4_rows_for(int M, int ncl);
 hipError_t launch_fp4(const Fp4Launch &L, int mr, int ncl);
 hipError_t launch_pack_mxfp4(const void *head, int64_t V, int H, const int32_t *ids, int64_t C,
-                             void *q, uint8_t *scales, int num_cus, hipStream_t stream);
+                             void *q, uint8_t *scales, int rule, int num_cus,
+                             hipStream_t stream);
 
 // Streaming-read reference (probe.hip): sink words written per call, at most.
 constexpr int kStreamSinkWords = 8192;

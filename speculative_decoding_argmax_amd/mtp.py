@@ -94,6 +94,7 @@ def _load() -> ctypes.CDLL:
         "mtp_mxfp4_table_bytes": ([I64, I], S),
         "mtp_mxfp4_scale_bytes": ([I64, I], S),
         "mtp_pack_candidates_mxfp4": ([P, I64, I, P, I64, P, P, P], I),
+        "mtp_pack_candidates_mxfp4_rule": ([P, I64, I, P, I64, P, P, I, P], I),
         "mtp_draft_argmax_mxfp4": ([P, I, I, P, P, P, I64, P, P, P, S, P], I),
         "mtp_draft_argmax_mxfp4_cfg": ([P, I, I, P, P, P, I64, P, P, P, S, P, P], I),
         "mtp_draft_argmax_mxfp4_gather": ([P, I, I, P, P, I64, P, I64, P, P, P, S, P], I),
@@ -109,6 +110,7 @@ def _load() -> ctypes.CDLL:
         "mtp_tiled_mxfp4_bytes": ([I64, I], S),
         "mtp_tiled_mxfp4_scale_bytes": ([I64, I], S),
         "mtp_pack_tiled_mxfp4": ([P, I64, I, P, I64, P, S, P, S, P], I),
+        "mtp_pack_tiled_mxfp4_rule": ([P, I64, I, P, I64, P, S, P, S, I, P], I),
         "mtp_draft_argmax_tiled_mxfp4": ([P, I, I, P, P, P, I64, P, P, P, S, P], I),
         "mtp_draft_argmax_tiled_mxfp4_cfg": ([P, I, I, P, P, P, I64, P, P, P, S, P, P], I),
         "mtp_pack_tiled_fp8": ([P, I64, I, P, I64, P, S, P, P], I),
@@ -543,19 +545,25 @@ def mtp_mxfp4_scale_bytes(C: int, H: int) -> int:
     return int(lib.mtp_mxfp4_scale_bytes(C, H))
 
 
+MTP_MX_SCALE_OCP = 0
+MTP_MX_SCALE_FIT = 1
+MX_SCALE_RULES = {"ocp": MTP_MX_SCALE_OCP, "fit": MTP_MX_SCALE_FIT}
+
+
 def mtp_pack_candidates_mxfp4(head, ids, table_q, scales, C: Optional[int] = None,
-                              stream=None) -> None:
+                              stream=None, rule: int = MTP_MX_SCALE_OCP) -> None:
     """Quantise head rows ids (None: the first C rows) to MXFP4: packed E2M1
-    codes table_q [C][H/2] and E8M0 block scales [C][H/32] (both uint8)."""
+    codes table_q [C][H/2] and E8M0 block scales [C][H/32] (both uint8), block
+    scales by the OCP rule or the fit rule (MTP_MX_SCALE_*)."""
     torch = _torch()
     V, H = head.shape
     C = ids.numel() if ids is not None else (V if C is None else C)
     if tuple(table_q.shape) != (C, H // 2) or tuple(scales.shape) != (C, H // 32):
         raise ValueError("table_q must be [C][H/2] and scales [C][H/32]")
-    _check(lib.mtp_pack_candidates_mxfp4(
+    _check(lib.mtp_pack_candidates_mxfp4_rule(
         _ptr(head, "head", _bf16_types()), V, H, _ptr(ids, "ids", (torch.int32,), allow_none=True),
         C, _ptr(table_q, "table_q", (torch.uint8,)), _ptr(scales, "scales", (torch.uint8,)),
-        _stream(stream)), "mtp_pack_candidates_mxfp4")
+        int(rule), _stream(stream)), "mtp_pack_candidates_mxfp4_rule")
 
 
 def mtp_draft_argmax_mxfp4(hidden, table_q, scales, ids, out_ids, out_logit=None, ws=None,
@@ -656,15 +664,15 @@ def alloc_tiled_mxfp4(rows: int, H: int, device=None):
 
 
 def mtp_pack_tiled_mxfp4(head, ids, tiled_q, tiled_scales, C: Optional[int] = None,
-                         stream=None) -> None:
+                         stream=None, rule: int = MTP_MX_SCALE_OCP) -> None:
     torch = _torch()
     V, H = head.shape
     C = ids.numel() if ids is not None else (V if C is None else C)
-    _check(lib.mtp_pack_tiled_mxfp4(
+    _check(lib.mtp_pack_tiled_mxfp4_rule(
         _ptr(head, "head", _bf16_types()), V, H, _ptr(ids, "ids", (torch.int32,), allow_none=True),
         C, _ptr(tiled_q, "tiled_q", (torch.uint8,)), tiled_q.numel(),
         _ptr(tiled_scales, "tiled_scales", (torch.uint8,)), tiled_scales.numel(),
-        _stream(stream)), "mtp_pack_tiled_mxfp4")
+        int(rule), _stream(stream)), "mtp_pack_tiled_mxfp4_rule")
 
 
 def mtp_draft_argmax_tiled_mxfp4(hidden, table_q, tiled_scales, C: int, ids, out_ids,

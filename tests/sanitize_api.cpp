@@ -108,6 +108,9 @@ int main() {
   EXPECT(mtp_pack_candidates_mxfp4(F, 10, 40, FI, 5, FQ, FQ, nullptr) == INV);
   EXPECT(mtp_pack_tiled_fp8(F, 10, 64, nullptr, 10, WS, 8, FL, nullptr) == INV);
   EXPECT(mtp_pack_tiled_mxfp4(F, 10, 64, nullptr, 10, WS, 1 << 20, FQ, 1, nullptr) == INV);
+  EXPECT(mtp_pack_candidates_mxfp4_rule(F, 10, 64, FI, 5, FQ, FQ, 2, nullptr) == INV);
+  EXPECT(mtp_pack_tiled_mxfp4_rule(F, 10, 64, nullptr, 10, WS, 1 << 20, FQ, 1,
+                                   MTP_MX_SCALE_FIT, nullptr) == INV);
   EXPECT(mtp_workspace_init(WS, 12, nullptr) == INV);
   EXPECT(mtp_workspace_init(nullptr, 64, nullptr) == INV);
   uint32_t *SINK = reinterpret_cast<uint32_t *>(uintptr_t(0x10000));

@@ -320,6 +320,12 @@ def test_mxfp4_entry_points_reject_bad_arguments():
     assert p(*ok[:3], None, 101, *ok[5:]) == INVALID     # C > V without ids
     assert p(*ok[:5], P(0x10008), *ok[6:]) == INVALID    # codes not 16-byte aligned
     assert p(*ok[:6], None, None) == INVALID             # no scales
+    r = mtp.lib.mtp_pack_candidates_mxfp4_rule
+    okr = ok[:7] + (mtp.MTP_MX_SCALE_FIT, None)
+    assert r(None, *okr[1:]) == INVALID
+    assert r(*okr[:2], 48, *okr[3:]) == INVALID          # H % 32
+    assert r(*okr[:7], 2, None) == INVALID               # no such scale rule
+    assert r(*okr[:7], -1, None) == INVALID
     d = mtp.lib.mtp_draft_argmax_mxfp4
     dk = (FAKE, 1, 64, FAKE, FAKE, None, 100, FAKE, None, FAKE, 4096, None)
     assert d(*dk[:2], 48, *dk[3:]) == INVALID
@@ -346,6 +352,11 @@ def test_tiled_mxfp4_entry_points_reject_bad_arguments():
     assert p(*ok[:8], ns - 1, None) == INVALID                  # scale buffer too small
     assert p(*ok[:7], None, ns, None) == INVALID                # no scales
     assert p(*ok[:5], P(0x10008), *ok[6:]) == INVALID           # codes not 16-byte aligned
+    r = mtp.lib.mtp_pack_tiled_mxfp4_rule
+    okr = ok[:9] + (mtp.MTP_MX_SCALE_OCP, None)
+    assert r(None, *okr[1:]) == INVALID
+    assert r(*okr[:6], nq - 1, *okr[7:]) == INVALID             # codes buffer too small
+    assert r(*okr[:9], 3, None) == INVALID                      # no such scale rule
     d = mtp.lib.mtp_draft_argmax_tiled_mxfp4
     dk = (FAKE, 1, 64, FAKE, FAKE, None, 100, FAKE, None, FAKE, 4096, None)
     assert d(*dk[:2], 48, *dk[3:]) == INVALID
