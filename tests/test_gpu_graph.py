@@ -117,9 +117,10 @@ def _equal(a, b):
                                   y.view(np.uint32) if y.dtype == np.float32 else y), k
 
 
-# (True, 160): wide tiled drafts, two kernels per call (hidden pack, then the
-# register-ring kernel) recorded into the graph
-@pytest.mark.parametrize("tiled,M", [(False, 1), (False, B), (True, 8), (True, 160)])
+# (True, 160) and (False, 160): wide drafts on a tiled table and on row-major
+# rows, two kernels per call (hidden pack into the workspace's staging area,
+# then the register-ring kernel) recorded into the graph
+@pytest.mark.parametrize("tiled,M", [(False, 1), (False, B), (True, 8), (True, 160), (False, 160)])
 def test_graph_replays_equal_eager(torch, mtp, tiled, M):
     head = wl.head_weights(V, H, 9101)
     ids = wl.candidate_ids(V, C, 9101)
