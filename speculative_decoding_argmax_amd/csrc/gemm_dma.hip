@@ -665,7 +665,6 @@ __global__ void __launch_bounds__(WV * 64)
   };
   auto issue_a = [&](auto tag) __attribute__((always_inline)) {
     constexpr int SL = decltype(tag)::value;
-    const int tile = a_t;
     const int c = a_c;
     if constexpr (RM) {
       const __amdgpu_buffer_rsrc_t r = a_rs;
@@ -682,9 +681,9 @@ __global__ void __launch_bounds__(WV * 64)
           ar[SL][h][rw] = make_uint4(v.x, v.y, v.z, v.w);
         }
       }
-      (void)tile;
       return;
     }
+    const int tile = a_t;
     if (++a_c == nchunks) {
       a_c = 0;
       a_t += gdx;
