@@ -655,6 +655,21 @@ __global__ void __launch_bounds__(WV * 64)
         0x00020000);
   };
   __amdgpu_buffer_rsrc_t a_rs = rm_rsrc(bx);
+  // tiled: one descriptor per tile over this wave's 64-row groups (groups
+  // past the table read zeros, never reported); a chunk's fragments sit at
+  // the chunk's scalar offset (c * KS + s) * 4 KiB plus a fixed lane offset,
+  // so the loads need no per-load address arithmetic (the tiled ring ran
+  // about 3% faster than with 64-bit addresses per load, same-box A/B)
+  auto t_rsrc = [&](int tile) __attribute__((always_inline)) {
+    const int64_t g0 = (int64_t)tile * (RBT / 4) + wave * (RW / 4);
+    const int64_t left = ((int64_t)(nrb / 4) - g0) * S * 4096;
+    const int64_t span = (int64_t)((RW + 3) / 4) * S * 4096;
+    const int64_t n = left < span ? left : span;
+    const int nrec = n <= 0 ? 0 : n > 0x7FFFFFFF ? 0x7FFFFFFF : (int)n;
+    return __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(reinterpret_cast<const char *>(WT) + g0 * S * 4096), (short)0, nrec, 0x00020000);
+  };
+  __amdgpu_buffer_rsrc_t t_rs = t_rsrc(bx);
   // keep `own` in lanes 0..7 (swap_hi) or 8..15 (swap_lo) of each 16-lane
   // row and take the other half from `other` rotated by 8 lanes (row_ror:8)
   auto swap_hi = [](uint32_t own, uint32_t other) __attribute__((always_inline)) -> uint32_t {
@@ -683,20 +698,18 @@ __global__ void __launch_bounds__(WV * 64)
       }
       return;
     }
-    const int tile = a_t;
+    const __amdgpu_buffer_rsrc_t r = t_rs;
     if (++a_c == nchunks) {
       a_c = 0;
       a_t += gdx;
+      t_rs = t_rsrc(a_t);
     }
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
 #pragma unroll
       for (int rw = 0; rw < RW; ++rw) {
-        int rb = tile * RBT + wave * RW + rw;
-        rb = rb < nrb ? rb : nrb - 1;            // past the table: valid, never reported
-        const uint4 *src =
-            WT + (((int64_t)(rb >> 2) * S + c * KS + s) * 4 + (rb & 3)) * kWave + lane;
-        const u32x4_ring_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_ring_t *>(src));
+        const u32x4_ring_t v = __builtin_amdgcn_raw_buffer_load_b128(
+            r, lane * 16 + (rw / 4) * S * 4096 + (rw % 4) * 1024, (c * KS + s) * 4096, CP);
         ar[SL][s][rw] = make_uint4(v.x, v.y, v.z, v.w);
       }
     }
