@@ -115,14 +115,23 @@ mtp_status mtp_validate_ids(const int32_t *ids_host, int64_t C, int64_t V);
 
 /* Bytes of workspace needed by mtp_draft_argmax for M hidden rows, and by
  * mtp_verify_accept for B sequences with k drafts each (the same sizes serve
- * every variant of these calls; with M or B*(k+1) above 128 they include a
- * staging area of about M*H*2 bytes for the packed hidden block, placed past
- * 33 KiB of counters). 0 for arguments out of range. A tiled call with more
- * than 128 hidden rows returns MTP_ERR_WORKSPACE when given less. A row-major
- * call needs only the counters (256 + 8*M bytes, rounded up to 256): given
- * the full size, its passes of more than 128 rows (H % 64 == 0) run the
- * register-ring matrix-core kernel, given less the LDS-fed one; both sum
- * every logit in the same order, so the results are the same bits. */
+ * every variant of these calls). 0 for arguments out of range.
+ *   - Counters: 256 bytes of header and 8 regions of 64 + 8*M bytes, each
+ *     rounded up to 256 (2,304 bytes at M = 1). Launches whose workgroups
+ *     each stream less than 384 KiB of the table spread the cross-workgroup
+ *     finish over the 8 regions (a grouped finish: 8 group tickets and key
+ *     sets, so that hundreds of workgroups arriving together do not queue
+ *     on one address). Every call accepts the counters' least size, 256 +
+ *     8*M bytes rounded up to 256, and then runs the one-level finish; the
+ *     winner is the same either way.
+ *   - With M or B*(k+1) above 128 the size includes a staging area of about
+ *     M*H*2 bytes for the packed hidden block, placed past the counters of
+ *     the largest call (MTP_MAX_ROWS rows, 264,448 bytes). A tiled call with
+ *     more than 128 hidden rows returns MTP_ERR_WORKSPACE when given less. A
+ *     row-major call given the full size runs its passes of more than 128
+ *     rows (H % 64 == 0) on the register-ring matrix-core kernel, given less
+ *     on the LDS-fed one; both sum every logit in the same order, so the
+ *     results are the same bits. */
 size_t mtp_draft_workspace_bytes(int M, int64_t C, int H);
 size_t mtp_verify_workspace_bytes(int B, int k, int64_t V, int H);
 

@@ -48,9 +48,34 @@ hipError_t current_cus(int *cus) {
   return hipSuccess;
 }
 
+// Workspace of a call with M hidden rows: the ticket header and the regions
+// of the grouped finish (which also hold the one-level finish's M keys).
 size_t rows_workspace_bytes(int64_t M) {
+  return mtp::kWsHeader + (size_t)mtp::kFinishGroups * mtp::finish_group_stride(M);
+}
+
+// The least a call accepts: the ticket header and M keys (one-level finish).
+size_t min_rows_workspace_bytes(int64_t M) {
   const size_t keys = (size_t)M * 8;
   return mtp::kWsHeader + ((keys + 255) / 256) * 256;
+}
+
+// The grouped finish, when the workspace holds its regions and each
+// workgroup of the launch streams less than kGroupedFinishBytes of the table:
+// such workgroups reach the finish within a few microseconds of each other,
+// and hundreds of same-address atomics then queue (measured on MI355X,
+// same-box A/B: MXFP4 M = 1 drafts at 32,768 and 65,536 x 2,048 rows 13.9 ->
+// 10.4 and 18.2 -> 15.6 us, bf16 at 16,384 rows 14.7 -> 13.7 us, fp8 at
+// 32,768 rows 15.3 -> 14.5 us; at 1 MiB and more per workgroup the extra
+// round trip cost 0.3-0.7 us, e.g. the bf16 65,536-row draft 40.6 -> 41.3).
+constexpr double kGroupedFinishBytes = 384.0 * 1024.0;
+
+void choose_finish(mtp::RowSink &s, size_t ws_bytes, double table_bytes, int64_t workgroups) {
+  if (ws_bytes >= rows_workspace_bytes(s.M) && workgroups > 0 &&
+      table_bytes / (double)workgroups < kGroupedFinishBytes) {
+    s.groups = mtp::kFinishGroups;
+    s.gstride = (uint32_t)mtp::finish_group_stride(s.M);
+  }
 }
 
 // Tiled calls with more than 128 hidden rows also stage the packed hidden
@@ -101,8 +126,10 @@ mtp_status check_cfg(const mtp_config *cfg) {
 // Gathered candidates (gather_ids != nullptr: candidate i is head row
 // gather_ids[i]) run on the vector-ALU kernel only.
 mtp_status run_rows(const mtp_bf16 *X, int M, int H, const mtp_bf16 *W, int64_t N,
-                    mtp::RowSink sink, hipStream_t stream, const mtp_config *cfg, void *stage,
-                    const int32_t *gather_ids = nullptr, int64_t gather_V = 0) {
+                    mtp::RowSink sink, size_t ws_bytes, hipStream_t stream,
+                    const mtp_config *cfg, void *stage, const int32_t *gather_ids = nullptr,
+                    int64_t gather_V = 0) {
+  const double table_bytes = (double)N * H * 2;
   const int nch = H / 8;
   const int ncl = mtp::valu_ncl_for(nch);
   int path = cfg ? cfg->path : MTP_PATH_AUTO;
@@ -121,6 +148,7 @@ mtp_status run_rows(const mtp_bf16 *X, int M, int H, const mtp_bf16 *W, int64_t 
     // (prefetching variant; measured best on MI355X at the workload shapes)
     const int per_cu =
         (cfg && cfg->blocks_per_cu > 0) ? cfg->blocks_per_cu : (ncl <= 5 ? 1 : 2);
+    choose_finish(sink, ws_bytes, table_bytes, (int64_t)per_cu * cus);
     mtp::ValuLaunch L;
     L.X = X;
     L.W = W;
@@ -137,6 +165,7 @@ mtp_status run_rows(const mtp_bf16 *X, int M, int H, const mtp_bf16 *W, int64_t 
   } else if (mtp::dma_rm_ok(H)) {
     // matrix cores fed by LDS DMA straight from the row-major rows
     const int per_cu = (cfg && cfg->blocks_per_cu > 0) ? cfg->blocks_per_cu : 1;
+    choose_finish(sink, ws_bytes, table_bytes, (int64_t)per_cu * cus);
     mtp::DmaLaunch L;
     L.X = X;
     L.WT = W;
@@ -155,6 +184,7 @@ mtp_status run_rows(const mtp_bf16 *X, int M, int H, const mtp_bf16 *W, int64_t 
   } else {
     // widths that are not a multiple of 64: register-staged matrix-core kernel
     const int per_cu = (cfg && cfg->blocks_per_cu > 0) ? cfg->blocks_per_cu : 2;
+    choose_finish(sink, ws_bytes, table_bytes, (int64_t)per_cu * cus);
     mtp::MfmaLaunch L;
     L.X = X;
     L.W = W;
@@ -176,11 +206,14 @@ mtp_status run_rows_tiled(const mtp_bf16 *X, int M, int H, const void *WT, int64
                           const mtp_config *cfg) {
   if (cfg && cfg->path == MTP_PATH_VALU) return MTP_ERR_UNSUPPORTED;
   const bool stage = mtp::ring_stage_bytes(M, H) != 0;
-  if (ws_bytes < call_workspace_bytes(M, H)) return MTP_ERR_WORKSPACE;
+  if (ws_bytes < (stage ? call_workspace_bytes(M, H) : min_rows_workspace_bytes(M)))
+    return MTP_ERR_WORKSPACE;
   int cus = 0;
   hipError_t e = current_cus(&cus);
   if (e != hipSuccess) return hip_fail(e);
   const int per_cu = (cfg && cfg->blocks_per_cu > 0) ? cfg->blocks_per_cu : 1;
+  choose_finish(sink, ws_bytes, (double)mtp::tiled_rows(N) * mtp::tiled_cols(H) * 2,
+                (int64_t)per_cu * cus);
   mtp::DmaLaunch L;
   L.X = X;
   L.WT = WT;
@@ -214,7 +247,7 @@ mtp_status check_draft_args(const mtp_bf16 *hidden, int M, int H, const void *ta
   mtp_status st = check_cfg(cfg);
   if (st != MTP_OK) return st;
   if (!ws || !aligned(ws, 8)) return MTP_ERR_WORKSPACE;
-  if (ws_bytes < rows_workspace_bytes(M)) return MTP_ERR_WORKSPACE;
+  if (ws_bytes < min_rows_workspace_bytes(M)) return MTP_ERR_WORKSPACE;
   return MTP_OK;
 }
 
@@ -223,6 +256,8 @@ mtp::RowSink draft_sink(void *ws, const int32_t *ids, int32_t *out_ids, float *o
   std::memset(&s, 0, sizeof s);
   s.ticket = (uint32_t *)ws;
   s.keys = (unsigned long long *)((char *)ws + mtp::kWsHeader);
+  s.groups = 1;
+  s.gstride = 0;
   s.ids = ids;
   s.out_ids = out_ids;
   s.out_logit = out_logit;
@@ -261,7 +296,7 @@ mtp_status check_verify_args(const mtp_bf16 *hidden, int B, int k, int H, const 
   st = check_cfg(cfg);
   if (st != MTP_OK) return st;
   if (!ws || !aligned(ws, 8)) return MTP_ERR_WORKSPACE;
-  if (ws_bytes < rows_workspace_bytes(M)) return MTP_ERR_WORKSPACE;
+  if (ws_bytes < min_rows_workspace_bytes(M)) return MTP_ERR_WORKSPACE;
   return MTP_OK;
 }
 
@@ -271,6 +306,8 @@ mtp::RowSink verify_sink(void *ws, int B, int k, const int32_t *draft, int32_t *
   std::memset(&s, 0, sizeof s);
   s.ticket = (uint32_t *)ws;
   s.keys = (unsigned long long *)((char *)ws + mtp::kWsHeader);
+  s.groups = 1;
+  s.gstride = 0;
   s.ids = nullptr;
   s.out_ids = out_argmax;
   s.out_logit = out_logit;
@@ -399,8 +436,8 @@ mtp_status mtp_draft_argmax_cfg(const mtp_bf16 *hidden, int M, int H, const mtp_
   mtp_status st =
       check_draft_args(hidden, M, H, table, ids, C, out_ids, out_logit, ws, ws_bytes, cfg);
   if (st != MTP_OK) return st;
-  return run_rows(hidden, M, H, table, C, draft_sink(ws, ids, out_ids, out_logit, M), stream,
-                  cfg, rows_stage(ws, ws_bytes, M, H));
+  return run_rows(hidden, M, H, table, C, draft_sink(ws, ids, out_ids, out_logit, M), ws_bytes,
+                  stream, cfg, rows_stage(ws, ws_bytes, M, H));
 }
 
 mtp_status mtp_draft_argmax(const mtp_bf16 *hidden, int M, int H, const mtp_bf16 *table,
@@ -420,7 +457,7 @@ mtp_status mtp_verify_accept_cfg(const mtp_bf16 *hidden, int B, int k, int H,
   if (st != MTP_OK) return st;
   return run_rows(hidden, B * (k + 1), H, head, V,
                   verify_sink(ws, B, k, draft, out_argmax, out_logit, out_accept, out_tokens),
-                  stream, cfg, rows_stage(ws, ws_bytes, (int64_t)B * (k + 1), H));
+                  ws_bytes, stream, cfg, rows_stage(ws, ws_bytes, (int64_t)B * (k + 1), H));
 }
 
 mtp_status mtp_verify_accept(const mtp_bf16 *hidden, int B, int k, int H, const mtp_bf16 *head,
@@ -446,11 +483,13 @@ mtp_status mtp_verify_accept_noalloc(const mtp_bf16 *hidden, int B, int k, int H
   // The array keeps whatever the last call on this device left in it: clear
   // the ticket and this call's keys first (a kernel, stream-ordered before
   // the verify kernels; no hipMemsetAsync).
-  const size_t used = rows_workspace_bytes(M);
+  const size_t used = min_rows_workspace_bytes(M);
   e = mtp::launch_fill_zero(ws, used, stream);
   if (e != hipSuccess) return hip_fail(e);
+  // one-level finish (no workspace size given): the array holds the ticket
+  // and the keys only
   return run_rows(hidden, B * (k + 1), H, head, V,
-                  verify_sink(ws, B, k, draft, out_argmax, out_logit, out_accept, out_tokens),
+                  verify_sink(ws, B, k, draft, out_argmax, out_logit, out_accept, out_tokens), 0,
                   stream, nullptr, nullptr);
 }
 
@@ -530,8 +569,8 @@ mtp_status mtp_draft_argmax_gather_cfg(const mtp_bf16 *hidden, int M, int H,
       check_draft_args(hidden, M, H, head, ids, C, out_ids, out_logit, ws, ws_bytes, cfg);
   if (st != MTP_OK) return st;
   // the key of a gathered candidate is its id, so the finish needs no id map
-  return run_rows(hidden, M, H, head, C, draft_sink(ws, nullptr, out_ids, out_logit, M), stream,
-                  cfg, nullptr, ids, V);
+  return run_rows(hidden, M, H, head, C, draft_sink(ws, nullptr, out_ids, out_logit, M), ws_bytes,
+                  stream, cfg, nullptr, ids, V);
 }
 
 mtp_status mtp_draft_argmax_gather(const mtp_bf16 *hidden, int M, int H, const mtp_bf16 *head,
@@ -598,6 +637,7 @@ static mtp_status run_fp8(const mtp_bf16 *hidden, int M, int H, const uint8_t *t
   L.max_blocks_x = per_cu * cus;
   // gathered candidates are keyed by id: the finish needs no id map
   L.sink = draft_sink(ws, gather_ids ? nullptr : ids, out_ids, out_logit, M);
+  choose_finish(L.sink, ws_bytes, (double)C * (H + 4), (int64_t)per_cu * cus);
   L.stream = stream;
   L.gather_ids = gather_ids;
   L.gather_V = gather_V;
@@ -710,6 +750,7 @@ static mtp_status run_mxfp4(const mtp_bf16 *hidden, int M, int H, const uint8_t 
   L.max_blocks_x = per_cu * cus;
   // gathered candidates are keyed by id: the finish needs no id map
   L.sink = draft_sink(ws, gather_ids ? nullptr : ids, out_ids, out_logit, M);
+  choose_finish(L.sink, ws_bytes, (double)C * (H / 2 + H / 32), (int64_t)per_cu * cus);
   L.stream = stream;
   L.gather_ids = gather_ids;
   L.gather_V = gather_V;
@@ -819,6 +860,7 @@ mtp_status mtp_draft_argmax_tiled_mxfp4_cfg(const mtp_bf16 *hidden, int M, int H
   L.S = mtp::tiled_cols_fp4(H) / 32;
   L.max_blocks_x = per_cu * cus;
   L.sink = draft_sink(ws, ids, out_ids, out_logit, M);
+  choose_finish(L.sink, ws_bytes, (double)C * (H / 2 + H / 32), (int64_t)per_cu * cus);
   L.stream = stream;
   L.scales = reinterpret_cast<const float *>(tiled_scales);
   e = mtp::launch_dma_fp4(L, nb);
@@ -881,6 +923,7 @@ mtp_status mtp_draft_argmax_tiled_fp8_cfg(const mtp_bf16 *hidden, int M, int H,
   L.S = mtp::tiled_cols(H) / 32;
   L.max_blocks_x = per_cu * cus;
   L.sink = draft_sink(ws, ids, out_ids, out_logit, M);
+  choose_finish(L.sink, ws_bytes, (double)C * (H + 4), (int64_t)per_cu * cus);
   L.stream = stream;
   L.scales = scales;
   e = mtp::launch_dma_fp8(L, mtp::dma_nb_for_fp8(M));

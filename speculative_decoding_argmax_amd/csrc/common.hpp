@@ -10,7 +10,9 @@
 //  * the cross-workgroup finish: each workgroup merges its per-row winners
 //    into the workspace keys, and the last workgroup to arrive (ticket)
 //    decodes them, writes the outputs, runs greedy acceptance for verify,
-//    and clears the workspace for the next call.
+//    and clears the workspace for the next call. Launches whose workgroups
+//    reach the finish together spread its keys and counters over
+//    kFinishGroups regions of the workspace (grouped finish).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -23,8 +25,17 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 constexpr int kWave = 64;
 
 // Workspace layout: [0, 256) ticket (uint32 at offset 0), then one 64-bit key
-// per hidden row.
+// per hidden row. The grouped finish uses instead kFinishGroups regions of
+// finish_group_stride(M) bytes from offset kWsHeader on: region g holds group
+// g's counter (uint32 at its offset 0) and, from offset 64, its M keys.
 constexpr size_t kWsHeader = 256;
+constexpr int kFinishGroups = 8;
+
+// Bytes per group region: the counter's 64 bytes and M keys, rounded up to
+// 256 so that every group's counter and keys lie in lines of their own.
+__host__ __device__ constexpr size_t finish_group_stride(int64_t M) {
+  return ((64 + (size_t)M * 8 + 255) / 256) * 256;
+}
 
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
@@ -91,6 +102,8 @@ __device__ __forceinline__ unsigned long long make_key(float v, uint32_t row) {
 struct RowSink {
   uint32_t *ticket;          // workspace + 0
   unsigned long long *keys;  // workspace + kWsHeader, one per hidden row
+  int groups;                // 1, or kFinishGroups for the grouped finish
+  uint32_t gstride;          // grouped finish: finish_group_stride(M)
   const int32_t *ids;        // row -> token id, or nullptr for identity
   int32_t *out_ids;          // [M]
   float *out_logit;          // [M] or nullptr
@@ -101,6 +114,98 @@ struct RowSink {
   int32_t *out_accept;       // [B]
   int32_t *out_tokens;       // [B][k+1]
 };
+
+// Writes the outputs of every hidden row from its final key (0: no
+// candidate) and, for verify, runs greedy acceptance; the last workgroup
+// calls it once every key is final.
+__device__ __forceinline__ void finish_outputs(const RowSink &s, int m,
+                                               unsigned long long key) {
+  int32_t id = -1;
+  float val = __builtin_nanf("");
+  if (key != 0ull) {
+    const uint32_t row = ~(uint32_t)(key & 0xFFFFFFFFull);
+    val = unorder_bits((uint32_t)(key >> 32));
+    id = s.ids ? s.ids[row] : (int32_t)row;
+  }
+  s.out_ids[m] = id;
+  if (s.out_logit) s.out_logit[m] = val;
+}
+
+__device__ __forceinline__ void finish_accept(const RowSink &s) {
+  if (s.k >= 0) {
+    __syncthreads();  // out_ids (the target argmax) written by this workgroup
+    const int k = s.k;
+    for (int b = threadIdx.x; b < s.B; b += blockDim.x) {
+      const int32_t *t = s.out_ids + (int64_t)b * (k + 1);
+      int n = 0;
+      while (n < k && s.draft[(int64_t)b * k + n] == t[n]) ++n;
+      s.out_accept[b] = n;
+      for (int p = 0; p <= k; ++p) s.out_tokens[(int64_t)b * (k + 1) + p] = p <= n ? t[p] : -1;
+    }
+  }
+  if (threadIdx.x == 0)
+    __hip_atomic_exchange(s.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The grouped finish (see finish_rows). The group count is a constant, so
+// the last workgroup issues its G key reads per row back to back.
+__device__ __forceinline__ void finish_rows_grouped(const RowSink &s, const float *wg_val,
+                                                 const int64_t *wg_row, int m_begin,
+                                                 int m_count) {
+  __shared__ int s_last;
+  __shared__ int s_seen;
+  constexpr uint32_t G = kFinishGroups;
+  const int tid = threadIdx.x;
+  const int nthreads = blockDim.x;
+  const uint32_t bid = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+  const uint32_t g = bid % G;
+  char *const groups = reinterpret_cast<char *>(s.ticket) + kWsHeader;
+  unsigned long long *const keys =
+      reinterpret_cast<unsigned long long *>(groups + (size_t)g * s.gstride + 64);
+  if (tid == 0) s_seen = 0;
+  __syncthreads();
+  for (int t = tid; t < m_count; t += nthreads) {
+    if (wg_row[t] >= 0) {
+      const unsigned long long key = make_key(wg_val[t], (uint32_t)wg_row[t]);
+      const unsigned long long old = __hip_atomic_fetch_max(&keys[m_begin + t], key,
+                                                            __ATOMIC_RELAXED,
+                                                            __HIP_MEMORY_SCOPE_AGENT);
+      if (old >= key) s_seen = 1;  // consumes the returned value
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t nblocks = gridDim.x * gridDim.y * gridDim.z;
+    uint32_t *const gt = reinterpret_cast<uint32_t *>(groups + (size_t)g * s.gstride);
+    const uint32_t gsize = nblocks / G + (g < nblocks % G ? 1u : 0u);
+    const uint32_t ngroups = nblocks < G ? nblocks : G;
+    const uint32_t pg = __hip_atomic_fetch_add(gt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    int last = 0;
+    if (pg == gsize - 1) {
+      // every workgroup of the group has counted: reset its counter
+      __hip_atomic_exchange(gt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t prev =
+          __hip_atomic_fetch_add(s.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      last = prev == ngroups - 1;
+    }
+    s_last = last;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  for (int m = tid; m < s.M; m += nthreads) {
+    unsigned long long key = 0ull;
+#pragma unroll
+    for (uint32_t q = 0; q < G; ++q) {
+      unsigned long long *const kq =
+          reinterpret_cast<unsigned long long *>(groups + (size_t)q * s.gstride + 64);
+      const unsigned long long v =
+          __hip_atomic_exchange(&kq[m], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      key = v > key ? v : key;
+    }
+    finish_outputs(s, m, key);
+  }
+  finish_accept(s);
+}
 
 // Called by every thread of every workgroup after the workgroup's per-row
 // winners for rows [m_begin, m_begin + m_count) sit in wg_val / wg_row
@@ -114,8 +219,21 @@ struct RowSink {
 // returned value feeds an LDS write), and only then does one thread take a
 // ticket; the last ticket holder reads the keys with atomic exchanges, which
 // also clear them for the next call.
+//
+// Grouped finish (s.groups > 1): workgroup b updates the keys of group
+// b mod G and takes that group's ticket; the last workgroup of each group
+// takes the call's ticket, and the last of those reads every group's keys.
+// Same-address atomics are performed one after another, so when hundreds of
+// workgroups arrive together the single ticket and key queue up; G groups in
+// separate lines split the queue at the cost of one more dependent round
+// trip. It is a function of its own so that the one-level path keeps its
+// code (reading the grid size where it did, inside the ticket branch).
 __device__ __forceinline__ void finish_rows(const RowSink &s, const float *wg_val,
                                             const int64_t *wg_row, int m_begin, int m_count) {
+  if (s.groups > 1) {
+    finish_rows_grouped(s, wg_val, wg_row, m_begin, m_count);
+    return;
+  }
   __shared__ int s_last;
   __shared__ int s_seen;
   const int tid = threadIdx.x;
@@ -140,31 +258,10 @@ __device__ __forceinline__ void finish_rows(const RowSink &s, const float *wg_va
   }
   __syncthreads();
   if (!s_last) return;
-  for (int m = tid; m < s.M; m += nthreads) {
-    const unsigned long long key =
-        __hip_atomic_exchange(&s.keys[m], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    int32_t id = -1;
-    float val = __builtin_nanf("");
-    if (key != 0ull) {
-      const uint32_t row = ~(uint32_t)(key & 0xFFFFFFFFull);
-      val = unorder_bits((uint32_t)(key >> 32));
-      id = s.ids ? s.ids[row] : (int32_t)row;
-    }
-    s.out_ids[m] = id;
-    if (s.out_logit) s.out_logit[m] = val;
-  }
-  if (s.k >= 0) {
-    __syncthreads();  // out_ids (the target argmax) written by this workgroup
-    const int k = s.k;
-    for (int b = tid; b < s.B; b += nthreads) {
-      const int32_t *t = s.out_ids + (int64_t)b * (k + 1);
-      int n = 0;
-      while (n < k && s.draft[(int64_t)b * k + n] == t[n]) ++n;
-      s.out_accept[b] = n;
-      for (int p = 0; p <= k; ++p) s.out_tokens[(int64_t)b * (k + 1) + p] = p <= n ? t[p] : -1;
-    }
-  }
-  if (tid == 0) __hip_atomic_exchange(s.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int m = tid; m < s.M; m += nthreads)
+    finish_outputs(
+        s, m, __hip_atomic_exchange(&s.keys[m], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  finish_accept(s);
 }
 
 }  // namespace mtp

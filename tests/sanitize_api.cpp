@@ -36,7 +36,7 @@ int main() {
   EXPECT(mtp_last_hip_error() == 0);
 
   // size queries at their limits
-  EXPECT(mtp_draft_workspace_bytes(1, 65536, 2048) == 512);
+  EXPECT(mtp_draft_workspace_bytes(1, 65536, 2048) == 2304);
   EXPECT(mtp_draft_workspace_bytes(MTP_MAX_ROWS, 1, 8) > 0);
   EXPECT(mtp_draft_workspace_bytes(MTP_MAX_ROWS + 1, 1, 8) == 0);
   EXPECT(mtp_draft_workspace_bytes(1, INT64_MAX, 8) == 0);

@@ -37,15 +37,29 @@ def test_validate_ids():
     assert mtp.lib.mtp_validate_ids(None, 3, 10) == mtp.MTP_ERR_INVALID_ARG
 
 
+def counters(M):
+    """Header and the grouped finish's 8 regions (64 bytes of group ticket,
+    then M keys, rounded up to 256 bytes each)."""
+    return 256 + 8 * (-(-(64 + 8 * M) // 256) * 256)
+
+
+def least_counters(M):
+    """The least workspace a call accepts: header and M keys (one-level
+    finish)."""
+    return 256 + -(-M * 8 // 256) * 256
+
+
 def test_workspace_sizes():
-    assert mtp.mtp_draft_workspace_bytes(1, 65536, 2048) == 512
-    assert mtp.mtp_draft_workspace_bytes(32, 65536, 5120) == 512
-    assert mtp.mtp_draft_workspace_bytes(33, 65536, 5120) == 768
+    assert mtp.mtp_draft_workspace_bytes(1, 65536, 2048) == 2304 == counters(1)
+    assert mtp.mtp_draft_workspace_bytes(24, 65536, 5120) == 2304
+    assert mtp.mtp_draft_workspace_bytes(25, 65536, 5120) == 4352 == counters(25)
+    assert mtp.mtp_draft_workspace_bytes(128, 65536, 5120) == counters(128) == 10496
     # 160 rows: the counters of the largest call, then the tiled calls'
     # staging area (see below)
+    assert counters(4096) == 264448
     assert mtp.mtp_verify_workspace_bytes(32, 4, 248320, 5120) == \
-        256 + 4096 * 8 + 160 * 10 * 1024 + 256
-    assert mtp.mtp_verify_workspace_bytes(1, 0, 10, 8) == 512
+        counters(4096) + 160 * 10 * 1024 + 256
+    assert mtp.mtp_verify_workspace_bytes(1, 0, 10, 8) == counters(1)
     for bad in ((0, 10, 8), (1, 0, 8), (1, 10, 12), (1, 10, 4), (4097, 10, 8), (1, 10, 16392)):
         assert mtp.mtp_draft_workspace_bytes(*bad) == 0, bad
     assert mtp.mtp_verify_workspace_bytes(1, 16, 10, 8) == 0
@@ -290,7 +304,6 @@ def test_wide_tiled_calls_need_the_staging_area():
     256 bytes of alignment slack) past the counters of the largest possible
     call, and a tiled call given only the counters' size is refused before
     anything is enqueued."""
-    counters = lambda M: 256 + -(-M * 8 // 256) * 256
     assert mtp.mtp_draft_workspace_bytes(128, 1000, 5120) == counters(128)
     base = counters(4096)
     stage160 = (5120 // 32) * 10 * 1024 + 256
