@@ -74,7 +74,6 @@ void choose_finish(mtp::RowSink &s, size_t ws_bytes, double table_bytes, int64_t
   if (ws_bytes >= rows_workspace_bytes(s.M) && workgroups > 0 &&
       table_bytes / (double)workgroups < kGroupedFinishBytes) {
     s.groups = mtp::kFinishGroups;
-    s.gstride = (uint32_t)mtp::finish_group_stride(s.M);
   }
 }
 
@@ -257,7 +256,6 @@ mtp::RowSink draft_sink(void *ws, const int32_t *ids, int32_t *out_ids, float *o
   s.ticket = (uint32_t *)ws;
   s.keys = (unsigned long long *)((char *)ws + mtp::kWsHeader);
   s.groups = 1;
-  s.gstride = 0;
   s.ids = ids;
   s.out_ids = out_ids;
   s.out_logit = out_logit;
@@ -307,7 +305,6 @@ mtp::RowSink verify_sink(void *ws, int B, int k, const int32_t *draft, int32_t *
   s.ticket = (uint32_t *)ws;
   s.keys = (unsigned long long *)((char *)ws + mtp::kWsHeader);
   s.groups = 1;
-  s.gstride = 0;
   s.ids = nullptr;
   s.out_ids = out_argmax;
   s.out_logit = out_logit;

@@ -99,21 +99,25 @@ __device__ __forceinline__ unsigned long long make_key(float v, uint32_t row) {
   return ((unsigned long long)order_bits(v) << 32) | (unsigned long long)(~row);
 }
 
+// A kernel argument of every row kernel: its size is kept at 80 bytes (the
+// group count sits in the padding after k), since some kernels already use
+// every scalar register and a larger argument made the compiler reload
+// arguments and drain the loads in flight inside their main loop.
 struct RowSink {
   uint32_t *ticket;          // workspace + 0
   unsigned long long *keys;  // workspace + kWsHeader, one per hidden row
-  int groups;                // 1, or kFinishGroups for the grouped finish
-  uint32_t gstride;          // grouped finish: finish_group_stride(M)
   const int32_t *ids;        // row -> token id, or nullptr for identity
   int32_t *out_ids;          // [M]
   float *out_logit;          // [M] or nullptr
   int M;
   // verify only (k < 0 for draft)
   int B, k;
+  int groups;                // 1, or kFinishGroups for the grouped finish
   const int32_t *draft;      // [B][k]
   int32_t *out_accept;       // [B]
   int32_t *out_tokens;       // [B][k+1]
 };
+static_assert(sizeof(RowSink) == 80, "kept at 80 bytes (see above)");
 
 // Writes the outputs of every hidden row from its final key (0: no
 // candidate) and, for verify, runs greedy acceptance; the last workgroup
@@ -159,9 +163,10 @@ __device__ __forceinline__ void finish_rows_grouped(const RowSink &s, const floa
   const int nthreads = blockDim.x;
   const uint32_t bid = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
   const uint32_t g = bid % G;
+  const size_t gstride = finish_group_stride(s.M);
   char *const groups = reinterpret_cast<char *>(s.ticket) + kWsHeader;
   unsigned long long *const keys =
-      reinterpret_cast<unsigned long long *>(groups + (size_t)g * s.gstride + 64);
+      reinterpret_cast<unsigned long long *>(groups + (size_t)g * gstride + 64);
   if (tid == 0) s_seen = 0;
   __syncthreads();
   for (int t = tid; t < m_count; t += nthreads) {
@@ -176,7 +181,7 @@ __device__ __forceinline__ void finish_rows_grouped(const RowSink &s, const floa
   __syncthreads();
   if (tid == 0) {
     const uint32_t nblocks = gridDim.x * gridDim.y * gridDim.z;
-    uint32_t *const gt = reinterpret_cast<uint32_t *>(groups + (size_t)g * s.gstride);
+    uint32_t *const gt = reinterpret_cast<uint32_t *>(groups + (size_t)g * gstride);
     const uint32_t gsize = nblocks / G + (g < nblocks % G ? 1u : 0u);
     const uint32_t ngroups = nblocks < G ? nblocks : G;
     const uint32_t pg = __hip_atomic_fetch_add(gt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -197,7 +202,7 @@ __device__ __forceinline__ void finish_rows_grouped(const RowSink &s, const floa
 #pragma unroll
     for (uint32_t q = 0; q < G; ++q) {
       unsigned long long *const kq =
-          reinterpret_cast<unsigned long long *>(groups + (size_t)q * s.gstride + 64);
+          reinterpret_cast<unsigned long long *>(groups + (size_t)q * gstride + 64);
       const unsigned long long v =
           __hip_atomic_exchange(&kq[m], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       key = v > key ? v : key;

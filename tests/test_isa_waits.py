@@ -14,7 +14,11 @@ instantiated ring kernel, that
 
 A compiler change that moves a load across the wait, splits a body or drains
 the pipeline makes it fail, instead of leaving the parity tests to catch an
-early LDS read on the GPU."""
+early LDS read on the GPU.
+
+It also checks the main loop of every LDS-fed kernel (gemm_argmax_dma) for
+two things that keep results right but cost speed: a scalar reload of a
+kernel argument, and a full drain (vmcnt(0)) right before an LDS read."""
 
 import os
 import re
@@ -146,3 +150,64 @@ def test_checker_flags_loads_sunk_below_the_wait(asm):
         moved[at + 2:at + 2] = [loop[i] for i in sorted(block)]  # loads after it
         with pytest.raises(AssertionError):
             check_ring_loop(moved)
+
+
+def mfma_loop(lines):
+    """Lines of the loop that holds the kernel's first MFMA: every block the
+    compiler marks as that loop's header or as inside it."""
+    starts = []
+    for i, l in enumerate(lines):
+        m = re.match(r"^(\.LBB\d+_\d+|; %bb\.\d+):(.*)$", l)
+        if m:
+            name = m.group(1)
+            name = "BB" + name.split("BB", 1)[1] if name.startswith(".LBB") else name
+            inside = re.search(r"in Loop: Header=(\w+)", m.group(2))
+            starts.append((i, name if "Loop Header" in m.group(2) else
+                           (inside.group(1) if inside else None)))
+    starts.append((len(lines), None))
+    first = next(i for i, l in enumerate(lines) if "v_mfma" in l)
+    hdr = starts[max(j for j, b in enumerate(starts[:-1]) if b[0] <= first)][1]
+    assert hdr is not None, "the first MFMA is in no loop"
+    return [l for j, b in enumerate(starts[:-1]) if b[1] == hdr
+            for l in lines[b[0]:starts[j + 1][0]]]
+
+
+def check_dma_loop(loop):
+    """Inside the copy/MFMA loop of the LDS-fed kernel: no scalar reload of a
+    kernel argument, and no full drain of the copies in flight right before
+    an LDS read (the waits before the reads are the hand-counted ones)."""
+    ins = [l.strip() for l in loop
+           if l.strip() and not l.strip().startswith(";") and not re.match(r"^[.\w%]+:", l.strip())]
+    for i, l in enumerate(ins):
+        assert not l.startswith("s_load"), f"scalar load inside the loop: {l}"
+        if re.match(r"s_waitcnt\b.*\bvmcnt\(0\)", l):
+            nxt = next((x for x in ins[i + 1:i + 4] if not x.startswith("s_nop")), "")
+            assert not nxt.startswith("ds_read"), f"vmcnt(0) right before {nxt}"
+
+
+def test_dma_kernel_loops_keep_copies_in_flight(asm):
+    """Every LDS-fed matrix-core kernel (gemm_argmax_dma) keeps its copies in
+    flight across the LDS reads of its main loop. A larger kernel argument
+    once pushed the compiler, at the scalar-register limit, into reloading an
+    argument inside the loop and draining every copy before an LDS read: 10%
+    slower, with correct results."""
+    dmas = kernels(asm, "_ZN3mtp15gemm_argmax_dma")
+    assert len(dmas) >= 20, len(dmas)
+    for name, lines in dmas.items():
+        try:
+            check_dma_loop(mfma_loop(lines))
+        except AssertionError as e:
+            raise AssertionError(f"{name}: {e}") from None
+
+
+def test_dma_checker_flags_a_drain_before_an_lds_read(asm):
+    """The check itself: a full drain inserted before the first LDS read of
+    a loop, or a scalar load inside it, must fail it."""
+    lines = next(iter(kernels(asm, "_ZN3mtp15gemm_argmax_dma").values()))
+    loop = mfma_loop(lines)
+    check_dma_loop(loop)
+    k = next(i for i, l in enumerate(loop) if l.strip().startswith("ds_read"))
+    with pytest.raises(AssertionError):
+        check_dma_loop(loop[:k] + ["\ts_waitcnt vmcnt(0)"] + loop[k:])
+    with pytest.raises(AssertionError):
+        check_dma_loop(loop[:k] + ["\ts_load_dwordx4 s[40:43], s[0:1], 0x20"] + loop[k:])
