@@ -115,14 +115,44 @@ def parse_args():
     return ap.parse_args()
 
 
+def code_text(src: str) -> str:
+    """C/C++/HIP source without its comments and with runs of blank space
+    collapsed, so that an edit of comments or layout leaves the hash alone.
+    String and character literals are kept whole (a "//" inside one is not a
+    comment)."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            out.append(" ")
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_hash(path: str) -> str:
+    """Hash of a kernel family's sources (code only: see code_text). A profile
+    summary carries it, and the bench uses a summary's counters only when
+    its hash equals that of the sources as they are now."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "speculative_decoding_argmax_amd", "csrc")
     for name in KERNEL_SOURCES[path]:
         p = os.path.join(csrc, name)
         if os.path.exists(p):
             h.update(name.encode())
-            h.update(open(p, "rb").read())
+            h.update(code_text(open(p, encoding="utf-8").read()).encode())
     return h.hexdigest()[:16]
 
 

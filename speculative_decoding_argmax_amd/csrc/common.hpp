@@ -119,9 +119,8 @@ struct RowSink {
 };
 static_assert(sizeof(RowSink) == 80, "kept at 80 bytes (see above)");
 
-// Writes the outputs of every hidden row from its final key (0: no
-// candidate) and, for verify, runs greedy acceptance; the last workgroup
-// calls it once every key is final.
+// The last workgroup, once every key is final: hidden row m's id and logit
+// from its key (0: no candidate seen, id -1 and NaN).
 __device__ __forceinline__ void finish_outputs(const RowSink &s, int m,
                                                unsigned long long key) {
   int32_t id = -1;
@@ -135,6 +134,9 @@ __device__ __forceinline__ void finish_outputs(const RowSink &s, int m,
   if (s.out_logit) s.out_logit[m] = val;
 }
 
+// The last workgroup, after finish_outputs for every row: for verify, greedy
+// acceptance of each sequence's drafts against the target ids just written;
+// then the call's ticket goes back to zero for the next call.
 __device__ __forceinline__ void finish_accept(const RowSink &s) {
   if (s.k >= 0) {
     __syncthreads();  // out_ids (the target argmax) written by this workgroup

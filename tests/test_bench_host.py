@@ -117,3 +117,18 @@ def bench_logit(h, head, token):
     x = (h.astype(np.uint32) << 16).view(np.float32).astype(np.float64).ravel()
     w = (head[token].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     return float(x @ w)
+
+
+def test_source_hash_ignores_comments_and_layout_only():
+    """Profile summaries carry a hash of their kernels' code: editing a
+    comment or the layout keeps it, editing code (or a string) changes it."""
+    src = 'int f(int a) {  // the sum\n  /* twice */ return a + a; }\nconst char *s = "x // y";\n'
+    same = 'int f(int a) {\n  return a + a;   // twice, reworded\n}\nconst char *s = "x // y";\n'
+    code = 'int f(int a) {  // the sum\n  /* twice */ return a + 2; }\nconst char *s = "x // y";\n'
+    text = 'int f(int a) {  // the sum\n  /* twice */ return a + a; }\nconst char *s = "x // z";\n'
+    assert bench.code_text(src) == bench.code_text(same)
+    assert bench.code_text(src) != bench.code_text(code)
+    assert bench.code_text(src) != bench.code_text(text)
+    assert bench.code_text("char c = '\\'';  // q") == "char c = '\\'';"
+    for fam in bench.KERNEL_SOURCES:
+        assert len(bench.kernel_source_hash(fam)) == 16
