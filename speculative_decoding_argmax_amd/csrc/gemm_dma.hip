@@ -25,8 +25,9 @@
 // unrolled by NBUF, so the compiler can see that reads of slot it do not alias
 // the copies into other slots and leaves those copies in flight. Before
 // reading a slot, every wave waits (s_waitcnt vmcnt) until its own copies into
-// that slot have landed (all waves issue the same number of copies per chunk,
-// so the count of younger copies is a constant), then all waves meet at a
+// that slot have landed (all waves issue the same number of fragment copies
+// per chunk, so the count of younger copies is a constant; scale copies are
+// left out of it and only make their waves wait longer), then all waves meet at a
 // plain s_barrier (no fence, which would wait for every copy in flight). The
 // barrier also orders the next copy into a slot after every wave's reads of
 // that slot's previous chunk.
@@ -339,7 +340,11 @@ __global__ void __launch_bounds__(WV * 64)
 
   auto body = [&](auto tag, int it) {
     constexpr int SL = decltype(tag)::value;
-    // copies younger than this chunk's: chunks it+1 .. it+NBUF-2
+    // copies younger than this chunk's: chunks it+1 .. it+NBUF-2, PER_WAVE
+    // each. The scale copies are not counted (fp4: one per chunk from waves
+    // below NPC; fp8: one per tile-last chunk from waves below RBT / 4), so
+    // those waves also wait for the oldest younger copy; an exact count,
+    // chosen per wave by a scalar branch, measured no faster on MI355X.
     if (it + NBUF - 2 < total)
       wait_vmcnt<(NBUF - 2) * PER_WAVE>();
     else
