@@ -16,9 +16,11 @@ A compiler change that moves a load across the wait, splits a body or drains
 the pipeline makes it fail, instead of leaving the parity tests to catch an
 early LDS read on the GPU.
 
-It also checks the main loop of every LDS-fed kernel (gemm_argmax_dma) for
-two things that keep results right but cost speed: a scalar reload of a
-kernel argument, and a full drain (vmcnt(0)) right before an LDS read."""
+It also checks the main loop of every LDS-fed kernel (gemm_argmax_dma):
+each barrier comes right after a hand wait with no LDS copy between them
+(a copy sunk below the wait would make it too weak), and two things that
+keep results right but cost speed are absent: a scalar reload of a kernel
+argument, and a full drain (vmcnt(0)) right before an LDS read."""
 
 import os
 import re
@@ -198,6 +200,63 @@ def test_dma_kernel_loops_keep_copies_in_flight(asm):
             check_dma_loop(mfma_loop(lines))
         except AssertionError as e:
             raise AssertionError(f"{name}: {e}") from None
+
+
+def check_dma_barriers(loop, nbuf):
+    """Inside the loop of the LDS-fed kernel: one barrier per LDS slot (the
+    loop is unrolled by the slot count), each right after a hand wait
+    vmcnt(n > 0), with no LDS copy between that wait and the barrier. The
+    copies of a body are issued after its barrier and must stay ahead of the
+    next body's wait: a copy sunk below that wait would no longer count as
+    younger, and the wait would then let the oldest copies of the chunk
+    about to be read still be in flight. (The barrier's compiler fence stops
+    a copy from sinking further.)"""
+    ev = []
+    for l in loop:
+        s = l.strip()
+        m = VMEM.match(l)
+        if m:
+            ev.append(("copy" if (" lds" in m.group(2) or "_lds" in m.group(1)) else "load",))
+            continue
+        w = WAIT.match(l)
+        if w:
+            ev.append(("wait", int(w.group(1))))
+        elif re.match(r"s_barrier\b", s):
+            ev.append(("bar",))
+        elif s and not s.startswith(";") and not re.match(r"^[.\w%]+:", s):
+            ev.append(("op",))
+    bars = [i for i, e in enumerate(ev) if e[0] == "bar"]
+    assert len(bars) == nbuf, f"{len(bars)} barriers in a loop of {nbuf} slots"
+    for b in bars:
+        hand = next((j for j in range(b - 1, max(b - 24, -1), -1)
+                     if ev[j][0] == "wait" and ev[j][1] > 0), None)
+        assert hand is not None, "no hand wait right before a barrier"
+        assert all(e[0] != "copy" for e in ev[hand + 1:b]), "an LDS copy between a hand wait and its barrier"
+
+
+def test_dma_kernel_waits_precede_their_barriers(asm):
+    """Every LDS-fed kernel keeps each body's copies ahead of the next body's
+    hand wait (check_dma_barriers)."""
+    dmas = kernels(asm, "_ZN3mtp15gemm_argmax_dma")
+    for name, lines in dmas.items():
+        nbuf = int(re.match(r"_ZN3mtp15gemm_argmax_dmaILi\d+ELi\d+ELi\d+ELi(\d+)E", name).group(1))
+        try:
+            check_dma_barriers(mfma_loop(lines), nbuf)
+        except AssertionError as e:
+            raise AssertionError(f"{name}: {e}") from None
+
+
+def test_dma_barrier_checker_flags_a_sunk_copy(asm):
+    """The check itself: an LDS copy moved between a hand wait and its
+    barrier must fail it."""
+    name, lines = next(iter(kernels(asm, "_ZN3mtp15gemm_argmax_dma").items()))
+    nbuf = int(re.match(r"_ZN3mtp15gemm_argmax_dmaILi\d+ELi\d+ELi\d+ELi(\d+)E", name).group(1))
+    loop = mfma_loop(lines)
+    check_dma_barriers(loop, nbuf)
+    copy = next(l for l in loop if VMEM.match(l) and "lds" in l)
+    k = next(i for i, l in enumerate(loop) if re.match(r"^\s*s_barrier\b", l))
+    with pytest.raises(AssertionError):
+        check_dma_barriers(loop[:k] + [copy] + loop[k:], nbuf)
 
 
 def test_dma_checker_flags_a_drain_before_an_lds_read(asm):
