@@ -60,6 +60,47 @@ __device__ __forceinline__ bool better_row(float v, int i, float bv, int bi) {
   return bi < 0 || v > bv || (v == bv && i < bi);
 }
 
+// The better of two (logit, row) candidates, kept in (v, i): a row >= 0
+// beats none (-1), a higher logit beats a lower one, and equal logits go to
+// the lower row. This is a total order on the candidates, so every
+// reduction order picks the same winner.
+__device__ __forceinline__ void pick_better(float &v, int &i, float v2, int i2) {
+  const bool take = i2 >= 0 && (i < 0 || v2 > v || (v2 == v && i2 < i));
+  v = take ? v2 : v;
+  i = take ? i2 : i;
+}
+
+// Merge the 4 * WV candidates that the lanes hold for each of the NB * 16
+// hidden rows (entry (w * NB + nb) * 64 + j + 16 g of red_v / red_i: wave w,
+// lane j + 16 g, hidden row 16 nb + j) into f_val / f_row. Thread t < NB * 16
+// takes row t: it reads all of the row's candidates first, so that the LDS
+// reads overlap, then reduces them pairwise (a chain of log2(4 WV) picks
+// instead of 4 WV reads and compares one after another).
+template <int NB, int WV>
+__device__ __forceinline__ void merge_candidates(const float *red_v, const int *red_i, int tid,
+                                                 float *f_val, int64_t *f_row) {
+  constexpr int Q = 4 * WV;
+  static_assert((Q & (Q - 1)) == 0, "a power-of-two candidate count");
+  if (tid < NB * 16) {
+    const int nb = tid >> 4;
+    const int jj = tid & 15;
+    float cv[Q];
+    int ci[Q];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const int o = ((q >> 2) * NB + nb) * kWave + jj + 16 * (q & 3);
+      cv[q] = red_v[o];
+      ci[q] = red_i[o];
+    }
+#pragma unroll
+    for (int w = 1; w < Q; w <<= 1)
+#pragma unroll
+      for (int q = 0; q < Q; q += 2 * w) pick_better(cv[q], ci[q], cv[q + w], ci[q + w]);
+    f_val[tid] = cv[0];
+    f_row[tid] = ci[0];
+  }
+}
+
 // Workgroup barrier without a memory fence (a fence would wait for every copy
 // in flight). The empty asm statements keep the compiler from moving memory
 // accesses across it.
@@ -505,23 +546,7 @@ __global__ void __launch_bounds__(WV * 64)
     red_i[(wave * NB + nb) * kWave + lane] = bi[nb];
   }
   __syncthreads();
-  if (tid < NB * 16) {
-    const int nb = tid >> 4;
-    const int jj = tid & 15;
-    float v = 0.f;
-    int ix = -1;
-    for (int w = 0; w < WV; ++w) {
-      for (int gg = 0; gg < 4; ++gg) {
-        const int o = (w * NB + nb) * kWave + jj + 16 * gg;
-        if (red_i[o] >= 0 && better_row(red_v[o], red_i[o], v, ix)) {
-          v = red_v[o];
-          ix = red_i[o];
-        }
-      }
-    }
-    f_val[tid] = v;
-    f_row[tid] = ix;
-  }
+  merge_candidates<NB, WV>(red_v, red_i, tid, f_val, f_row);
   __syncthreads();
   const int mcount = M - m0 < NB * 16 ? M - m0 : NB * 16;
   finish_rows(sink, f_val, f_row, m0, mcount);
@@ -893,23 +918,7 @@ __global__ void __launch_bounds__(WV * 64)
     }
   }
   __syncthreads();
-  if (tid < NB * 16) {
-    const int nb = tid >> 4;
-    const int jj = tid & 15;
-    float v = 0.f;
-    int ix = -1;
-    for (int w = 0; w < WV; ++w) {
-      for (int gg = 0; gg < 4; ++gg) {
-        const int o = (w * NB + nb) * kWave + jj + 16 * gg;
-        if (red_i[o] >= 0 && better_row(red_v[o], red_i[o], v, ix)) {
-          v = red_v[o];
-          ix = red_i[o];
-        }
-      }
-    }
-    f_val[tid] = v;
-    f_row[tid] = ix;
-  }
+  merge_candidates<NB, WV>(red_v, red_i, tid, f_val, f_row);
   __syncthreads();
   const int mcount = M - m0 < NB * 16 ? M - m0 : NB * 16;
   finish_rows(sink, f_val, f_row, m0, mcount);
