@@ -118,7 +118,7 @@ mtp_status mtp_validate_ids(const int32_t *ids_host, int64_t C, int64_t V);
  * every variant of these calls). 0 for arguments out of range.
  *   - Counters: 256 bytes of header and 8 regions of 64 + 8*M bytes, each
  *     rounded up to 256 (2,304 bytes at M = 1). Launches whose workgroups
- *     each stream less than 384 KiB of the table spread the cross-workgroup
+ *     each stream less than 448 KiB of the table spread the cross-workgroup
  *     finish over the 8 regions (a grouped finish: 8 group tickets and key
  *     sets, so that hundreds of workgroups arriving together do not queue
  *     on one address). Every call accepts the counters' least size, 256 +

@@ -66,9 +66,12 @@ size_t min_rows_workspace_bytes(int64_t M) {
 // and hundreds of same-address atomics then queue (measured on MI355X,
 // same-box A/B: MXFP4 M = 1 drafts at 32,768 and 65,536 x 2,048 rows 13.9 ->
 // 10.4 and 18.2 -> 15.6 us, bf16 at 16,384 rows 14.7 -> 13.7 us, fp8 at
-// 32,768 rows 15.3 -> 14.5 us; at 1 MiB and more per workgroup the extra
-// round trip cost 0.3-0.7 us, e.g. the bf16 65,536-row draft 40.6 -> 41.3).
-constexpr double kGroupedFinishBytes = 384.0 * 1024.0;
+// 32,768 rows 15.3 -> 14.5 us, bf16 at 24,576 rows (384 KiB per workgroup)
+// 18.8 -> 18.4 us; at 512 KiB the two finishes time the same, bf16 at
+// 32,768 rows 23.0 us; beyond that the extra round trip costs 0.3-0.7 us,
+// e.g. 27.7 -> 28.2 us at 32,768 x 2,560 and 40.6 -> 41.3 us for the bf16
+// 65,536-row draft).
+constexpr double kGroupedFinishBytes = 448.0 * 1024.0;
 
 void choose_finish(mtp::RowSink &s, size_t ws_bytes, double table_bytes, int64_t workgroups) {
   if (ws_bytes >= rows_workspace_bytes(s.M) && workgroups > 0 &&

@@ -1,5 +1,5 @@
 """GPU tests of the grouped cross-workgroup finish. A launch whose workgroups
-each stream less than 384 KiB of the table, given the workspace's full size,
+each stream less than 448 KiB of the table, given the workspace's full size,
 merges its winners through 8 group tickets and key sets; given only the
 least size (header and one key per row) the same call runs the one-level
 finish. Both must return the same bits, match the oracle, and leave the
