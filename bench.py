@@ -487,6 +487,30 @@ def main() -> int:
                    "head_bytes": int(head_bytes),
                    "head_GBps": stream_gbps([head_v], head_bytes, 20)}
 
+    # Atomic round trip (the unit the cross-workgroup finish repeats three or
+    # four times at the end of every call): chains of dependent agent-scope
+    # fetch-and-adds, one lane per workgroup, alone, in one workgroup per CU
+    # on their own lines, and in one workgroup per CU on one line.
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    words = torch.zeros(64 * cus, dtype=torch.int32, device=dev)
+    ticks = torch.zeros(cus, dtype=torch.int64, device=dev)
+
+    def round_trip_us(wgs, same, iters=64, reps=5):
+        per = []
+        for _ in range(reps):
+            mtp.mtp_probe_atomic(words, ticks, wgs, iters, same)
+            torch.cuda.synchronize()
+            t = (ticks[:wgs].cpu() & ((1 << 63) - 1)).tolist()
+            per.append(statistics.median(t) / iters / 100.0)
+        return round(statistics.median(per), 3)
+
+    atomic_round_trip = {"alone_us": round_trip_us(1, False),
+                         "one_wg_per_cu_own_lines_us": round_trip_us(cus, False),
+                         "one_wg_per_cu_one_line_us": round_trip_us(cus, True, iters=16),
+                         "method": "median over workgroups of one lane's chain of dependent "
+                                   "agent-scope fetch-and-adds (mtp_probe_atomic), in 100 MHz "
+                                   "real-time counter ticks, median of 5 launches"}
+
     # Draft-head ablation (workloads that list table sizes): the same M = 1
     # draft over each table, plus the pages' per-rank shard shape as context.
     draft_tables = None
@@ -638,6 +662,7 @@ def main() -> int:
             "draft_same_table_us": round(warm_draft_us, 2),
             "single_call_us": {"draft": single_draft_us, "verify": single_verify_us},
             "stream_read": stream_read,
+            "atomic_round_trip": atomic_round_trip,
             "acceptance": acceptance,
             "quantised_draft_agrees_with_bf16": agreement,
             "agreement_rows": (max(1, min(args.agree_rows, 4096)) if (fp8 or fp4) else None),

@@ -640,6 +640,32 @@ void mtp_graph_destroy(mtp_graph *graph);
 #define MTP_STREAM_SINK_WORDS 8192
 mtp_status mtp_stream_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t stream);
 
+/* Atomic round-trip reference (a probe, like mtp_stream_read).
+ *
+ * Every call merges its workgroups' winners through device-scope atomics at
+ * its end: each workgroup updates its keys and takes a ticket, and the last
+ * one reads the merged keys, a few dependent round trips to the memory's
+ * coherence point. [Qwen3.8 Flash dual-Spark tuning log, section "read one
+ * fewer big table": the draft finds the maximum within its candidates and
+ * exchanges (max score, global token id).] This probe times that round trip:
+ * in each of `wgs` workgroups one lane runs `iters` agent-scope
+ * fetch-and-adds, each waiting for the one before, on its own word
+ * (words[64 b], 256 bytes apart; same == 0) or all on words[0] (same == 1),
+ * and writes the chain's duration in ticks of the 100 MHz real-time counter
+ * to ticks[b] (the top bit carries no meaning; mask it off).
+ *
+ * words: device uint32 [64 * wgs] (same == 0) or [2] (same == 1), 4-byte
+ * aligned, any contents (they are incremented). ticks: device uint64 [wgs],
+ * 8-byte aligned. 1 <= wgs <= MTP_PROBE_MAX_WGS, 1 <= iters <=
+ * MTP_PROBE_MAX_ITERS. Errors: MTP_ERR_INVALID_ARG for a null pointer,
+ * misalignment or a value out of range; MTP_ERR_HIP for a launch failure.
+ * Asynchronous on `stream`; allocates nothing.
+ */
+#define MTP_PROBE_MAX_WGS 4096
+#define MTP_PROBE_MAX_ITERS 1024
+mtp_status mtp_probe_atomic(uint32_t *words, int wgs, int iters, int same,
+                            unsigned long long *ticks, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

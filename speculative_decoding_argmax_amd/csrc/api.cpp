@@ -952,6 +952,17 @@ mtp_status mtp_stream_read(const void *buf, size_t bytes, uint32_t *sink, hipStr
   return MTP_OK;
 }
 
+mtp_status mtp_probe_atomic(uint32_t *words, int wgs, int iters, int same,
+                            unsigned long long *ticks, hipStream_t stream) {
+  if (!words || !ticks || wgs < 1 || wgs > MTP_PROBE_MAX_WGS || iters < 1 ||
+      iters > MTP_PROBE_MAX_ITERS || (same != 0 && same != 1))
+    return MTP_ERR_INVALID_ARG;
+  if (!aligned(words, 4) || !aligned(ticks, 8)) return MTP_ERR_INVALID_ARG;
+  hipError_t e = mtp::launch_atomic_chain(words, wgs, iters, same, ticks, stream);
+  if (e != hipSuccess) return hip_fail(e);
+  return MTP_OK;
+}
+
 struct mtp_graph {
   hipGraph_t graph;
   hipGraphExec_t exec;

@@ -167,5 +167,8 @@ hipError_t launch_pack_mxfp4(const void *head, int64_t V, int H, const int32_t *
 constexpr int kStreamSinkWords = 8192;
 hipError_t launch_stream_read(const void *buf, size_t bytes, uint32_t *sink, int cus,
                               hipStream_t stream);
+// Atomic round-trip reference (probe.hip).
+hipError_t launch_atomic_chain(uint32_t *words, int wgs, int iters, int same,
+                               unsigned long long *ticks, hipStream_t stream);
 
 }  // namespace mtp

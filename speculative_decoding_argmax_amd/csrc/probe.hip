@@ -42,6 +42,34 @@ __global__ void __launch_bounds__(256)
   if (lane == 0) sink[gw] = x;
 }
 
+// Atomic round-trip reference: the latency of one dependent agent-scope
+// atomic, the step that the cross-workgroup finish of every call repeats
+// three or four times at the call's end. Lane 0 of workgroup b runs a chain
+// of `iters` fetch-and-adds on word 64 b (or word 0 when `same`), each
+// address taken from the previous return (always the same word, but the
+// compiler cannot know it), so every atomic waits for the one before. The
+// chain's duration in ticks of the 100 MHz real-time counter goes to
+// ticks[b].
+__global__ void __launch_bounds__(64)
+    atomic_chain(uint32_t *words, int iters, int same, unsigned long long *ticks) {
+  if (threadIdx.x != 0) return;
+  uint32_t *w = words + (same ? 0 : 64 * (int64_t)blockIdx.x);
+  uint32_t v = 0;
+  const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+  for (int i = 0; i < iters; ++i)
+    v = __hip_atomic_fetch_add(&w[(v >> 31) & 1u], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // the last return must have arrived before the clock is read
+  asm volatile("" : : "v"(v) : "memory");
+  const unsigned long long t1 = __builtin_amdgcn_s_memrealtime();
+  ticks[blockIdx.x] = (t1 - t0) | ((unsigned long long)(v >> 31) << 63);  // v keeps the chain live
+}
+
+hipError_t launch_atomic_chain(uint32_t *words, int wgs, int iters, int same,
+                               unsigned long long *ticks, hipStream_t stream) {
+  hipLaunchKernelGGL(atomic_chain, dim3(wgs), dim3(64), 0, stream, words, iters, same, ticks);
+  return hipGetLastError();
+}
+
 hipError_t launch_stream_read(const void *buf, size_t bytes, uint32_t *sink, int cus,
                               hipStream_t stream) {
   // two 4-wave workgroups per CU, at most one sink word per wave

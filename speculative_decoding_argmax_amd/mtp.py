@@ -117,6 +117,7 @@ def _load() -> ctypes.CDLL:
         "mtp_draft_argmax_tiled_fp8": ([P, I, I, P, P, P, I64, P, P, P, S, P], I),
         "mtp_draft_argmax_tiled_fp8_cfg": ([P, I, I, P, P, P, I64, P, P, P, S, P, P], I),
         "mtp_stream_read": ([P, S, P, P], I),
+        "mtp_probe_atomic": ([P, I, I, I, P, P], I),
         "mtp_graph_begin": ([P], I),
         "mtp_graph_end": ([P, ctypes.POINTER(P)], I),
         "mtp_graph_launch": ([P, P], I),
@@ -769,6 +770,27 @@ def mtp_stream_read(buf, sink, nbytes: Optional[int] = None, stream=None) -> Non
     _check(lib.mtp_stream_read(_ptr(buf, "buf", (buf.dtype,)), n,
                                _ptr(sink, "sink", (torch.int32, torch.uint8)), _stream(stream)),
            "mtp_stream_read")
+
+
+MTP_PROBE_MAX_WGS = 4096
+MTP_PROBE_MAX_ITERS = 1024
+
+
+def mtp_probe_atomic(words, ticks, wgs: int, iters: int, same: bool = False, stream=None) -> None:
+    """Atomic round-trip probe: in each of wgs workgroups one lane runs iters
+    dependent agent-scope fetch-and-adds on its own word of words (int32 device
+    tensor of 64 * wgs words) or all on words[0] (same); ticks (int64 device
+    tensor of wgs) gets each chain's 100 MHz tick count in its low 63 bits."""
+    torch = _torch()
+    need = 2 if same else 64 * wgs
+    if words.numel() * words.element_size() < 4 * need:
+        raise ValueError("words too small")
+    if ticks.numel() * ticks.element_size() < 8 * wgs:
+        raise ValueError("ticks too small")
+    _check(lib.mtp_probe_atomic(_ptr(words, "words", (torch.int32,)), int(wgs), int(iters),
+                                1 if same else 0, _ptr(ticks, "ticks", (torch.int64,)),
+                                _stream(stream)),
+           "mtp_probe_atomic")
 
 
 # ---- graph-captured MTP step ----------------------------------------------

@@ -298,6 +298,19 @@ def test_stream_read_rejects_bad_arguments():
     assert f(FAKE, 1024, P(0x10002), None) == INVALID    # sink not 4-byte aligned
 
 
+def test_probe_atomic_rejects_bad_arguments():
+    f = mtp.lib.mtp_probe_atomic
+    assert f(None, 1, 1, 0, FAKE, None) == INVALID
+    assert f(FAKE, 1, 1, 0, None, None) == INVALID
+    assert f(FAKE, 0, 1, 0, FAKE, None) == INVALID                       # no workgroup
+    assert f(FAKE, mtp.MTP_PROBE_MAX_WGS + 1, 1, 0, FAKE, None) == INVALID
+    assert f(FAKE, 1, 0, 0, FAKE, None) == INVALID                       # no iteration
+    assert f(FAKE, 1, mtp.MTP_PROBE_MAX_ITERS + 1, 0, FAKE, None) == INVALID
+    assert f(FAKE, 1, 1, 2, FAKE, None) == INVALID                       # same is 0 or 1
+    assert f(P(0x10002), 1, 1, 0, FAKE, None) == INVALID                 # words not 4-byte aligned
+    assert f(FAKE, 1, 1, 0, P(0x10004), None) == INVALID                 # ticks not 8-byte aligned
+
+
 def test_wide_tiled_calls_need_the_staging_area():
     """Above 128 hidden rows the workspace query adds the packed-hidden
     staging area (S steps x 10 row blocks x 1 KiB per 160-row pass, plus
