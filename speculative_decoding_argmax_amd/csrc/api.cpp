@@ -624,9 +624,14 @@ static mtp_status run_fp8(const mtp_bf16 *hidden, int M, int H, const uint8_t *t
   const int mr = mtp::fp8_rows_for(M, ncl);
   // two workgroups per CU when one pass covers every hidden row with enough
   // arithmetic per byte (MR * NCL >= 8) to be ALU-limited; one otherwise
-  // (measured on MI355X at H = 2,048 .. 5,120, M = 1 .. 8)
+  // (measured on MI355X at H = 2,048 .. 5,120, M = 1 .. 8). Short rows (at
+  // most two chunks per lane, H <= 2,048) with 2 to 4 hidden rows in one
+  // pass take four: a same-box sweep of 1-4 workgroups per CU at 65,536 x
+  // 2,048 gave 29.9 -> 26.3 us at M = 2, 31.9 -> 30.4 at M = 3 and 32.2 ->
+  // 30.4 at M = 4, while every other cell measured kept its count.
   const int per_cu = (cfg && cfg->blocks_per_cu > 0) ? cfg->blocks_per_cu
-                                                      : ((mr >= M && mr * ncl >= 8) ? 2 : 1);
+                     : (ncl <= 2 && mr >= 2 && mr <= 4 && mr >= M) ? 4
+                     : ((mr >= M && mr * ncl >= 8) ? 2 : 1);
   mtp::Fp8Launch L;
   L.X = hidden;
   L.Q = table_q;
@@ -738,8 +743,13 @@ static mtp_status run_mxfp4(const mtp_bf16 *hidden, int M, int H, const uint8_t 
   const int mr = mtp::fp4_rows_for(M, ncl);
   // two workgroups per CU: a row is only H/2 bytes, so one workgroup per CU
   // keeps too little in flight (measured on MI355X, 65,536 rows at H = 2,048:
-  // 19.3 us against 21.4 us at M = 1, 35.7 against 45.8 us at M = 4)
-  const int per_cu = (cfg && cfg->blocks_per_cu > 0) ? cfg->blocks_per_cu : 2;
+  // 19.3 us against 21.4 us at M = 1, 35.7 against 45.8 us at M = 4). With
+  // one block per lane (H <= 2,048) and 2 to 4 hidden rows per pass the
+  // kernel is bound by its arithmetic, and four workgroups per CU hide more
+  // of it (same-box A/B at 65,536 x 2,048: 21.7 -> 21.0 us at M = 2, 30.9 ->
+  // 28.3 us at M = 4; at M = 1 and 8, and at H = 4,096, two stay faster).
+  const int per_cu = (cfg && cfg->blocks_per_cu > 0) ? cfg->blocks_per_cu
+                                                      : (ncl == 1 && mr >= 2 && mr <= 4 ? 4 : 2);
   mtp::Fp4Launch L;
   L.X = hidden;
   L.Q = table_q;
