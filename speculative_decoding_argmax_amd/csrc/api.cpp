@@ -146,10 +146,20 @@ mtp_status run_rows(const mtp_bf16 *X, int M, int H, const mtp_bf16 *W, int64_t 
   if (e != hipSuccess) return hip_fail(e);
   if (path == MTP_PATH_VALU) {
     if (ncl == 0) return MTP_ERR_UNSUPPORTED;
-    // one resident workgroup per CU for rows up to 2,560 wide, two beyond
-    // (prefetching variant; measured best on MI355X at the workload shapes)
-    const int per_cu =
-        (cfg && cfg->blocks_per_cu > 0) ? cfg->blocks_per_cu : (ncl <= 5 ? 1 : 2);
+    // Resident workgroups per CU, from a same-box sweep of 1-4 on MI355X
+    // (65,536 rows, M = 1, 2, 4, 8, H = 1,024 .. 4,096, and checks at 5,120
+    // and 8,192): one for rows of 3 to 8 chunks per lane (H 2,048 .. 4,096;
+    // at 4,096 one beats two, 83.1 -> 78.3 us at M = 1), two when a pass holds
+    // 8 hidden rows there (H = 2,048, M = 8: 69.0 -> 53.3 us). Short rows (at
+    // most 2 chunks, H <= 1,024) keep too little in flight with one: two, four
+    // with 8 rows per pass (29.0 -> 23.0 us at M = 1, 59.8 -> 36.1 us at
+    // M = 8). Wider rows than 8 chunks take two (H = 8,192: 83.0 against
+    // 85.4 us with one; even at 5,120).
+    const int mr_v = mtp::valu_rows_for(M, ncl);
+    const int per_cu = (cfg && cfg->blocks_per_cu > 0) ? cfg->blocks_per_cu
+                       : ncl <= 2                    ? (mr_v >= 8 ? 4 : 2)
+                       : ncl <= 8                    ? (mr_v >= 8 ? 2 : 1)
+                                                     : 2;
     choose_finish(sink, ws_bytes, table_bytes, (int64_t)per_cu * cus);
     mtp::ValuLaunch L;
     L.X = X;
@@ -631,6 +641,7 @@ static mtp_status run_fp8(const mtp_bf16 *hidden, int M, int H, const uint8_t *t
   // 30.4 at M = 4, while every other cell measured kept its count.
   const int per_cu = (cfg && cfg->blocks_per_cu > 0) ? cfg->blocks_per_cu
                      : (ncl <= 2 && mr >= 2 && mr <= 4 && mr >= M) ? 4
+                     : (ncl == 1 && M == 1) ? 2  // H <= 1,024: 18.9 -> 15.0 us
                      : ((mr >= M && mr * ncl >= 8) ? 2 : 1);
   mtp::Fp8Launch L;
   L.X = hidden;
